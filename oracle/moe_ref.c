@@ -196,7 +196,7 @@ void ref_expert_ffn(int fmt, int H, int F, const uint8_t *const *banks, const in
  * idx holds pool rows: slot ids over a slot pool, or expert ids over a
  * whole layer's pool (the streamed layer). */
 void ref_routed(int fmt, int H, int F, const uint8_t *const *banks, const int64_t *rb,
-                int T, int K, const int32_t *idx, const float *w, const uint16_t *x,
+                int T, int K, const int32_t *idx, const double *w, const uint16_t *x,
                 const double *addend, double *out)
 {
     ref_pool p;
@@ -212,7 +212,7 @@ void ref_routed(int fmt, int H, int F, const uint8_t *const *banks, const int64_
                 continue;
             ref_expert(&p, r, x + (int64_t)t * H, d);
             for (int i = 0; i < H; i++)
-                o[i] += (double)w[(int64_t)t * K + k] * d[i];
+                o[i] += w[(int64_t)t * K + k] * d[i];
         }
         if (addend)
             for (int i = 0; i < H; i++)

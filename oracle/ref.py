@@ -159,7 +159,7 @@ def expert_ffn(pool: Pool, row: int, x_bf16: np.ndarray) -> np.ndarray:
 
 def routed(pool: Pool, idx: np.ndarray, w: np.ndarray, x_bf16: np.ndarray, addend=None) -> np.ndarray:
     idx = np.ascontiguousarray(idx, np.int32)
-    w = np.ascontiguousarray(w, np.float32)
+    w = np.ascontiguousarray(w, np.float64)
     x = np.ascontiguousarray(x_bf16, np.uint16)
     T, K = idx.shape
     out = np.zeros((T, pool.H), np.float64)

@@ -181,9 +181,9 @@ def test_worked_split_example_gpu_part():
     H, F = 64, 128
     _, _, pool = _bf16_pool(rng, 4, H, F)
     x = _bf16(rng.standard_normal((1, H)))
-    a = oracle.routed(pool, np.array([[3, -1]], np.int32), np.array([[0.7, 0.3]], np.float32), x)
-    b = oracle.routed(pool, np.array([[3, 0]], np.int32), np.array([[0.7, 0.0]], np.float32), x)
-    c = float(np.float32(0.7)) * oracle.expert_ffn(pool, 3, x[0])
+    a = oracle.routed(pool, np.array([[3, -1]], np.int32), np.array([[0.7, 0.3]]), x)
+    b = oracle.routed(pool, np.array([[3, 0]], np.int32), np.array([[0.7, 0.0]]), x)
+    c = 0.7 * oracle.expert_ffn(pool, 3, x[0])
     np.testing.assert_array_equal(a, b)
     np.testing.assert_allclose(a[0], c, rtol=1e-15)
 
