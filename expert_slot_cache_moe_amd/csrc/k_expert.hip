@@ -1,0 +1,227 @@
+// Routed and shared SwiGLU experts over pool rows (slot ids, or expert ids
+// of a whole layer's pool), bf16 or 4-bit E2M1 weights.
+//
+// What is computed (FreeToken issue #753, sections "Problem in upstream
+// today" and "What we changed"; FreeToken PR #491, section 5):
+//   g = W1[r] x, u = W3[r] x (fp32 accumulation), h = bf16(silu(g) * u),
+//   d = W2[r] h, out[t] = bf16(sum_k w[t][k] d[t][k] + addend[t]),
+// summing k in ascending order and skipping -1 routes.  The arithmetic of
+// a route depends only on the bytes of its pool row, never on the row's
+// number, so a slot pool and a streamed layer pool give bit-identical
+// results (FreeToken PR #680, section Tests).
+//
+// Layout and mapping on CDNA4:
+//  - Weights are row-major [rows][cols], so one output element is a dot of
+//    one contiguous weight row with the activation.  A row is read as
+//    16-byte chunks; LPR lanes share a row (LPR = chunks per row, up to
+//    64) so every lane issues full 16-byte loads and a wave reads whole
+//    contiguous rows -- coalesced, no LDS round trip.  The activation
+//    chunks a lane needs are the same for every row it touches and stay
+//    in registers.  Partial sums are reduced across the LPR lanes with
+//    xor shuffles in a fixed order.
+//  - Routes are items: one route (decode, one token), or a group of
+//    routes sharing a pool row (wide steps), so each expert's weights are
+//    read from HBM once per step; the tokens of a group loop over the
+//    weights held in registers.
+//  - The path is HBM-bound at decode sizes (2 flops per weight byte for
+//    bf16), so it runs on the vector ALUs; no GEMM reshaping.
+#include "k_expert.inc"
+
+namespace moe {
+
+// Instantiated in k_expert_bf16.hip and k_expert_e2m1.hip.
+namespace expert_detail {
+#define MOE_EXTERN_FMT(FMT)                                                                        \
+    extern template hipError_t launch_up_fmt<FMT>(const PoolView &, const Items &, int,            \
+                                                  const uint16_t *, uint16_t *, const uint16_t *,  \
+                                                  float *, hipStream_t);                           \
+    extern template hipError_t launch_down_to_d_fmt<FMT>(const PoolView &, const Items &, int,     \
+                                                         const uint16_t *, float *, const float *, \
+                                                         hipStream_t);                             \
+    extern template hipError_t launch_down_fused_fmt<FMT>(const PoolView &, const int32_t *,       \
+                                                          const float *, int, int,                 \
+                                                          const uint16_t *, const float *,         \
+                                                          uint16_t *, hipStream_t);
+MOE_EXTERN_FMT(MOE_FMT_BF16)
+MOE_EXTERN_FMT(MOE_FMT_E2M1)
+#undef MOE_EXTERN_FMT
+}  // namespace expert_detail
+
+using expert_detail::kThreads;
+using expert_detail::kWavesPerBlock;
+
+namespace {
+
+// The ordered combine of per-route down projections (wide steps).
+__global__ __launch_bounds__(kThreads) void combine_kernel(const int32_t *__restrict__ idx,
+                                                           const float *__restrict__ w, int K,
+                                                           int H, int num_rows,
+                                                           const float *__restrict__ d,
+                                                           const float *__restrict__ addend,
+                                                           uint16_t *__restrict__ out) {
+    const int t = blockIdx.y;
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= H) return;
+    float acc = 0.f;
+    for (int k = 0; k < K; ++k) {
+        const int64_t r = (int64_t)t * K + k;
+        const int s = idx[r];
+        if (s < 0 || s >= num_rows) continue;
+        acc = fmaf(w[r], d[r * H + i], acc);
+    }
+    const float v = addend != nullptr ? acc + addend[(int64_t)t * H + i] : acc;
+    out[(int64_t)t * H + i] = f32_to_bf16(v);
+}
+
+// Groups routes by pool row: one workgroup ranks the (row, route) pairs
+// (row ascending, then route) in LDS and writes the group table.
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupWaves = kGroupThreads / kWave;
+
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t *__restrict__ idx,
+                                                              int n, int num_rows,
+                                                              int32_t *__restrict__ n_groups,
+                                                              int32_t *__restrict__ grp_row,
+                                                              int32_t *__restrict__ grp_start,
+                                                              int32_t *__restrict__ grp_count,
+                                                              int32_t *__restrict__ grp_routes) {
+    extern __shared__ __align__(16) int32_t lds[];
+    int32_t *wsum = lds;           // [32]
+    int32_t *key = lds + 32;       // [n]
+    int32_t *skey = key + n;       // [n] sorted keys
+    int32_t *sroute = skey + n;    // [n] routes in sorted order
+    int32_t *gstart = sroute + n;  // [n + 1]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    constexpr int kInvalid = 0x7fffffff;
+
+    for (int i = tid; i < n; i += kGroupThreads) {
+        const int r = idx[i];
+        key[i] = (r >= 0 && r < num_rows) ? r : kInvalid;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kGroupThreads) {
+        const int ki = key[i];
+        int rank = 0;
+        for (int j = 0; j < n; ++j) {
+            const int kj = key[j];
+            rank += (kj < ki) || (kj == ki && j < i);
+        }
+        skey[rank] = ki;
+        sroute[rank] = i;
+    }
+    __syncthreads();
+
+    int ng = 0, nvalid = 0;
+    for (int base = 0; base < n; base += kGroupThreads) {
+        const int i = base + tid;
+        const bool valid = i < n && skey[i] != kInvalid;
+        const bool head = valid && (i == 0 || skey[i - 1] != skey[i]);
+        const uint64_t mh = __ballot(head), mv = __ballot(valid);
+        const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(mh >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mh, 0u));
+        if (lane == 0) {
+            wsum[wave] = __popcll(mh);
+            wsum[16 + wave] = __popcll(mv);
+        }
+        __syncthreads();
+        int off = 0, toth = 0, totv = 0;
+        for (int w = 0; w < kGroupWaves; ++w) {
+            off += (w < wave) ? wsum[w] : 0;
+            toth += wsum[w];
+            totv += wsum[16 + w];
+        }
+        __syncthreads();
+        if (head) {
+            gstart[ng + off + pre] = i;
+            grp_row[ng + off + pre] = skey[i];
+            grp_start[ng + off + pre] = i;
+        }
+        ng += toth;
+        nvalid += totv;
+    }
+    __syncthreads();
+    for (int g = tid; g < ng; g += kGroupThreads)
+        grp_count[g] = (g + 1 < ng ? gstart[g + 1] : nvalid) - gstart[g];
+    for (int i = tid; i < nvalid; i += kGroupThreads) grp_routes[i] = sroute[i];
+    if (tid == 0) *n_groups = ng;
+}
+
+bool chunks_ok(int chunks, int max_chunks) {
+    switch (chunks) {
+    case 2: case 4: case 8: case 16: case 32: case 64: case 128: case 256: case 512:
+        return chunks <= max_chunks;
+    default: return false;
+    }
+}
+
+int epc(int fmt) { return fmt == MOE_FMT_BF16 ? 8 : 32; }
+int max_chunks(int fmt) {
+    return fmt == MOE_FMT_BF16 ? expert_detail::MaxChunks<MOE_FMT_BF16>::v
+                               : expert_detail::MaxChunks<MOE_FMT_E2M1>::v;
+}
+
+}  // namespace
+
+bool expert_shape_supported(int fmt, int H, int F) {
+    if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_E2M1) return false;
+    if (H <= 0 || F <= 0 || H % epc(fmt) || F % epc(fmt)) return false;
+    // the shared gate reads H in 8-element chunks
+    if (H % 8) return false;
+    return chunks_ok(H / epc(fmt), max_chunks(fmt)) && chunks_ok(F / epc(fmt), max_chunks(fmt));
+}
+
+size_t group_lds_bytes(int n) { return (32 + 4 * (size_t)n + 1) * 4; }
+
+hipError_t group_prepare(size_t lds_bytes) {
+    if (lds_bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&group_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+}
+
+hipError_t launch_group_routes(const int32_t *idx, int routes, int num_rows, int32_t *n_groups,
+                               int32_t *grp_row, int32_t *grp_start, int32_t *grp_count,
+                               int32_t *grp_routes, hipStream_t s) {
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), group_lds_bytes(routes), s, idx,
+                       routes, num_rows, n_groups, grp_row, grp_start, grp_count, grp_routes);
+    return hipGetLastError();
+}
+
+hipError_t launch_up(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
+                     uint16_t *h, const uint16_t *gate_vec, float *gamma, hipStream_t s) {
+    if (max_items <= 0) return hipSuccess;
+    using namespace expert_detail;
+    return pool.fmt == MOE_FMT_BF16
+               ? launch_up_fmt<MOE_FMT_BF16>(pool, items, max_items, x, h, gate_vec, gamma, s)
+               : launch_up_fmt<MOE_FMT_E2M1>(pool, items, max_items, x, h, gate_vec, gamma, s);
+}
+
+hipError_t launch_down_to_d(const PoolView &pool, const Items &items, int max_items,
+                            const uint16_t *h, float *d, const float *gamma, hipStream_t s) {
+    if (max_items <= 0) return hipSuccess;
+    using namespace expert_detail;
+    return pool.fmt == MOE_FMT_BF16
+               ? launch_down_to_d_fmt<MOE_FMT_BF16>(pool, items, max_items, h, d, gamma, s)
+               : launch_down_to_d_fmt<MOE_FMT_E2M1>(pool, items, max_items, h, d, gamma, s);
+}
+
+hipError_t launch_down_fused(const PoolView &pool, const int32_t *idx, const float *w, int T,
+                             int K, const uint16_t *h, const float *addend, uint16_t *out,
+                             hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    using namespace expert_detail;
+    return pool.fmt == MOE_FMT_BF16
+               ? launch_down_fused_fmt<MOE_FMT_BF16>(pool, idx, w, T, K, h, addend, out, s)
+               : launch_down_fused_fmt<MOE_FMT_E2M1>(pool, idx, w, T, K, h, addend, out, s);
+}
+
+hipError_t launch_combine(const int32_t *idx, const float *w, int T, int K, int H, int num_rows,
+                          const float *d, const float *addend, uint16_t *out, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    dim3 grid((H + kThreads - 1) / kThreads, T);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, idx, w, K, H, num_rows, d,
+                       addend, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

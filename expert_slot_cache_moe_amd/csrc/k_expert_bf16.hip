@@ -1,0 +1,15 @@
+// Expert kernels instantiated for the bf16 weight format (see k_expert.inc).
+#include "k_expert.inc"
+
+namespace moe {
+namespace expert_detail {
+template hipError_t launch_up_fmt<MOE_FMT_BF16>(const PoolView &, const Items &, int, const uint16_t *,
+                                         uint16_t *, const uint16_t *, float *, hipStream_t);
+template hipError_t launch_down_to_d_fmt<MOE_FMT_BF16>(const PoolView &, const Items &, int,
+                                                const uint16_t *, float *, const float *,
+                                                hipStream_t);
+template hipError_t launch_down_fused_fmt<MOE_FMT_BF16>(const PoolView &, const int32_t *, const float *,
+                                                 int, int, const uint16_t *, const float *,
+                                                 uint16_t *, hipStream_t);
+}  // namespace expert_detail
+}  // namespace moe

@@ -1,0 +1,804 @@
+// The C ABI (include/moe_cache.h): argument checks, the cache's device
+// state, and the launch sequence of one layer step on the compute and side
+// streams.  Every check happens on the host before any launch, so a
+// failing call launches nothing; launching calls never synchronise and
+// never allocate, so a whole token's layers capture into one hipGraph.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+moe_status_t hip_fail(hipError_t e, const char *what) {
+    return fail(MOE_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call, what)                          \
+    do {                                             \
+        hipError_t e_ = (call);                      \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+void row_bytes_of(int fmt, int H, int F, int64_t rb[MOE_MAX_BANKS], int *nb) {
+    for (int b = 0; b < MOE_MAX_BANKS; ++b) rb[b] = 0;
+    if (fmt == MOE_FMT_BF16) {
+        rb[0] = (int64_t)2 * F * H * 2;
+        rb[1] = (int64_t)H * F * 2;
+        *nb = 2;
+    } else {
+        rb[0] = (int64_t)2 * F * H / 2;
+        rb[1] = (int64_t)2 * F * H / 16;
+        rb[2] = 4;
+        rb[3] = (int64_t)H * F / 2;
+        rb[4] = (int64_t)H * F / 16;
+        rb[5] = 4;
+        *nb = 6;
+    }
+}
+
+// Workspace of the routed experts for n = T*K routes.
+struct RoutedWs {
+    size_t h, d, ngroups, grp_row, grp_start, grp_count, grp_routes, total;
+};
+
+RoutedWs routed_ws(int H, int F, int T, int K) {
+    RoutedWs w;
+    const size_t n = (size_t)T * K;
+    size_t off = 0;
+    w.h = off;
+    off += align_up(n * F * 2);
+    w.d = off;
+    off += align_up(std::max(n * H * 4, (size_t)T * 4));
+    w.ngroups = off;
+    off += align_up(4);
+    w.grp_row = off;
+    off += align_up(n * 4);
+    w.grp_start = off;
+    off += align_up(n * 4);
+    w.grp_count = off;
+    off += align_up(n * 4);
+    w.grp_routes = off;
+    off += align_up(n * 4);
+    w.total = off;
+    return w;
+}
+
+constexpr int kMaxTopK = 64;
+constexpr int kMaxRoutedRoutes = 8192;
+
+bool is_capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+    return st == hipStreamCaptureStatusActive;
+}
+
+hipError_t record_timing(hipEvent_t ev, hipStream_t s) {
+    if (is_capturing(s)) return hipEventRecordWithFlags(ev, s, hipEventRecordExternal);
+    return hipEventRecord(ev, s);
+}
+
+}  // namespace
+
+struct moe_cache {
+    moe_cache_desc_t d{};
+    int device = 0;
+    int nb = 0;
+    int64_t rb[MOE_MAX_BANKS] = {};
+    std::vector<const uint8_t *> host_dev;  // [L * nb] device-visible host rows
+    // device state
+    void *state = nullptr;
+    int32_t *res = nullptr, *own = nullptr, *order = nullptr;
+    int32_t *plan_slot = nullptr, *plan_expert = nullptr, *n_miss = nullptr;
+    uint32_t *stamp = nullptr, *clock = nullptr;
+    int64_t *stats = nullptr, *freq = nullptr;
+    int plan_cap = 0;
+    size_t admit_lds = 0;
+    // layer workspace
+    void *ws = nullptr;
+    int32_t *ws_ids = nullptr;
+    float *ws_w = nullptr;
+    float *ws_addend = nullptr;
+    uint8_t *ws_routed = nullptr;
+    size_t ws_routed_bytes = 0;
+    uint8_t *ws_shared = nullptr;
+    size_t ws_shared_bytes = 0;
+    int shared_ffn_cap = 0;
+    // ordering
+    hipStream_t side = nullptr;
+    hipEvent_t ready = nullptr, done = nullptr;
+    int last_layer = -1;
+    int gather_wg = 64;
+    // timing
+    int timing = 0;
+    std::vector<hipEvent_t> tev;     // [L * 4]: gather start/end, routed start/end
+    std::vector<int> trecorded;      // [L]
+};
+
+namespace {
+
+PoolView slot_pool_view(const moe_cache *c) {
+    PoolView pv{};
+    pv.fmt = c->d.weight_format;
+    pv.H = c->d.hidden;
+    pv.F = c->d.ffn;
+    pv.num_rows = c->d.num_slots;
+    for (int b = 0; b < c->nb; ++b) {
+        pv.bank[b] = static_cast<const uint8_t *>(c->d.slot_banks_dev[b]);
+        pv.rb[b] = c->rb[b];
+    }
+    return pv;
+}
+
+moe_status_t pool_view_of(const moe_pool_t *pool, PoolView &pv) {
+    if (!pool) return fail(MOE_INVALID_ARG, "pool is NULL");
+    if (pool->weight_format != MOE_FMT_BF16 && pool->weight_format != MOE_FMT_E2M1)
+        return fail(MOE_INVALID_ARG, "unknown weight format %d", pool->weight_format);
+    if (pool->num_rows < 1) return fail(MOE_INVALID_ARG, "pool has %d rows", pool->num_rows);
+    if (!expert_shape_supported(pool->weight_format, pool->hidden, pool->ffn))
+        return fail(MOE_UNSUPPORTED, "hidden %d / ffn %d not supported for format %d", pool->hidden,
+                    pool->ffn, pool->weight_format);
+    int nb;
+    pv = PoolView{};
+    pv.fmt = pool->weight_format;
+    pv.H = pool->hidden;
+    pv.F = pool->ffn;
+    pv.num_rows = pool->num_rows;
+    row_bytes_of(pv.fmt, pv.H, pv.F, pv.rb, &nb);
+    for (int b = 0; b < nb; ++b) {
+        if (!pool->banks_dev[b]) return fail(MOE_INVALID_ARG, "pool bank %d is NULL", b);
+        if (pv.rb[b] % 16 == 0 && !aligned16(pool->banks_dev[b]))
+            return fail(MOE_INVALID_ARG, "pool bank %d is not 16-byte aligned", b);
+        pv.bank[b] = static_cast<const uint8_t *>(pool->banks_dev[b]);
+    }
+    return MOE_OK;
+}
+
+// The routed experts + combine on one stream (no argument checks).
+hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t *idx,
+                           const float *w, int T, int K, const float *addend, uint16_t *out,
+                           uint8_t *ws, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const RoutedWs L = routed_ws(pv.H, pv.F, T, K);
+    uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
+    const int n = T * K;
+    if (T == 1) {
+        Items it{};
+        it.mode = ITEM_ROUTE;
+        it.K = K;
+        it.n = n;
+        it.idx = idx;
+        hipError_t e = launch_up(pv, it, n, x, h, nullptr, nullptr, s);
+        if (e != hipSuccess) return e;
+        return launch_down_fused(pv, idx, w, T, K, h, addend, out, s);
+    }
+    int32_t *ng = reinterpret_cast<int32_t *>(ws + L.ngroups);
+    int32_t *grow = reinterpret_cast<int32_t *>(ws + L.grp_row);
+    int32_t *gstart = reinterpret_cast<int32_t *>(ws + L.grp_start);
+    int32_t *gcount = reinterpret_cast<int32_t *>(ws + L.grp_count);
+    int32_t *groutes = reinterpret_cast<int32_t *>(ws + L.grp_routes);
+    float *d = reinterpret_cast<float *>(ws + L.d);
+    hipError_t e = launch_group_routes(idx, n, pv.num_rows, ng, grow, gstart, gcount, groutes, s);
+    if (e != hipSuccess) return e;
+    Items it{};
+    it.mode = ITEM_GROUP;
+    it.K = K;
+    it.n = n;
+    it.n_groups = ng;
+    it.grp_row = grow;
+    it.grp_start = gstart;
+    it.grp_count = gcount;
+    it.grp_routes = groutes;
+    const int max_items = std::min(n, pv.num_rows);
+    e = launch_up(pv, it, max_items, x, h, nullptr, nullptr, s);
+    if (e != hipSuccess) return e;
+    e = launch_down_to_d(pv, it, max_items, h, d, nullptr, s);
+    if (e != hipSuccess) return e;
+    return launch_combine(idx, w, T, K, pv.H, pv.num_rows, d, addend, out, s);
+}
+
+hipError_t shared_sequence(const moe_shared_t *sh, int H, int Fs, const uint16_t *x, int T,
+                           float *addend, uint8_t *ws, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    PoolView pv{};
+    pv.fmt = MOE_FMT_BF16;
+    pv.H = H;
+    pv.F = Fs;
+    pv.num_rows = 1;
+    pv.bank[0] = static_cast<const uint8_t *>(sh->w13_dev);
+    pv.bank[1] = static_cast<const uint8_t *>(sh->w2_dev);
+    pv.rb[0] = (int64_t)4 * Fs * H;
+    pv.rb[1] = (int64_t)2 * H * Fs;
+    const RoutedWs L = routed_ws(H, Fs, T, 1);
+    uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
+    float *gamma = reinterpret_cast<float *>(ws + L.d);
+    Items it{};
+    it.mode = ITEM_ALL;
+    it.K = 1;
+    it.n = T;
+    hipError_t e = launch_up(pv, it, 1, x, h, static_cast<const uint16_t *>(sh->gate_dev), gamma, s);
+    if (e != hipSuccess) return e;
+    return launch_down_to_d(pv, it, 1, h, addend, gamma, s);
+}
+
+moe_status_t check_shared(const moe_shared_t *sh, int H, int F, int *Fs) {
+    if (!sh->w13_dev || !sh->w2_dev || !sh->gate_dev)
+        return fail(MOE_INVALID_ARG, "shared expert has a NULL weight");
+    if (!aligned16(sh->w13_dev) || !aligned16(sh->w2_dev) || !aligned16(sh->gate_dev))
+        return fail(MOE_INVALID_ARG, "shared expert weights must be 16-byte aligned");
+    *Fs = sh->ffn > 0 ? sh->ffn : F;
+    if (sh->ffn < 0) return fail(MOE_INVALID_ARG, "shared ffn %d", sh->ffn);
+    if (!expert_shape_supported(MOE_FMT_BF16, H, *Fs))
+        return fail(MOE_UNSUPPORTED, "shared expert hidden %d / ffn %d not supported", H, *Fs);
+    return MOE_OK;
+}
+
+moe_status_t launch_admit_checked(moe_cache *c, int layer, int32_t *ids, int R, int max_fetch,
+                                  hipStream_t s) {
+    AdmitParams p{};
+    p.ids = ids;
+    p.R = R;
+    p.layer = layer;
+    p.max_fetch = max_fetch;
+    p.E = c->d.num_experts;
+    p.S = c->d.num_slots;
+    p.one_call = c->d.one_call_width;
+    p.query_width = c->d.query_width;
+    p.res = c->res;
+    p.own = c->own;
+    p.stamp = c->stamp;
+    p.order = c->order;
+    p.clock = c->clock;
+    p.stats = c->stats;
+    p.freq = c->freq;
+    p.plan_slot = c->plan_slot;
+    p.plan_expert = c->plan_expert;
+    p.n_miss = c->n_miss;
+    HIP_TRY(launch_admit(p, c->admit_lds, s), "admission launch");
+    c->last_layer = layer;
+    return MOE_OK;
+}
+
+moe_status_t launch_gather_checked(moe_cache *c, hipStream_t s) {
+    if (c->nb == 0) return MOE_OK;
+    GatherParams g{};
+    g.n_miss = c->n_miss;
+    g.plan_slot = c->plan_slot;
+    g.plan_expert = c->plan_expert;
+    g.nb = c->nb;
+    const int unit = gather_unit_bytes();
+    int units = 0;
+    for (int b = 0; b < c->nb; ++b) {
+        g.unit_start[b] = units;
+        units += (int)((c->rb[b] + unit - 1) / unit);
+        g.host[b] = c->host_dev[(size_t)c->last_layer * c->nb + b];
+        g.slot[b] = static_cast<uint8_t *>(c->d.slot_banks_dev[b]);
+        g.rb[b] = c->rb[b];
+    }
+    g.unit_start[c->nb] = units;
+    g.units_per_entry = units;
+    HIP_TRY(launch_gather(g, c->gather_wg, s), "gather launch");
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" {
+
+const char *moe_status_string(moe_status_t s) {
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_INVALID_ARG: return "invalid argument";
+    case MOE_UNSUPPORTED: return "unsupported";
+    case MOE_HIP_ERROR: return "HIP error";
+    case MOE_OUT_OF_MEMORY: return "out of memory";
+    }
+    return "unknown status";
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status_t moe_bank_row_bytes(int32_t weight_format, int32_t hidden, int32_t ffn,
+                                int64_t row_bytes_out[MOE_MAX_BANKS], int32_t *num_banks_out) {
+    if (!row_bytes_out || !num_banks_out) return fail(MOE_INVALID_ARG, "NULL output");
+    if (weight_format != MOE_FMT_BF16 && weight_format != MOE_FMT_E2M1)
+        return fail(MOE_INVALID_ARG, "unknown weight format %d", weight_format);
+    if (hidden < 1 || ffn < 1) return fail(MOE_INVALID_ARG, "hidden/ffn must be >= 1");
+    if (weight_format == MOE_FMT_E2M1 && (hidden % 16 || ffn % 16))
+        return fail(MOE_INVALID_ARG, "4-bit rows need hidden and ffn multiples of 16");
+    int nb;
+    row_bytes_of(weight_format, hidden, ffn, row_bytes_out, &nb);
+    *num_banks_out = nb;
+    return MOE_OK;
+}
+
+moe_status_t moe_query_widths(int32_t R, int32_t E, int32_t one_call_width, int32_t query_width,
+                              int32_t *out_host, int32_t cap, int32_t *n_out) {
+    if (!n_out || (cap > 0 && !out_host)) return fail(MOE_INVALID_ARG, "NULL output");
+    if (R < 0 || E < 1 || one_call_width < 1 || query_width < 1)
+        return fail(MOE_INVALID_ARG, "bad sizes R=%d E=%d widths %d/%d", R, E, one_call_width,
+                    query_width);
+    int n = 0;
+    if (R > 0 && R <= one_call_width) {
+        if (n < cap) out_host[n] = R;
+        n = 1;
+    } else if (R > 0) {
+        const int len = std::min(R, E);
+        for (int start = 0; start < len; start += query_width) {
+            if (n < cap) out_host[n] = std::min(query_width, len - start);
+            ++n;
+        }
+    }
+    *n_out = n;
+    return MOE_OK;
+}
+
+moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
+    if (!d || !out) return fail(MOE_INVALID_ARG, "NULL desc or out");
+    *out = nullptr;
+    if (d->num_layers < 1 || d->num_experts < 1 || d->num_slots < 1)
+        return fail(MOE_INVALID_ARG, "layers/experts/slots must be >= 1");
+    if (d->one_call_width < 1 || d->query_width < 1)
+        return fail(MOE_INVALID_ARG, "one_call_width and query_width must be >= 1");
+    if (d->max_routes < 1) return fail(MOE_INVALID_ARG, "max_routes must be >= 1");
+    if (d->overlap != 0 && d->overlap != 1)
+        return fail(MOE_INVALID_ARG, "overlap must be 0 or 1, got %d", d->overlap);
+    if (d->max_tokens < 0 || d->max_top_k < 0)
+        return fail(MOE_INVALID_ARG, "max_tokens/max_top_k must be >= 0");
+    if (d->gather_workgroups < 0) return fail(MOE_INVALID_ARG, "gather_workgroups < 0");
+    if ((int64_t)d->num_layers * d->num_experts > INT32_MAX)
+        return fail(MOE_INVALID_ARG, "num_layers * num_experts overflows int32");
+
+    moe_cache *c = new moe_cache();
+    c->d = *d;
+    c->d.host_banks_host = nullptr;
+    c->gather_wg = d->gather_workgroups > 0 ? d->gather_workgroups : 64;
+    auto bail = [&](moe_status_t s) {
+        moe_cache_destroy(c);
+        return s;
+    };
+    HIP_TRY(hipGetDevice(&c->device), "hipGetDevice");
+
+    // Weights.
+    if (d->num_banks != 0) {
+        if (d->weight_format != MOE_FMT_BF16 && d->weight_format != MOE_FMT_E2M1) {
+            moe_status_t s = fail(MOE_INVALID_ARG, "unknown weight format %d", d->weight_format);
+            return bail(s);
+        }
+        if (!expert_shape_supported(d->weight_format, d->hidden, d->ffn))
+            return bail(fail(MOE_UNSUPPORTED, "hidden %d / ffn %d not supported for format %d",
+                             d->hidden, d->ffn, d->weight_format));
+        row_bytes_of(d->weight_format, d->hidden, d->ffn, c->rb, &c->nb);
+        if (d->num_banks != c->nb)
+            return bail(fail(MOE_INVALID_ARG, "format %d has %d banks, desc says %d",
+                             d->weight_format, c->nb, d->num_banks));
+        if (!d->host_banks_host) return bail(fail(MOE_INVALID_ARG, "host_banks_host is NULL"));
+        for (int b = 0; b < c->nb; ++b) {
+            if (!d->slot_banks_dev[b] || !aligned16(d->slot_banks_dev[b]))
+                return bail(fail(MOE_INVALID_ARG, "slot bank %d is NULL or not 16-byte aligned", b));
+        }
+        c->host_dev.resize((size_t)d->num_layers * c->nb);
+        for (int l = 0; l < d->num_layers; ++l)
+            for (int b = 0; b < c->nb; ++b) {
+                void *hp = const_cast<void *>(d->host_banks_host[(size_t)l * c->nb + b]);
+                const size_t align = (c->rb[b] % 16 == 0) ? 16 : 4;
+                if (!hp || (reinterpret_cast<uintptr_t>(hp) % align))
+                    return bail(fail(MOE_INVALID_ARG, "host bank (layer %d, bank %d) is NULL or unaligned",
+                                     l, b));
+                void *dp = nullptr;
+                hipError_t e = hipHostGetDevicePointer(&dp, hp, 0);
+                if (e != hipSuccess || !dp) {
+                    (void)hipGetLastError();
+                    return bail(fail(MOE_INVALID_ARG,
+                                     "host bank (layer %d, bank %d) is not pinned, device-mapped host memory",
+                                     l, b));
+                }
+                c->host_dev[(size_t)l * c->nb + b] = static_cast<const uint8_t *>(dp);
+            }
+    }
+
+    // Admission state.
+    int max_lds = 0;
+    HIP_TRY(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device),
+            "device attribute");
+    c->admit_lds = admit_lds_bytes(d->num_experts, d->num_slots, d->max_routes);
+    if (c->admit_lds > (size_t)max_lds)
+        return bail(fail(MOE_UNSUPPORTED, "admission needs %zu B of LDS (E=%d, S=%d, max_routes=%d); device has %d",
+                         c->admit_lds, d->num_experts, d->num_slots, d->max_routes, max_lds));
+    HIP_TRY(admit_prepare(c->admit_lds), "admission LDS attribute");
+
+    const size_t L = d->num_layers, E = d->num_experts, S = d->num_slots;
+    c->plan_cap = (int)std::min<size_t>(E, (size_t)d->max_routes);
+    size_t off = 0;
+    const size_t o_res = off; off += align_up(L * E * 4);
+    const size_t o_own = off; off += align_up(S * 4);
+    const size_t o_stamp = off; off += align_up(S * 4);
+    const size_t o_order = off; off += align_up(S * 4);
+    const size_t o_clock = off; off += align_up(4);
+    const size_t o_stats = off; off += align_up(L * MOE_NUM_STATS * 8);
+    const size_t o_freq = off; off += align_up(L * E * 8);
+    const size_t o_ps = off; off += align_up((size_t)c->plan_cap * 4);
+    const size_t o_pe = off; off += align_up((size_t)c->plan_cap * 4);
+    const size_t o_nm = off; off += align_up(4);
+    {
+        hipError_t e = hipMalloc(&c->state, off);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return bail(fail(MOE_OUT_OF_MEMORY, "cache state (%zu B): %s", off, hipGetErrorString(e)));
+        }
+    }
+    uint8_t *base = static_cast<uint8_t *>(c->state);
+    c->res = reinterpret_cast<int32_t *>(base + o_res);
+    c->own = reinterpret_cast<int32_t *>(base + o_own);
+    c->stamp = reinterpret_cast<uint32_t *>(base + o_stamp);
+    c->order = reinterpret_cast<int32_t *>(base + o_order);
+    c->clock = reinterpret_cast<uint32_t *>(base + o_clock);
+    c->stats = reinterpret_cast<int64_t *>(base + o_stats);
+    c->freq = reinterpret_cast<int64_t *>(base + o_freq);
+    c->plan_slot = reinterpret_cast<int32_t *>(base + o_ps);
+    c->plan_expert = reinterpret_cast<int32_t *>(base + o_pe);
+    c->n_miss = reinterpret_cast<int32_t *>(base + o_nm);
+    {
+        moe_status_t s = MOE_OK;
+        hipError_t e = hipMemset(c->state, 0, off);
+        if (e == hipSuccess) e = hipMemset(c->res, 0xff, L * E * 4);
+        if (e == hipSuccess) e = hipMemset(c->own, 0xff, S * 4);
+        std::vector<int32_t> order(S);
+        std::iota(order.begin(), order.end(), 0);
+        if (e == hipSuccess) e = hipMemcpy(c->order, order.data(), S * 4, hipMemcpyHostToDevice);
+        if (e != hipSuccess) s = hip_fail(e, "cache state init");
+        if (s != MOE_OK) return bail(s);
+    }
+
+    // Layer workspace.
+    if (d->max_tokens > 0) {
+        if (d->max_top_k < 1 || d->max_top_k > kMaxTopK || d->max_top_k > d->num_experts)
+            return bail(fail(MOE_INVALID_ARG, "max_top_k must be in [1, min(64, E)]"));
+        if ((int64_t)d->max_tokens * d->max_top_k > kMaxRoutedRoutes)
+            return bail(fail(MOE_UNSUPPORTED, "max_tokens * max_top_k > %d", kMaxRoutedRoutes));
+        const size_t T = d->max_tokens, K = d->max_top_k, H = std::max(d->hidden, 1);
+        const int F = std::max(d->ffn, 8);
+        c->shared_ffn_cap = F;
+        const RoutedWs rw = routed_ws((int)H, F, (int)T, (int)K);
+        const RoutedWs sw = routed_ws((int)H, c->shared_ffn_cap, (int)T, 1);
+        size_t o = 0;
+        const size_t o_ids = o; o += align_up(T * K * 4);
+        const size_t o_w = o; o += align_up(T * K * 4);
+        const size_t o_add = o; o += align_up(T * H * 4);
+        const size_t o_r = o; o += rw.total;
+        const size_t o_s = o; o += sw.total;
+        hipError_t e = hipMalloc(&c->ws, o);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return bail(fail(MOE_OUT_OF_MEMORY, "layer workspace (%zu B): %s", o, hipGetErrorString(e)));
+        }
+        uint8_t *wb = static_cast<uint8_t *>(c->ws);
+        c->ws_ids = reinterpret_cast<int32_t *>(wb + o_ids);
+        c->ws_w = reinterpret_cast<float *>(wb + o_w);
+        c->ws_addend = reinterpret_cast<float *>(wb + o_add);
+        c->ws_routed = wb + o_r;
+        c->ws_routed_bytes = rw.total;
+        c->ws_shared = wb + o_s;
+        c->ws_shared_bytes = sw.total;
+        const size_t glds = group_lds_bytes((int)(T * K));
+        if (glds > (size_t)max_lds) return bail(fail(MOE_UNSUPPORTED, "route grouping LDS too large"));
+        HIP_TRY(group_prepare(glds), "grouping LDS attribute");
+        if ((int64_t)T * K > d->max_routes)
+            return bail(fail(MOE_INVALID_ARG, "max_tokens * max_top_k > max_routes"));
+    }
+
+    // Side stream and the two events, made before any capture.
+    HIP_TRY(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking), "side stream");
+    HIP_TRY(hipEventCreateWithFlags(&c->ready, hipEventDisableTiming), "ready event");
+    HIP_TRY(hipEventCreateWithFlags(&c->done, hipEventDisableTiming), "done event");
+    c->tev.assign((size_t)d->num_layers * 4, nullptr);
+    c->trecorded.assign(d->num_layers, 0);
+    HIP_TRY(hipDeviceSynchronize(), "create sync");
+    *out = c;
+    return MOE_OK;
+}
+
+void moe_cache_destroy(moe_cache_t *c) {
+    if (!c) return;
+    (void)hipDeviceSynchronize();
+    for (hipEvent_t e : c->tev)
+        if (e) (void)hipEventDestroy(e);
+    if (c->ready) (void)hipEventDestroy(c->ready);
+    if (c->done) (void)hipEventDestroy(c->done);
+    if (c->side) (void)hipStreamDestroy(c->side);
+    if (c->ws) (void)hipFree(c->ws);
+    if (c->state) (void)hipFree(c->state);
+    delete c;
+}
+
+moe_status_t moe_cache_pool(const moe_cache_t *c, moe_pool_t *pool) {
+    if (!c || !pool) return fail(MOE_INVALID_ARG, "NULL cache or pool");
+    if (c->nb == 0) return fail(MOE_INVALID_ARG, "cache has no weight banks");
+    memset(pool, 0, sizeof *pool);
+    pool->weight_format = c->d.weight_format;
+    pool->hidden = c->d.hidden;
+    pool->ffn = c->d.ffn;
+    pool->num_rows = c->d.num_slots;
+    for (int b = 0; b < c->nb; ++b) pool->banks_dev[b] = c->d.slot_banks_dev[b];
+    return MOE_OK;
+}
+
+moe_status_t moe_topk(const float *logits, int32_t T, int32_t E, int32_t K, int32_t *ids, float *w,
+                      void *stream) {
+    if (T < 0 || E < 1 || K < 1 || K > E || K > kMaxTopK)
+        return fail(MOE_INVALID_ARG, "bad top-k sizes T=%d E=%d K=%d", T, E, K);
+    if (T > 0 && (!logits || !ids || !w)) return fail(MOE_INVALID_ARG, "NULL top-k buffer");
+    HIP_TRY(launch_topk(logits, T, E, K, ids, w, static_cast<hipStream_t>(stream)), "top-k launch");
+    return MOE_OK;
+}
+
+moe_status_t moe_admit(moe_cache_t *c, int32_t layer, int32_t *ids, int32_t R, int32_t max_fetch,
+                       void *stream) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    if (layer < 0 || layer >= c->d.num_layers)
+        return fail(MOE_INVALID_ARG, "layer %d outside [0, %d)", layer, c->d.num_layers);
+    if (R < 0 || R > c->d.max_routes)
+        return fail(MOE_INVALID_ARG, "R=%d outside [0, max_routes=%d]", R, c->d.max_routes);
+    if (R > 0 && !ids) return fail(MOE_INVALID_ARG, "NULL ids");
+    return launch_admit_checked(c, layer, ids, R, max_fetch, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_gather_misses(moe_cache_t *c, void *stream) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    if (c->last_layer < 0) return fail(MOE_INVALID_ARG, "no admission to gather for");
+    return launch_gather_checked(c, static_cast<hipStream_t>(stream));
+}
+
+int64_t moe_routed_workspace_bytes(int32_t weight_format, int32_t hidden, int32_t ffn, int32_t T,
+                                   int32_t K) {
+    (void)weight_format;
+    if (hidden < 1 || ffn < 1 || T < 0 || K < 1) return 0;
+    return (int64_t)routed_ws(hidden, ffn, T, K).total;
+}
+
+moe_status_t moe_routed_decode(const moe_pool_t *pool, const void *x, const int32_t *idx,
+                               const float *w, int32_t T, int32_t K, const float *addend, void *out,
+                               void *ws, int64_t ws_bytes, void *stream) {
+    PoolView pv;
+    moe_status_t s = pool_view_of(pool, pv);
+    if (s != MOE_OK) return s;
+    if (T < 0 || K < 1 || K > kMaxTopK) return fail(MOE_INVALID_ARG, "bad T=%d K=%d", T, K);
+    if ((int64_t)T * K > kMaxRoutedRoutes)
+        return fail(MOE_UNSUPPORTED, "T*K=%lld > %d routes", (long long)T * K, kMaxRoutedRoutes);
+    if (T == 0) return MOE_OK;
+    if (!x || !idx || !w || !out || !ws) return fail(MOE_INVALID_ARG, "NULL routed buffer");
+    if (!aligned16(x)) return fail(MOE_INVALID_ARG, "x must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(MOE_INVALID_ARG, "workspace must be 256-byte aligned");
+    const RoutedWs L = routed_ws(pv.H, pv.F, T, K);
+    if (ws_bytes < (int64_t)L.total)
+        return fail(MOE_INVALID_ARG, "workspace %lld B < %zu B", (long long)ws_bytes, L.total);
+    if (T > 1) {
+        int max_lds = 0;
+        int dev = 0;
+        HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+        HIP_TRY(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev), "attr");
+        const size_t glds = group_lds_bytes(T * K);
+        if (glds > (size_t)max_lds) return fail(MOE_UNSUPPORTED, "too many routes to group");
+        HIP_TRY(group_prepare(glds), "grouping LDS attribute");
+    }
+    HIP_TRY(routed_sequence(pv, static_cast<const uint16_t *>(x), idx, w, T, K, addend,
+                            static_cast<uint16_t *>(out), static_cast<uint8_t *>(ws),
+                            static_cast<hipStream_t>(stream)),
+            "routed launch");
+    return MOE_OK;
+}
+
+moe_status_t moe_shared_expert(const moe_shared_t *sh, int32_t H, const void *x, int32_t T,
+                               float *addend, void *ws, int64_t ws_bytes, void *stream) {
+    if (!sh) return fail(MOE_INVALID_ARG, "NULL shared expert");
+    int Fs;
+    moe_status_t s = check_shared(sh, H, 0, &Fs);
+    if (s != MOE_OK) return s;
+    if (sh->ffn == 0) return fail(MOE_INVALID_ARG, "standalone shared expert needs ffn > 0");
+    if (T < 0) return fail(MOE_INVALID_ARG, "T < 0");
+    if (T == 0) return MOE_OK;
+    if (!x || !addend || !ws) return fail(MOE_INVALID_ARG, "NULL shared buffer");
+    if (!aligned16(x)) return fail(MOE_INVALID_ARG, "x must be 16-byte aligned");
+    const RoutedWs L = routed_ws(H, Fs, T, 1);
+    if (ws_bytes < (int64_t)L.total)
+        return fail(MOE_INVALID_ARG, "workspace %lld B < %zu B", (long long)ws_bytes, L.total);
+    HIP_TRY(shared_sequence(sh, H, Fs, static_cast<const uint16_t *>(x), T, addend,
+                            static_cast<uint8_t *>(ws), static_cast<hipStream_t>(stream)),
+            "shared launch");
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, const float *logits,
+                              int32_t T, int32_t K, const moe_shared_t *shared, int32_t max_fetch,
+                              void *out, int32_t *ids_out, float *w_out, void *stream) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    if (c->nb == 0) return fail(MOE_INVALID_ARG, "cache has no weight banks");
+    if (layer < 0 || layer >= c->d.num_layers)
+        return fail(MOE_INVALID_ARG, "layer %d outside [0, %d)", layer, c->d.num_layers);
+    if (T < 0 || T > c->d.max_tokens) return fail(MOE_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, c->d.max_tokens);
+    if (K < 1 || K > c->d.max_top_k || K > c->d.num_experts)
+        return fail(MOE_INVALID_ARG, "K=%d outside [1, %d]", K, c->d.max_top_k);
+    if ((int64_t)T * K > c->d.max_routes) return fail(MOE_INVALID_ARG, "T*K > max_routes");
+    if (T > 0 && (!x || !logits || !out)) return fail(MOE_INVALID_ARG, "NULL layer buffer");
+    if (T > 0 && !aligned16(x)) return fail(MOE_INVALID_ARG, "x must be 16-byte aligned");
+    int Fs = 0;
+    if (shared) {
+        moe_status_t s = check_shared(shared, c->d.hidden, c->d.ffn, &Fs);
+        if (s != MOE_OK) return s;
+        if (Fs > c->shared_ffn_cap)
+            return fail(MOE_UNSUPPORTED, "shared ffn %d > the cache's workspace width %d", Fs, c->shared_ffn_cap);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t *ids = ids_out ? ids_out : c->ws_ids;
+    float *w = w_out ? w_out : c->ws_w;
+    const int R = T * K;
+    const bool timing = c->timing != 0;
+    hipEvent_t *tev = timing ? &c->tev[(size_t)layer * 4] : nullptr;
+    if (timing) {
+        for (int k = 0; k < 4; ++k)
+            if (!tev[k]) HIP_TRY(hipEventCreate(&tev[k]), "timing event");
+    }
+
+    HIP_TRY(launch_topk(logits, T, c->d.num_experts, K, ids, w, s), "top-k launch");
+    moe_status_t st = launch_admit_checked(c, layer, ids, R, max_fetch, s);
+    if (st != MOE_OK) return st;
+    hipStream_t gs = s;
+    if (c->d.overlap) {
+        HIP_TRY(hipEventRecord(c->ready, s), "record ready");
+        HIP_TRY(hipStreamWaitEvent(c->side, c->ready, 0), "side waits ready");
+        gs = c->side;
+    }
+    if (timing) HIP_TRY(record_timing(tev[0], gs), "timing");
+    st = launch_gather_checked(c, gs);
+    if (st != MOE_OK) return st;
+    if (timing) HIP_TRY(record_timing(tev[1], gs), "timing");
+    if (c->d.overlap) HIP_TRY(hipEventRecord(c->done, c->side), "record done");
+
+    // Shared expert and gate on the compute stream, between fork and join.
+    hipError_t e = hipSuccess;
+    if (shared)
+        e = shared_sequence(shared, c->d.hidden, Fs, static_cast<const uint16_t *>(x), T,
+                            c->ws_addend, c->ws_shared, s);
+    // The join is issued even if the shared launch failed, so the side
+    // stream never outlives the step.
+    if (c->d.overlap) {
+        hipError_t je = hipStreamWaitEvent(s, c->done, 0);
+        if (e == hipSuccess) e = je;
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared expert / join");
+
+    if (timing) HIP_TRY(record_timing(tev[2], s), "timing");
+    const PoolView pv = slot_pool_view(c);
+    HIP_TRY(routed_sequence(pv, static_cast<const uint16_t *>(x), ids, w, T, K,
+                            shared ? c->ws_addend : nullptr, static_cast<uint16_t *>(out),
+                            c->ws_routed, s),
+            "routed launch");
+    if (timing) {
+        HIP_TRY(record_timing(tev[3], s), "timing");
+        c->trecorded[layer] = 1;
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_cache_stats(moe_cache_t *c, int32_t layer, int64_t *out, void *stream) {
+    if (!c || !out) return fail(MOE_INVALID_ARG, "NULL cache or output");
+    if (layer < -1 || layer >= c->d.num_layers) return fail(MOE_INVALID_ARG, "layer %d", layer);
+    const int L = c->d.num_layers;
+    std::vector<int64_t> all((size_t)L * MOE_NUM_STATS);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIP_TRY(hipMemcpyAsync(all.data(), c->stats, all.size() * 8, hipMemcpyDeviceToHost, s), "stats copy");
+    HIP_TRY(hipStreamSynchronize(s), "stats sync");
+    for (int k = 0; k < MOE_NUM_STATS; ++k) out[k] = 0;
+    for (int l = 0; l < L; ++l)
+        if (layer < 0 || l == layer)
+            for (int k = 0; k < MOE_NUM_STATS; ++k) out[k] += all[(size_t)l * MOE_NUM_STATS + k];
+    return MOE_OK;
+}
+
+moe_status_t moe_cache_read_state(moe_cache_t *c, int32_t *res, int32_t *own, uint32_t *stamp,
+                                  uint32_t *clock, int64_t *stats, int64_t *freq, int32_t *order) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    const size_t L = c->d.num_layers, E = c->d.num_experts, S = c->d.num_slots;
+    HIP_TRY(hipDeviceSynchronize(), "sync");
+    if (res) HIP_TRY(hipMemcpy(res, c->res, L * E * 4, hipMemcpyDeviceToHost), "copy res");
+    if (own) HIP_TRY(hipMemcpy(own, c->own, S * 4, hipMemcpyDeviceToHost), "copy own");
+    if (stamp) HIP_TRY(hipMemcpy(stamp, c->stamp, S * 4, hipMemcpyDeviceToHost), "copy stamp");
+    if (clock) HIP_TRY(hipMemcpy(clock, c->clock, 4, hipMemcpyDeviceToHost), "copy clock");
+    if (stats) HIP_TRY(hipMemcpy(stats, c->stats, L * MOE_NUM_STATS * 8, hipMemcpyDeviceToHost), "copy stats");
+    if (freq) HIP_TRY(hipMemcpy(freq, c->freq, L * E * 8, hipMemcpyDeviceToHost), "copy freq");
+    if (order) HIP_TRY(hipMemcpy(order, c->order, S * 4, hipMemcpyDeviceToHost), "copy order");
+    return MOE_OK;
+}
+
+moe_status_t moe_cache_write_state(moe_cache_t *c, const int32_t *res, const int32_t *own,
+                                   const uint32_t *stamp, uint32_t clock) {
+    if (!c || !res || !own || !stamp) return fail(MOE_INVALID_ARG, "NULL state");
+    const size_t L = c->d.num_layers, E = c->d.num_experts, S = c->d.num_slots;
+    for (size_t s = 0; s < S; ++s) {
+        if (own[s] < -1 || own[s] >= (int64_t)(L * E)) return fail(MOE_INVALID_ARG, "own[%zu] out of range", s);
+        if (own[s] >= 0 && res[own[s]] != (int32_t)s) return fail(MOE_INVALID_ARG, "res/own disagree at slot %zu", s);
+        if (stamp[s] > clock) return fail(MOE_INVALID_ARG, "stamp[%zu] > clock", s);
+    }
+    for (size_t i = 0; i < L * E; ++i) {
+        if (res[i] < -1 || res[i] >= (int32_t)S) return fail(MOE_INVALID_ARG, "res[%zu] out of range", i);
+        if (res[i] >= 0 && own[res[i]] != (int32_t)i) return fail(MOE_INVALID_ARG, "res/own disagree at %zu", i);
+    }
+    std::vector<int32_t> order(S);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return stamp[a] < stamp[b]; });
+    HIP_TRY(hipDeviceSynchronize(), "sync");
+    HIP_TRY(hipMemcpy(c->res, res, L * E * 4, hipMemcpyHostToDevice), "write res");
+    HIP_TRY(hipMemcpy(c->own, own, S * 4, hipMemcpyHostToDevice), "write own");
+    HIP_TRY(hipMemcpy(c->stamp, stamp, S * 4, hipMemcpyHostToDevice), "write stamp");
+    HIP_TRY(hipMemcpy(c->clock, &clock, 4, hipMemcpyHostToDevice), "write clock");
+    HIP_TRY(hipMemcpy(c->order, order.data(), S * 4, hipMemcpyHostToDevice), "write order");
+    return MOE_OK;
+}
+
+moe_status_t moe_cache_read_plan(moe_cache_t *c, int32_t *ps, int32_t *pe, int32_t cap, int32_t *n) {
+    if (!c || !n || (cap > 0 && (!ps || !pe))) return fail(MOE_INVALID_ARG, "NULL plan output");
+    HIP_TRY(hipDeviceSynchronize(), "sync");
+    int32_t nm = 0;
+    HIP_TRY(hipMemcpy(&nm, c->n_miss, 4, hipMemcpyDeviceToHost), "copy n_miss");
+    *n = nm;
+    const int k = std::min(std::max(cap, 0), nm);
+    if (k > 0) {
+        HIP_TRY(hipMemcpy(ps, c->plan_slot, (size_t)k * 4, hipMemcpyDeviceToHost), "copy plan");
+        HIP_TRY(hipMemcpy(pe, c->plan_expert, (size_t)k * 4, hipMemcpyDeviceToHost), "copy plan");
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_cache_set_timing(moe_cache_t *c, int32_t enable) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    if (enable != 0 && enable != 1) return fail(MOE_INVALID_ARG, "enable must be 0 or 1");
+    c->timing = enable;
+    return MOE_OK;
+}
+
+moe_status_t moe_cache_timing(moe_cache_t *c, float *ms, int32_t *layers_read) {
+    if (!c || !ms || !layers_read) return fail(MOE_INVALID_ARG, "NULL timing output");
+    int n = 0;
+    for (int l = 0; l < c->d.num_layers; ++l) {
+        ms[l * 2] = ms[l * 2 + 1] = -1.f;
+        if (!c->trecorded[l]) continue;
+        hipEvent_t *ev = &c->tev[(size_t)l * 4];
+        HIP_TRY(hipEventSynchronize(ev[3]), "timing sync");
+        HIP_TRY(hipEventSynchronize(ev[1]), "timing sync");
+        HIP_TRY(hipEventElapsedTime(&ms[l * 2], ev[0], ev[1]), "gather elapsed");
+        HIP_TRY(hipEventElapsedTime(&ms[l * 2 + 1], ev[2], ev[3]), "routed elapsed");
+        ++n;
+    }
+    *layers_read = n;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// Internal declarations shared by the gfx950 kernels and the C ABI layer.
+// Nothing here is part of the public interface (include/moe_cache.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_cache.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// 16-byte vector of four dwords (a native vector type, so the nontemporal
+// builtins and the vector memory instructions accept it).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ formats
+
+// bf16 <-> fp32.  bf16 is the upper half of an IEEE binary32.
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+__device__ __forceinline__ float bf16_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// OCP E4M3 (fn): bias 7, exponent 0 subnormal, S.1111.111 NaN.
+__device__ __forceinline__ float e4m3_f(uint32_t v) {
+    uint32_t s = (v & 0x80u) << 24;
+    uint32_t e = (v >> 3) & 0xFu;
+    uint32_t m = v & 7u;
+    float mag;
+    if (e == 0) {
+        mag = (float)m * 0.001953125f;  // m * 2^-9
+    } else {
+        mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    }
+    if (e == 0xFu && m == 7u) mag = __uint_as_float(0x7fc00000u);
+    return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// OCP E2M1: bias 1, exponent 0 subnormal (0 or 0.5).
+__device__ __forceinline__ float e2m1_f(uint32_t n) {
+    uint32_t e = (n >> 1) & 3u;
+    uint32_t m = n & 1u;
+    uint32_t bits = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3f000000u : 0u);
+    return __uint_as_float(bits | ((n & 8u) << 28));
+}
+
+// ------------------------------------------------------------------ reductions
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// ------------------------------------------------------------------ kernel parameters
+
+struct AdmitParams {
+    int32_t *ids;          // [R] in/out
+    int32_t R;
+    int32_t layer;
+    int32_t max_fetch;
+    int32_t E, S;
+    int32_t one_call, query_width;
+    int32_t *res;          // [L*E]
+    int32_t *own;          // [S]
+    uint32_t *stamp;       // [S]
+    int32_t *order;        // [S] slots, least recently used first
+    uint32_t *clock;       // [1]
+    int64_t *stats;        // [L*5]
+    int64_t *freq;         // [L*E]
+    int32_t *plan_slot;    // [min(max_routes, E)]
+    int32_t *plan_expert;
+    int32_t *n_miss;       // [1]
+};
+
+struct GatherParams {
+    const int32_t *n_miss;
+    const int32_t *plan_slot;
+    const int32_t *plan_expert;
+    int32_t nb;
+    int32_t units_per_entry;               // copy units per plan entry, all banks
+    int32_t unit_start[MOE_MAX_BANKS + 1]; // first unit of each bank
+    const uint8_t *host[MOE_MAX_BANKS];    // layer's rows [E][rb], device-visible
+    uint8_t *slot[MOE_MAX_BANKS];          // [S][rb]
+    int64_t rb[MOE_MAX_BANKS];
+};
+
+// Work items of the expert kernels.
+enum ItemMode : int32_t {
+    ITEM_ROUTE = 0,  // item g = route g: pool row idx[g] (skip < 0), token g / K
+    ITEM_GROUP = 1,  // item g = group g of routes that share a pool row
+    ITEM_ALL = 2,    // item 0 = routes 0..n-1 on pool row 0, token = route
+};
+
+struct Items {
+    int32_t mode;
+    int32_t K;                  // routes per token (ITEM_ROUTE)
+    int32_t n;                  // routes (ITEM_ROUTE / ITEM_ALL)
+    const int32_t *idx;         // [routes] pool rows (ITEM_ROUTE)
+    const int32_t *n_groups;    // [1] (ITEM_GROUP)
+    const int32_t *grp_row;     // [groups]
+    const int32_t *grp_start;   // [groups]
+    const int32_t *grp_count;   // [groups]
+    const int32_t *grp_routes;  // [routes] route ids sorted by group
+};
+
+struct PoolView {
+    int32_t fmt, H, F;
+    int32_t num_rows;           // rows in the pool; rows outside [0, num_rows) are skipped
+    const uint8_t *bank[MOE_MAX_BANKS];
+    int64_t rb[MOE_MAX_BANKS];
+};
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
+                       hipStream_t s);
+hipError_t launch_admit(const AdmitParams &p, size_t lds_bytes, hipStream_t s);
+size_t admit_lds_bytes(int E, int S, int max_routes);
+hipError_t admit_prepare(size_t lds_bytes);
+hipError_t launch_gather(const GatherParams &p, int workgroups, hipStream_t s);
+int gather_unit_bytes();
+
+// Expert kernels.  h: bf16 [routes][F]; d: fp32 [routes][H].
+size_t group_lds_bytes(int routes);
+hipError_t group_prepare(size_t lds_bytes);
+hipError_t launch_group_routes(const int32_t *idx, int routes, int num_rows, int32_t *n_groups,
+                               int32_t *grp_row, int32_t *grp_start, int32_t *grp_count,
+                               int32_t *grp_routes, hipStream_t s);
+hipError_t launch_up(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
+                     uint16_t *h, const uint16_t *gate_vec, float *gamma, hipStream_t s);
+hipError_t launch_down_to_d(const PoolView &pool, const Items &items, int max_items,
+                            const uint16_t *h, float *d, const float *gamma, hipStream_t s);
+hipError_t launch_down_fused(const PoolView &pool, const int32_t *idx, const float *w, int T,
+                             int K, const uint16_t *h, const float *addend, uint16_t *out,
+                             hipStream_t s);
+hipError_t launch_combine(const int32_t *idx, const float *w, int T, int K, int H, int num_rows,
+                          const float *d, const float *addend, uint16_t *out, hipStream_t s);
+
+// Shape support of the expert kernels for one matrix width.
+bool expert_shape_supported(int fmt, int H, int F);
+
+}  // namespace moe

@@ -1,0 +1,302 @@
+/*
+ * moe_cache.h -- C ABI of the MI355X (gfx950) offloaded MoE decode step.
+ *
+ * One layer's decode step over an expert slot cache:
+ *   (1) top-k routing, (2) LRU slot-cache admission, (3) the miss gather
+ *   from pinned host memory into device slots, (4) the routed expert
+ *   GEMV / grouped GEMM over slot ids, (5) the gated shared expert and the
+ *   final combine.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] FreeToken PR #491, "refactor(moe): extract hybrid decode
+ *        orchestration", sections 4-5: routes rewritten in place to a GPU
+ *        slot id or -1; a -1 route contributes nothing to the GPU part.
+ *   [P2] FreeToken issue #753, "[Perf] Offloaded decode: overlap the
+ *        expert-miss gather with the same layer's shared expert,
+ *        event-ordered inside the CUDA graph", sections "Problem in
+ *        upstream today" and "What we changed": router -> top-k ->
+ *        admission -> record(ready) -> shared expert + gate -> wait(done)
+ *        -> routed GEMM -> routed + shared on the compute stream; the side
+ *        stream waits for ready, gathers the misses, records done; one
+ *        writer of the slot map; side stream and events made at cache
+ *        construction, before any capture; device-side miss counts.
+ *   [P3] FreeToken PR #680, "fix(moe): admit a wide offloaded decode
+ *        step's experts 128 at a time", section Solution: load_experts
+ *        returns slot ids; one-call width 256; wider steps admitted as
+ *        a sorted fixed-length distinct-expert list in 128-wide queries,
+ *        no host sync; statistics once per step, histogram per route.
+ *   [P4] llama.cpp fork PR #126, "cuda : MoE look-ahead expert prefetch",
+ *        section Consumer: expert ids outside [0, n_experts) are ignored.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers (hipMalloc / torch cuda
+ *     tensors); pointers named *_host are host pointers.  `stream` is a
+ *     hipStream_t passed as void*; NULL is the null stream.
+ *   - Calls that launch work are asynchronous and capturable in a
+ *     hipGraph: they check their arguments on the host only, never
+ *     synchronise and never allocate.  Data conditions found on the
+ *     device (invalid ids, misses with no slot) never fail a call.
+ *   - Every call returns a moe_status_t; the message of the last failure
+ *     on the calling thread is moe_last_error().  Nothing throws.
+ *   - A cache has one writer: moe_admit and moe_layer_decode on one cache
+ *     must be issued from one thread, on one compute stream.
+ */
+#ifndef MOE_CACHE_H
+#define MOE_CACHE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_INVALID_ARG = 1,   /* a bad pointer, size, index or flag        */
+    MOE_UNSUPPORTED = 2,   /* a shape or alignment the kernels lack     */
+    MOE_HIP_ERROR = 3,     /* a HIP runtime call failed                 */
+    MOE_OUT_OF_MEMORY = 4  /* the cache's own device state did not fit  */
+} moe_status_t;
+
+/* Expert weight formats.
+ * MOE_FMT_BF16, two banks per expert row:
+ *   bank 0: w13 [2F][H] bf16, rows 0..F-1 the gate projection, rows
+ *           F..2F-1 the up projection;          row bytes 4*F*H
+ *   bank 1: w2  [H][F]  bf16 (down projection); row bytes 2*H*F
+ * MOE_FMT_E2M1, six banks per expert row (4-bit OCP E2M1 values, one OCP
+ * E4M3 scale per 16 consecutive elements of a row, one fp32 global scale
+ * per matrix; element c of a row sits in byte c/2, even c in the low
+ * nibble):
+ *   bank 0: w13 codes  [2F][H/2]    bank 3: w2 codes  [H][F/2]
+ *   bank 1: w13 scales [2F][H/16]   bank 4: w2 scales [H][F/16]
+ *   bank 2: w13 global fp32         bank 5: w2 global fp32
+ * A weight is code * scale * global. */
+enum { MOE_FMT_BF16 = 0, MOE_FMT_E2M1 = 1 };
+#define MOE_MAX_BANKS 6
+
+/* Statistics slots, per layer (int64 each) [P3 Solution]. */
+enum {
+    MOE_STAT_CALLS = 0,    /* admission steps                                  */
+    MOE_STAT_MET = 1,      /* distinct valid experts of each step              */
+    MOE_STAT_MISSED = 2,   /* distinct experts a query found non-resident      */
+    MOE_STAT_OVERFLOW = 3, /* misses left without a slot (cap or no victim)    */
+    MOE_STAT_INVALID = 4,  /* routes whose id is outside [0, E)                */
+    MOE_NUM_STATS = 5
+};
+
+typedef struct moe_cache moe_cache_t;
+
+typedef struct {
+    int32_t num_layers;       /* L >= 1                                         */
+    int32_t num_experts;      /* E >= 1, routed experts per layer               */
+    int32_t num_slots;        /* S >= 1, device slots shared by all layers      */
+    int32_t hidden;           /* H                                              */
+    int32_t ffn;              /* F, routed expert width                         */
+    int32_t weight_format;    /* MOE_FMT_*                                      */
+    int32_t one_call_width;   /* steps of <= this many routes are one query (256) */
+    int32_t query_width;      /* wider steps: distinct experts this many at a time (128) */
+    int32_t max_routes;       /* upper bound on routes per admission step       */
+    int32_t max_tokens;       /* upper bound on T for moe_layer_decode (0: no layer calls) */
+    int32_t max_top_k;        /* upper bound on K for moe_layer_decode          */
+    int32_t overlap;          /* 1: gather on the library's side stream, forked
+                                 and joined by events around the shared expert;
+                                 0: everything serial on the compute stream.
+                                 Other values are an error. [P2] */
+    int32_t num_banks;        /* 0 (admission only: no gather, no experts) or
+                                 the format's bank count (2 or 6)                */
+    int32_t gather_workgroups;/* workgroups of the gather kernel; 0 = default   */
+    /* host_banks_host[l * num_banks + b]: pinned host pointer (hipHostMalloc /
+       pinned torch tensor) to layer l's rows of bank b, [E][row bytes].  The
+       array is copied at create; the memory stays caller-owned and must
+       outlive the cache.  Layers may share memory. */
+    const void *const *host_banks_host;
+    /* slot_banks_dev[b]: device pointer to bank b of the slot pool,
+       [S][row bytes], caller-owned, 16-byte aligned. */
+    void *slot_banks_dev[MOE_MAX_BANKS];
+} moe_cache_desc_t;
+
+/* A weight pool the routed kernels read: slot banks of a cache, or a whole
+ * layer's experts in device memory (the "streamed" layer). */
+typedef struct {
+    int32_t weight_format;
+    int32_t hidden;
+    int32_t ffn;
+    int32_t num_rows;                        /* rows in each bank              */
+    const void *banks_dev[MOE_MAX_BANKS];    /* [num_rows][row bytes] each     */
+} moe_pool_t;
+
+/* The gated shared expert of a layer [P2 "Problem in upstream today"]:
+ * a bf16 SwiGLU expert plus a [H] -> 1 sigmoid gate. */
+typedef struct {
+    int32_t ffn;              /* shared expert width; 0 = the routed F          */
+    const void *w13_dev;      /* bf16 [2*ffn][H], gate rows then up rows        */
+    const void *w2_dev;       /* bf16 [H][ffn]                                  */
+    const void *gate_dev;     /* bf16 [H]                                       */
+} moe_shared_t;
+
+/* ---------------------------------------------------------------- helpers */
+
+const char *moe_status_string(moe_status_t s);
+/* Message of the last failed call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Bytes per row of each bank of a format; *num_banks_out gets 2 or 6. */
+moe_status_t moe_bank_row_bytes(int32_t weight_format, int32_t hidden, int32_t ffn,
+                                int64_t row_bytes_out[MOE_MAX_BANKS], int32_t *num_banks_out);
+
+/* The widths of the queries one admission step of R routes over E experts
+ * is cut into [P3 Solution]: {R} if R <= one_call_width, else the fixed
+ * length min(R, E) cut into query_width pieces.  Writes at most `cap`
+ * widths to out_host; *n_out gets the count. */
+moe_status_t moe_query_widths(int32_t R, int32_t E, int32_t one_call_width, int32_t query_width,
+                              int32_t *out_host, int32_t cap, int32_t *n_out);
+
+/* ---------------------------------------------------------------- cache */
+
+/* Validates the description, allocates the cache's device state (slot map,
+ * slot owners, stamps, LRU order, clock, miss plan, statistics, histogram,
+ * layer workspace), creates its side stream and its ready/done events --
+ * before any capture -- and leaves every slot empty.  Uses the current
+ * device.  Errors: MOE_INVALID_ARG (bad sizes, null or unaligned
+ * pointers, overlap not 0/1), MOE_UNSUPPORTED (shapes the kernels lack,
+ * LDS overflow), MOE_OUT_OF_MEMORY, MOE_HIP_ERROR. */
+moe_status_t moe_cache_create(const moe_cache_desc_t *desc, moe_cache_t **out);
+
+/* Synchronises the cache's streams and frees what create allocated. */
+void moe_cache_destroy(moe_cache_t *cache);
+
+/* The cache's slot banks as a pool for moe_routed_decode. */
+moe_status_t moe_cache_pool(const moe_cache_t *cache, moe_pool_t *pool_out);
+
+/* ---------------------------------------------------------------- the step */
+
+/* (1) Top-k routing [P2 "What we changed": router, fused top-k].
+ * logits_dev: fp32 [T][E] row-major.  For each row, the K largest logits,
+ * largest first, equal logits lower expert id first, NaN as -infinity;
+ * weights = softmax over the K selected logits (1/K each if all are
+ * -infinity).  ids_dev: int32 [T][K]; w_dev: fp32 [T][K].
+ * Errors: MOE_INVALID_ARG (T < 0, K < 1, K > E, K > 32, null pointers). */
+moe_status_t moe_topk(const float *logits_dev, int32_t T, int32_t E, int32_t K,
+                      int32_t *ids_dev, float *w_dev, void *stream);
+
+/* (2) Admission of one layer step [P3 Solution; P1 sections 4-5].
+ * ids_dev: int32 [R], expert ids in, rewritten in place to the slot now
+ * holding each route's expert, or -1 (invalid id, or a miss left without
+ * a slot).  One clock tick per call.  Steps of R <= one_call_width routes
+ * are one query; wider steps are admitted as the ascending distinct
+ * experts, padded to min(R, E), query_width at a time, and no query
+ * evicts a slot used earlier in the step.  Within a query hits are used
+ * first; misses, ascending, take the least recently used eligible slots
+ * (ties: lower slot id).  max_fetch >= 0 caps the experts fetched this
+ * step (first in plan order); < 0 is no cap.  Writes the miss plan
+ * (slot, expert) and its length on the device for moe_gather_misses, and
+ * the layer's statistics and histogram.  R may be 0 (an empty step).
+ * Errors: MOE_INVALID_ARG (layer outside [0, L), R < 0 or R > max_routes,
+ * null ids).  Launches one kernel on `stream`. */
+moe_status_t moe_admit(moe_cache_t *cache, int32_t layer, int32_t *ids_dev, int32_t R,
+                       int32_t max_fetch, void *stream);
+
+/* (3) The miss gather [P2 "What we changed"].  Copies every bank's host row
+ * of each plan entry of the last moe_admit (layer, expert) into its slot
+ * row, reading pinned host memory over the host link from a kernel; the
+ * miss count is read on the device.  The caller orders it after that
+ * moe_admit (same stream, or an event) and before any reader of the
+ * slots.  A cache without banks makes this a no-op.  Errors:
+ * MOE_INVALID_ARG (no admission yet). */
+moe_status_t moe_gather_misses(moe_cache_t *cache, void *stream);
+
+/* Bytes of device workspace moe_routed_decode needs for T tokens x K
+ * routes over a pool in this format and these widths. */
+int64_t moe_routed_workspace_bytes(int32_t weight_format, int32_t hidden, int32_t ffn,
+                                   int32_t T, int32_t K);
+
+/* (4) Routed experts over pool rows, plus the combine [P2 "What we
+ * changed": routed GEMM, then routed + shared; P1 section 5: -1 routes
+ * add nothing; P3 Tests: the GEMV over slots equals the one over the
+ * streamed layer].  For each token t:
+ *   out[t] = bf16( sum over k ascending with idx[t][k] >= 0 of
+ *                  w[t][k] * W2[r] (silu(W1[r] x_t) * (W3[r] x_t))
+ *                  + addend[t] ),    r = idx[t][k]
+ * x_dev: bf16 [T][H]; idx_dev: int32 [T][K] pool rows (slot ids, or expert
+ * ids over a layer pool), -1 = skip; w_dev: fp32 [T][K]; addend_dev: fp32
+ * [T][H] or NULL; out_dev: bf16 [T][H].  The intermediate activation is
+ * rounded to bf16; dot products accumulate in fp32.  The result for a
+ * route depends only on its pool row's bytes, never on the row's number,
+ * so a slot pool and a layer pool holding the same expert bytes give
+ * bit-identical outputs.  workspace_dev: at least
+ * moe_routed_workspace_bytes(...), 256-byte aligned.  Pool rows in idx
+ * must be < pool->num_rows (checked on the device: larger rows are
+ * skipped like -1).  Errors: MOE_INVALID_ARG, MOE_UNSUPPORTED (H or F
+ * not a supported width for the format). */
+moe_status_t moe_routed_decode(const moe_pool_t *pool, const void *x_dev, const int32_t *idx_dev,
+                               const float *w_dev, int32_t T, int32_t K, const float *addend_dev,
+                               void *out_dev, void *workspace_dev, int64_t workspace_bytes,
+                               void *stream);
+
+/* (5) Gated shared expert alone [P2 "Problem in upstream today"]:
+ * addend[t] = sigmoid(x_t . gate) * shared(x_t), fp32 [T][H], the term
+ * moe_routed_decode adds.  workspace: moe_routed_workspace_bytes(BF16, H,
+ * shared ffn, T, 1) bytes. */
+moe_status_t moe_shared_expert(const moe_shared_t *shared, int32_t hidden, const void *x_dev,
+                               int32_t T, float *addend_dev, void *workspace_dev,
+                               int64_t workspace_bytes, void *stream);
+
+/* The whole layer step, (1)-(5), ordered as on [P2 "What we changed"]:
+ * compute stream: top-k -> admission -> record(ready) -> shared expert
+ * and gate -> wait(done) -> routed experts -> routed + shared; side
+ * stream (overlap = 1): wait(ready) -> gather -> record(done).  With
+ * overlap = 0 the gather runs on the compute stream right after the
+ * admission.  The node set does not depend on the hit pattern, so the
+ * call captures into one hipGraph and replays with device-side counts.
+ * x_dev: bf16 [T][H]; logits_dev: fp32 [T][E]; shared: NULL for a layer
+ * without a shared expert; out_dev: bf16 [T][H]; ids_out_dev: int32
+ * [T][K] slot ids (or NULL); w_out_dev: fp32 [T][K] (or NULL).
+ * Errors: MOE_INVALID_ARG (layer, T > max_tokens, K > max_top_k, T*K >
+ * max_routes, a cache without banks), MOE_UNSUPPORTED. */
+moe_status_t moe_layer_decode(moe_cache_t *cache, int32_t layer, const void *x_dev,
+                              const float *logits_dev, int32_t T, int32_t K,
+                              const moe_shared_t *shared, int32_t max_fetch, void *out_dev,
+                              int32_t *ids_out_dev, float *w_out_dev, void *stream);
+
+/* ---------------------------------------------------------------- inspection */
+
+/* Copies the layer's statistics (layer = -1: sums over layers) into
+ * stats_host[MOE_NUM_STATS].  Synchronises `stream`. */
+moe_status_t moe_cache_stats(moe_cache_t *cache, int32_t layer, int64_t *stats_host, void *stream);
+
+/* Debug snapshot of the admission state into host arrays (any may be
+ * NULL): res [L*E], own [S], stamp [S], clock [1], stats [L*5],
+ * freq [L*E], order [S] (slots from least to most recently used).
+ * Synchronises the device. */
+moe_status_t moe_cache_read_state(moe_cache_t *cache, int32_t *res_host, int32_t *own_host,
+                                  uint32_t *stamp_host, uint32_t *clock_host, int64_t *stats_host,
+                                  int64_t *freq_host, int32_t *order_host);
+
+/* Debug restore of res/own/stamp/clock (stats and histogram are left as
+ * they are).  own must be the inverse of res; the LRU order is rebuilt
+ * from the stamps.  Synchronises the device.  Errors: MOE_INVALID_ARG if
+ * res and own disagree. */
+moe_status_t moe_cache_write_state(moe_cache_t *cache, const int32_t *res_host,
+                                   const int32_t *own_host, const uint32_t *stamp_host,
+                                   uint32_t clock);
+
+/* The miss plan of the last admission: up to cap (slot, expert) pairs and
+ * its length.  Synchronises the device. */
+moe_status_t moe_cache_read_plan(moe_cache_t *cache, int32_t *plan_slot_host,
+                                 int32_t *plan_expert_host, int32_t cap, int32_t *n_miss_host);
+
+/* Optional timing of the layer step's kernels with HIP events recorded on
+ * the stream each kernel runs on (as external event nodes when the step is
+ * captured into a graph).  enable = 1 makes later moe_layer_decode calls
+ * record, for each layer, events around its gather and around its routed
+ * kernels.  moe_cache_timing waits for the most recent recording of every
+ * layer and writes its elapsed times to ms_host[layer * 2 + {0: gather,
+ * 1: routed}] (-1 for a layer never recorded); *layers_read gets the
+ * count.  For measurement runs only. */
+moe_status_t moe_cache_set_timing(moe_cache_t *cache, int32_t enable);
+moe_status_t moe_cache_timing(moe_cache_t *cache, float *ms_host, int32_t *layers_read);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_CACHE_H */

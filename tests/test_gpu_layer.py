@@ -1,0 +1,296 @@
+"""GPU decode-step arithmetic vs the oracle.
+
+Tolerance for floating-point outputs: max |gpu - oracle| <= 2e-2 *
+max |oracle| per output tensor (bf16 operands, fp32 accumulation, bf16
+output, against the oracle's double precision).  Integer results (top-k
+ids, slot ids) must match exactly; cached and streamed layers must match
+bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import expert_slot_cache_moe_amd as m
+from expert_slot_cache_moe_amd import workloads as W
+from expert_slot_cache_moe_amd.layer import SlotCacheLayers
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _bf16_to_f64(t):
+    return t.view(torch.bfloat16).double().cpu().numpy()
+
+
+def _close(got, ref, what=""):
+    scale = np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    assert err <= TOL * scale, f"{what}: max err {err:.3e} > {TOL} * {scale:.3e}"
+
+
+def _dev_u16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+# ---------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("T,E,K", [(1, 8, 2), (37, 256, 8), (50, 640, 6), (600, 160, 2), (3, 4, 4), (2, 64, 64)])
+def test_topk_matches_oracle(T, E, K):
+    g = W.rng(3, "topk", T, E)
+    lg = W.zipf_logits(g, T, E, 1.05)
+    ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    m.moe_topk(torch.from_numpy(lg).cuda(), K, ids, w)
+    oi, ow = oracle.topk(lg, K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oi)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5, atol=1e-7)
+
+
+def test_topk_ties_nan_and_infinities():
+    lg = np.array([[0.5, 2.0, 2.0, np.nan, 2.0, -1.0],
+                   [np.nan, -np.inf, 1.0, np.nan, -np.inf, np.inf],
+                   [-np.inf] * 6], np.float32)
+    K = 4
+    ids = torch.empty((3, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((3, K), dtype=torch.float32, device="cuda")
+    m.moe_topk(torch.from_numpy(lg).cuda(), K, ids, w)
+    oi, ow = oracle.topk(lg, K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oi)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------- routed experts
+
+def _pool_pair(fmt, rows, H, F, seed):
+    banks = W.expert_rows(fmt, W.rng(seed, "pool", fmt, H, F), rows, H, F)
+    dev = [torch.from_numpy(b).cuda() for b in banks]
+    return banks, m.make_pool(fmt, H, F, rows, dev), oracle.Pool(fmt, H, F, banks)
+
+
+def _routed_gpu(pool, x, idx, w, H, addend=None):
+    T, K = idx.shape
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    wsb = m.moe_routed_workspace_bytes(pool.weight_format, pool.hidden, pool.ffn, T, K)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    m.moe_routed_decode(pool, _dev_u16(x), torch.from_numpy(idx).cuda(),
+                        torch.from_numpy(w.astype(np.float32)).cuda(), out, ws,
+                        addend=None if addend is None else torch.from_numpy(addend.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("fmt,H,F,rows,T,K", [
+    (0, 64, 128, 8, 1, 2),          # tiny, decode path
+    (0, 64, 128, 8, 5, 2),          # tiny, grouped path
+    (0, 2048, 512, 12, 1, 8),       # shared-expert decode shape
+    (0, 1024, 256, 40, 24, 2),      # wide bf16 shape, ragged T
+    (1, 1024, 256, 40, 1, 2),       # e2m1, decode path
+    (1, 1024, 256, 40, 33, 2),      # e2m1, grouped path
+    (0, 4096, 1024, 10, 7, 6),      # prefill-chunk shape
+    (1, 64, 64, 6, 3, 3),           # e2m1, smallest rows
+])
+def test_routed_matches_oracle(fmt, H, F, rows, T, K):
+    g = W.rng(4, "routed", fmt, H, T)
+    _, pool, opool = _pool_pair(fmt, rows, H, F, 5)
+    x = W.normal_bf16(g, (T, H))
+    idx = np.stack([g.choice(rows, K, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[g.random((T, K)) < 0.15] = -1
+    w = g.random((T, K))
+    add = g.standard_normal((T, H)) * 0.01
+    out = _routed_gpu(pool, x, idx, w, H, addend=add)
+    ref = oracle.routed(opool, idx, w.astype(np.float32).astype(np.float64), x, addend=add.astype(np.float32).astype(np.float64))
+    _close(_bf16_to_f64(out), ref, f"fmt{fmt} H{H} T{T}")
+
+
+def test_routed_skips_minus_one_and_rows_outside_the_pool():
+    """[P1 section 5] a -1 route adds nothing; rows >= num_rows are treated
+    the same way."""
+    _, pool, opool = _pool_pair(0, 4, 64, 128, 6)
+    g = W.rng(4, "skip")
+    x = W.normal_bf16(g, (1, 64))
+    w = np.array([[0.7, 0.3, 0.5]])
+    a = _routed_gpu(pool, x, np.array([[3, -1, 99]], np.int32), w, 64)
+    b = _routed_gpu(pool, x, np.array([[3, -1, -1]], np.int32), w, 64)
+    c = _routed_gpu(pool, x, np.array([[3, 0, 0]], np.int32), np.array([[0.7, 0.0, 0.0]]), 64)
+    assert torch.equal(a, b) and torch.equal(a, c)
+    ref = oracle.routed(opool, np.array([[3, -1, -1]], np.int32), np.float32(w).astype(np.float64), x)
+    _close(_bf16_to_f64(a), ref)
+
+
+def test_routed_empty_batch_is_a_noop():
+    _, pool, _ = _pool_pair(0, 4, 64, 128, 6)
+    out = torch.full((1, 64), 7, dtype=torch.int16, device="cuda")
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((0, 64), dtype=torch.int16, device="cuda")
+    m.moe_routed_decode(pool, x, torch.zeros((0, 2), dtype=torch.int32, device="cuda"),
+                        torch.zeros((0, 2), device="cuda"), out, ws)
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+
+
+# ---------------------------------------------------------------- shared expert
+
+def test_shared_expert_matches_oracle():
+    H, F, T = 2048, 512, 3
+    g = W.rng(6, "shared")
+    w13 = W.normal_bf16(g, 2 * F * H, 0.02)
+    w2 = W.normal_bf16(g, H * F, 0.02)
+    gate = W.normal_bf16(g, H, 0.02)
+    x = W.normal_bf16(g, (T, H))
+    sh = m.make_shared(_dev_u16(w13), _dev_u16(w2), _dev_u16(gate), ffn=F)
+    add = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.moe_routed_workspace_bytes(0, H, F, T, 1), dtype=torch.uint8, device="cuda")
+    m.moe_shared_expert(sh, H, _dev_u16(x), add, ws)
+    torch.cuda.synchronize()
+    _, ref = oracle.shared(H, F, w13, w2, gate, x)
+    _close(add.cpu().numpy(), ref, "shared")
+
+
+# ---------------------------------------------------------------- gather, layers
+
+def _tiny_layers(overlap, shared, seed=0, one=256, qw=128, fmt=0, L=1, E=8, S=4, H=64, F=128, T=1, K=2):
+    g = W.rng(seed, "layers", fmt, L, E, H)
+    host = [W.expert_rows(fmt, g, E, H, F) for _ in range(L)]
+    sh = None
+    if shared:
+        sh = [(W.normal_bf16(g, 2 * F * H, 0.02), W.normal_bf16(g, H * F, 0.02), W.normal_bf16(g, H, 0.02))
+              for _ in range(L)]
+    lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, fmt=fmt, host_rows=host,
+                          shared=sh, max_tokens=T, max_top_k=K, overlap=overlap,
+                          one_call_width=one, query_width=qw)
+    return lay, host, sh
+
+
+def _oracle_layer(oc, host, sh, layer, x, lg, K, fmt, H, F, max_fetch=-1):
+    ids_e, w = oracle.topk(lg, K)
+    T = lg.shape[0]
+    slots = oc.admit(layer, ids_e.reshape(-1), max_fetch).reshape(T, K)
+    add = None
+    if sh is not None:
+        _, add = oracle.shared(H, F, sh[layer][0], sh[layer][1], sh[layer][2], x)
+    idx = np.where(slots >= 0, ids_e, -1)
+    ref = oracle.routed(oracle.Pool(fmt, H, F, host[layer]), idx, w, x, addend=add)
+    return ref, slots, w
+
+
+@pytest.mark.parametrize("overlap", [0, 1])
+@pytest.mark.parametrize("shared", [False, True])
+def test_tiny_layer_decode_32_steps(overlap, shared):
+    lay, host, sh = _tiny_layers(overlap, shared)
+    oc = oracle.OracleCache(1, 8, 4)
+    lgs = W.tiny_logits(0, 32)
+    g = W.rng(0, "tiny", "x")
+    out = torch.empty((1, 64), dtype=torch.int16, device="cuda")
+    ids = torch.empty((1, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, 2), dtype=torch.float32, device="cuda")
+    try:
+        for t in range(32):
+            x = W.normal_bf16(g, (1, 64))
+            lay.decode(0, _dev_u16(x), torch.from_numpy(lgs[t]).cuda(), 2, out, ids_out=ids, w_out=w)
+            torch.cuda.synchronize()
+            ref, slots, ow = _oracle_layer(oc, host, sh, 0, x, lgs[t], 2, 0, 64, 128)
+            np.testing.assert_array_equal(ids.cpu().numpy(), slots, err_msg=f"step {t}")
+            np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5)
+            _close(_bf16_to_f64(out), ref, f"step {t}")
+            # after the gather every route's slot holds its expert's rows
+            for b in range(2):
+                sb = lay.slot_banks[b].cpu().numpy()
+                for s in slots.reshape(-1):
+                    e = oc.own[s]
+                    np.testing.assert_array_equal(sb[s], host[0][b][e])
+    finally:
+        lay.close()
+
+
+def _replicated_rows(fmt, g, E, H, F, distinct):
+    """E expert rows built from `distinct` random rows (row e = row e mod
+    distinct) -- the full-size pools without drawing every weight."""
+    base = W.expert_rows(fmt, g, distinct, H, F)
+    return [np.ascontiguousarray(np.tile(b, (E // distinct + 1, 1))[:E]) for b in base]
+
+
+@pytest.mark.parametrize("fmt,H,F,E,S,T,K,one,qw,distinct,sample", [
+    (0, 1024, 256, 160, 160, 150, 2, 256, 128, 160, 150),   # wide bf16 step
+    (1, 1024, 256, 160, 1100, 600, 2, 256, 128, 40, 64),    # wide e2m1 step over 1100 slots
+    (1, 1024, 256, 160, 160, 600, 2, 3, 3, 40, 64),         # ... one layer's experts, 3 per query
+    (0, 4096, 1024, 256, 256, 42, 6, 3, 3, 8, 6),           # prefill chunk, 3 per query
+    (0, 4096, 1024, 640, 640, 50, 6, 256, 128, 8, 4),       # prefill chunk over 640 experts
+])
+def test_wide_step_cached_equals_streamed_bit_for_bit(fmt, H, F, E, S, T, K, one, qw, distinct, sample):
+    """[P3 Tests] the GEMV over the slots equals the one over the streamed
+    layer exactly; sampled tokens match the oracle."""
+    g = W.rng(7, "wide", fmt, E, T)
+    host = [_replicated_rows(fmt, g, E, H, F, distinct)]
+    lay = SlotCacheLayers(layers=1, experts=E, slots=S, hidden=H, ffn=F, fmt=fmt, host_rows=host,
+                          max_tokens=T, max_top_k=K, one_call_width=one, query_width=qw)
+    try:
+        chosen = np.stack([g.choice(E, K, replace=False) for _ in range(T)])
+        lg = W.forced_logits(g, chosen, E)
+        x = W.normal_bf16(g, (T, H))
+        out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        lay.decode(0, _dev_u16(x), torch.from_numpy(lg).cuda(), K, out, ids_out=ids, w_out=w)
+        torch.cuda.synchronize()
+        st = m.moe_cache_stats(lay.cache, 0)
+        assert st[0] == 1 and st[1] == len(set(chosen.reshape(-1).tolist()))
+        own = m.moe_cache_read_state(lay.cache)["own"]
+        slot_ids = ids.cpu().numpy()
+        assert (slot_ids >= 0).all()
+        experts = own[slot_ids].astype(np.int32)
+        assert (np.sort(experts, 1) == np.sort(chosen, 1)).all()
+        # streamed: the same kernels over the layer's experts, rows = expert ids
+        out2 = torch.empty_like(out)
+        ws = torch.empty(m.moe_routed_workspace_bytes(fmt, H, F, T, K), dtype=torch.uint8, device="cuda")
+        m.moe_routed_decode(lay.streamed_pool(0), _dev_u16(x), torch.from_numpy(experts).cuda(), w, out2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2)
+        rows = np.sort(g.choice(T, min(sample, T), replace=False))
+        ref = oracle.routed(oracle.Pool(fmt, H, F, host[0]), experts[rows],
+                            w.cpu().numpy()[rows].astype(np.float64), x[rows])
+        _close(_bf16_to_f64(out)[rows], ref, "wide")
+    finally:
+        lay.close()
+
+
+def test_graph_replay_matches_eager_over_changing_routes():
+    """A whole token (3 layers) captured as one graph and replayed over 40
+    steps with changing routes equals the same steps run eagerly."""
+    L, E, S, H, F, K = 3, 16, 10, 64, 128, 2
+    mk = lambda: _tiny_layers(1, True, seed=3, L=L, E=E, S=S)[0]
+    graph_l, eager_l = mk(), mk()
+    g = W.rng(3, "graph")
+    steps = 40
+    xs = [W.normal_bf16(g, (L, 1, H)) for _ in range(steps)]
+    lgs = [W.zipf_logits(g, L, E, 1.1).reshape(L, 1, E) for _ in range(steps)]
+    x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
+    out_g = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    out_e = torch.empty_like(out_g)
+    try:
+        s = torch.cuda.Stream()
+        x_st.copy_(torch.from_numpy(xs[0].view(np.int16)))
+        lg_st.copy_(torch.from_numpy(lgs[0]))
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            for l in range(L):
+                graph_l.decode(l, x_st[l], lg_st[l], K, out_g[l])
+        for t in range(steps):
+            x_st.copy_(torch.from_numpy(xs[t].view(np.int16)))
+            lg_st.copy_(torch.from_numpy(lgs[t]))
+            graph.replay()
+            for l in range(L):
+                eager_l.decode(l, x_st[l], lg_st[l], K, out_e[l])
+            torch.cuda.synchronize()
+            assert torch.equal(out_g, out_e), f"step {t}"
+        a = m.moe_cache_read_state(graph_l.cache)
+        b = m.moe_cache_read_state(eager_l.cache)
+        for k in ("res", "own", "stamp", "stats", "freq", "order"):
+            np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+        # capture never ran the step: the graph cache saw exactly `steps` tokens
+        assert a["stats"][:, 0].tolist() == [steps] * L
+    finally:
+        graph_l.close()
+        eager_l.close()
