@@ -346,9 +346,9 @@ def moe_cache_set_timing(cache: Cache, enable: bool) -> None:
 
 
 def moe_cache_timing(cache: Cache) -> np.ndarray:
-    """[L, 2] elapsed ms of each layer's last recorded gather and routed
-    kernels (-1 where never recorded)."""
-    ms = np.zeros(cache.L * 2, np.float32)
+    """[L, 3] elapsed ms of each layer's last recorded admission, gather
+    and routed-expert kernels (-1 where never recorded)."""
+    ms = np.zeros(cache.L * 3, np.float32)
     n = np.zeros(1, np.int32)
     _check(lib().moe_cache_timing(cache.handle, _np_ptr(ms), _np_ptr(n)))
-    return ms.reshape(cache.L, 2)
+    return ms.reshape(cache.L, 3)

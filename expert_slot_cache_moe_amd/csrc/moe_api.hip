@@ -93,15 +93,21 @@ RoutedWs routed_ws(int H, int F, int T, int K) {
 constexpr int kMaxTopK = 64;
 constexpr int kMaxRoutedRoutes = 8192;
 
-bool is_capturing(hipStream_t s) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
-    return st == hipStreamCaptureStatusActive;
-}
-
+// Records a timing event on `s`.  Under stream capture the event becomes an
+// event-record node of the graph being captured, appended after the
+// stream's current capture dependencies, so every replay re-records it.
 hipError_t record_timing(hipEvent_t ev, hipStream_t s) {
-    if (is_capturing(s)) return hipEventRecordWithFlags(ev, s, hipEventRecordExternal);
-    return hipEventRecord(ev, s);
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    hipGraph_t graph = nullptr;
+    const hipGraphNode_t *deps = nullptr;
+    size_t ndeps = 0;
+    hipError_t e = hipStreamGetCaptureInfo_v2(s, &st, nullptr, &graph, &deps, &ndeps);
+    if (e != hipSuccess) return e;
+    if (st != hipStreamCaptureStatusActive) return hipEventRecord(ev, s);
+    hipGraphNode_t node = nullptr;
+    e = hipGraphAddEventRecordNode(&node, graph, deps, ndeps, ev);
+    if (e != hipSuccess) return e;
+    return hipStreamUpdateCaptureDependencies(s, &node, 1, hipStreamSetCaptureDependencies);
 }
 
 }  // namespace
@@ -137,7 +143,7 @@ struct moe_cache {
     int gather_wg = 64;
     // timing
     int timing = 0;
-    std::vector<hipEvent_t> tev;     // [L * 4]: gather start/end, routed start/end
+    std::vector<hipEvent_t> tev;     // [L * 6]: admission, gather, routed start/end
     std::vector<int> trecorded;      // [L]
 };
 
@@ -519,7 +525,7 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     HIP_TRY(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking), "side stream");
     HIP_TRY(hipEventCreateWithFlags(&c->ready, hipEventDisableTiming), "ready event");
     HIP_TRY(hipEventCreateWithFlags(&c->done, hipEventDisableTiming), "done event");
-    c->tev.assign((size_t)d->num_layers * 4, nullptr);
+    c->tev.assign((size_t)d->num_layers * 6, nullptr);
     c->trecorded.assign(d->num_layers, 0);
     HIP_TRY(hipDeviceSynchronize(), "create sync");
     *out = c;
@@ -661,25 +667,23 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
     float *w = w_out ? w_out : c->ws_w;
     const int R = T * K;
     const bool timing = c->timing != 0;
-    hipEvent_t *tev = timing ? &c->tev[(size_t)layer * 4] : nullptr;
-    if (timing) {
-        for (int k = 0; k < 4; ++k)
-            if (!tev[k]) HIP_TRY(hipEventCreate(&tev[k]), "timing event");
-    }
+    hipEvent_t *tev = timing ? &c->tev[(size_t)layer * 6] : nullptr;
 
     HIP_TRY(launch_topk(logits, T, c->d.num_experts, K, ids, w, s), "top-k launch");
+    if (timing) HIP_TRY(record_timing(tev[0], s), "timing");
     moe_status_t st = launch_admit_checked(c, layer, ids, R, max_fetch, s);
     if (st != MOE_OK) return st;
+    if (timing) HIP_TRY(record_timing(tev[1], s), "timing");
     hipStream_t gs = s;
     if (c->d.overlap) {
         HIP_TRY(hipEventRecord(c->ready, s), "record ready");
         HIP_TRY(hipStreamWaitEvent(c->side, c->ready, 0), "side waits ready");
         gs = c->side;
     }
-    if (timing) HIP_TRY(record_timing(tev[0], gs), "timing");
+    if (timing) HIP_TRY(record_timing(tev[2], gs), "timing");
     st = launch_gather_checked(c, gs);
     if (st != MOE_OK) return st;
-    if (timing) HIP_TRY(record_timing(tev[1], gs), "timing");
+    if (timing) HIP_TRY(record_timing(tev[3], gs), "timing");
     if (c->d.overlap) HIP_TRY(hipEventRecord(c->done, c->side), "record done");
 
     // Shared expert and gate on the compute stream, between fork and join.
@@ -695,14 +699,14 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
     }
     if (e != hipSuccess) return hip_fail(e, "shared expert / join");
 
-    if (timing) HIP_TRY(record_timing(tev[2], s), "timing");
+    if (timing) HIP_TRY(record_timing(tev[4], s), "timing");
     const PoolView pv = slot_pool_view(c);
     HIP_TRY(routed_sequence(pv, static_cast<const uint16_t *>(x), ids, w, T, K,
                             shared ? c->ws_addend : nullptr, static_cast<uint16_t *>(out),
                             c->ws_routed, s),
             "routed launch");
     if (timing) {
-        HIP_TRY(record_timing(tev[3], s), "timing");
+        HIP_TRY(record_timing(tev[5], s), "timing");
         c->trecorded[layer] = 1;
     }
     return MOE_OK;
@@ -780,6 +784,10 @@ moe_status_t moe_cache_read_plan(moe_cache_t *c, int32_t *ps, int32_t *pe, int32
 moe_status_t moe_cache_set_timing(moe_cache_t *c, int32_t enable) {
     if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
     if (enable != 0 && enable != 1) return fail(MOE_INVALID_ARG, "enable must be 0 or 1");
+    // events are made here, outside any capture
+    if (enable)
+        for (hipEvent_t &e : c->tev)
+            if (!e) HIP_TRY(hipEventCreate(&e), "timing event");
     c->timing = enable;
     return MOE_OK;
 }
@@ -788,13 +796,13 @@ moe_status_t moe_cache_timing(moe_cache_t *c, float *ms, int32_t *layers_read) {
     if (!c || !ms || !layers_read) return fail(MOE_INVALID_ARG, "NULL timing output");
     int n = 0;
     for (int l = 0; l < c->d.num_layers; ++l) {
-        ms[l * 2] = ms[l * 2 + 1] = -1.f;
+        ms[l * 3] = ms[l * 3 + 1] = ms[l * 3 + 2] = -1.f;
         if (!c->trecorded[l]) continue;
-        hipEvent_t *ev = &c->tev[(size_t)l * 4];
+        hipEvent_t *ev = &c->tev[(size_t)l * 6];
+        HIP_TRY(hipEventSynchronize(ev[5]), "timing sync");
         HIP_TRY(hipEventSynchronize(ev[3]), "timing sync");
-        HIP_TRY(hipEventSynchronize(ev[1]), "timing sync");
-        HIP_TRY(hipEventElapsedTime(&ms[l * 2], ev[0], ev[1]), "gather elapsed");
-        HIP_TRY(hipEventElapsedTime(&ms[l * 2 + 1], ev[2], ev[3]), "routed elapsed");
+        for (int k = 0; k < 3; ++k)
+            HIP_TRY(hipEventElapsedTime(&ms[l * 3 + k], ev[2 * k], ev[2 * k + 1]), "elapsed");
         ++n;
     }
     *layers_read = n;

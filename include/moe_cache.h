@@ -288,11 +288,12 @@ moe_status_t moe_cache_read_plan(moe_cache_t *cache, int32_t *plan_slot_host,
 /* Optional timing of the layer step's kernels with HIP events recorded on
  * the stream each kernel runs on (as external event nodes when the step is
  * captured into a graph).  enable = 1 makes later moe_layer_decode calls
- * record, for each layer, events around its gather and around its routed
- * kernels.  moe_cache_timing waits for the most recent recording of every
- * layer and writes its elapsed times to ms_host[layer * 2 + {0: gather,
- * 1: routed}] (-1 for a layer never recorded); *layers_read gets the
- * count.  For measurement runs only. */
+ * record, for each layer, events around its admission kernel, its gather
+ * and its routed-expert kernels.  moe_cache_timing waits for the most
+ * recent recording of every layer and writes its elapsed times to
+ * ms_host[layer * 3 + {0: admission, 1: gather, 2: routed}] (-1 for a
+ * layer never recorded); *layers_read gets the count.  For measurement
+ * runs only. */
 moe_status_t moe_cache_set_timing(moe_cache_t *cache, int32_t enable);
 moe_status_t moe_cache_timing(moe_cache_t *cache, float *ms_host, int32_t *layers_read);
 

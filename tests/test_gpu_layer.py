@@ -294,3 +294,33 @@ def test_graph_replay_matches_eager_over_changing_routes():
     finally:
         graph_l.close()
         eager_l.close()
+
+
+def test_kernel_timing_events_eager_and_captured():
+    """The optional timing events work in eager mode and as event-record
+    nodes of a captured graph."""
+    L = 2
+    lay, _, _ = _tiny_layers(1, True, seed=5, L=L, E=16, S=10)
+    try:
+        m.moe_cache_set_timing(lay.cache, True)
+        g = W.rng(5, "timing")
+        x = _dev_u16(W.normal_bf16(g, (L, 1, 64)))
+        lg = torch.from_numpy(W.zipf_logits(g, L, 16, 1.1).reshape(L, 1, 16)).cuda()
+        out = torch.empty((L, 1, 64), dtype=torch.int16, device="cuda")
+        for l in range(L):
+            lay.decode(l, x[l], lg[l], 2, out[l])
+        ms = m.moe_cache_timing(lay.cache)
+        assert ms.shape == (L, 3) and (ms >= 0).all()
+        s = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            for l in range(L):
+                lay.decode(l, x[l], lg[l], 2, out[l])
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            ms = m.moe_cache_timing(lay.cache)
+            assert (ms >= 0).all() and (ms < 1000).all()
+        m.moe_cache_set_timing(lay.cache, False)
+    finally:
+        lay.close()
