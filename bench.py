@@ -74,7 +74,7 @@ def traffic_ratios():
     return {k: float(v) for k, v in vals.items() if k.endswith("_ratio")}
 
 
-def build_stack(torch, m, W, seed=0):
+def build_stack(torch, m, W, seed=0, gather_workgroups=0, overlap=1):
     """Pinned host store for 40 x 256 experts, shared experts, the cache."""
     from expert_slot_cache_moe_amd.layer import SlotCacheLayers
 
@@ -97,7 +97,8 @@ def build_stack(torch, m, W, seed=0):
     shared = [(W.normal_bf16(gs, 2 * F * H, 0.02), W.normal_bf16(gs, H * F, 0.02),
                W.normal_bf16(gs, H, 0.02)) for _ in range(L)]
     lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, host_rows=host,
-                          shared=shared, max_tokens=1, max_top_k=K, overlap=1)
+                          shared=shared, max_tokens=1, max_top_k=K, overlap=overlap,
+                          gather_workgroups=gather_workgroups)
     return lay
 
 
@@ -216,6 +217,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-admission", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=6)
+    ap.add_argument("--overlap", type=int, default=2,
+                    help="layer-step schedule passed to the cache (0 serial, 1 side-stream "
+                         "fork/join, 2 two staged launches on one stream)")
+    ap.add_argument("--gather-workgroups", type=int, default=0,
+                    help="workgroups of the miss-gather kernel (0: the library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -232,7 +238,7 @@ def main():
     m.lib()
     torch.cuda.set_device(0)
     W_, K_ = args.warmup, args.steps
-    lay = build_stack(torch, m, W)
+    lay = build_stack(torch, m, W, gather_workgroups=args.gather_workgroups, overlap=args.overlap)
     n_tok = W_ + K_
     t0 = time.time()
     lg_all, x_all = make_trace(torch, W, n_tok)
@@ -262,30 +268,49 @@ def main():
     log(f"[bench] timed {K_} tokens in {dt:.3f}s, {fetched / K_:.1f} misses/token")
 
     # Same tokens again from the same cache state, with HIP events captured
-    # around each layer's admission, gather and routed kernels.
+    # around each layer's kernels, and each layer's fetch count read after
+    # every token, so that layer-steps with misses (host-link bound) and
+    # all-hit layer-steps (HBM bound) are timed apart.
     m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"])
     m.moe_cache_set_timing(lay.cache, True)
     tgraph = capture(torch, lay, x_st, lg_st, out)
-    sums = np.zeros(3)
-    st2 = m.moe_cache_stats(lay.cache)
+    staged = args.overlap == 2
+    adm_ms = 0.0
+    miss_rows, miss_ms, miss_n = 0, 0.0, 0      # layer-steps that fetched
+    hit_ms, hit_n = 0.0, 0                      # layer-steps that fetched nothing
+    prev = m.moe_cache_read_state(lay.cache)["stats"]
     for t in range(W_, n_tok):
         x_st.copy_(x_all[t])
         lg_st.copy_(lg_all[t])
         tgraph.replay()
         torch.cuda.synchronize()
-        sums += m.moe_cache_timing(lay.cache).sum(axis=0)
-    st3 = m.moe_cache_stats(lay.cache)
+        ms = m.moe_cache_timing(lay.cache).astype(np.float64)
+        cur = m.moe_cache_read_state(lay.cache)["stats"]
+        d = cur - prev
+        prev = cur
+        fetched_l = d[:, m.MOE_STAT_MISSED] - d[:, m.MOE_STAT_OVERFLOW]
+        adm_ms += ms[:, 0].sum()
+        fl = fetched_l > 0
+        miss_rows += int(fetched_l.sum())
+        miss_ms += ms[fl, 1].sum()
+        miss_n += int(fl.sum())
+        hit_n += int((~fl).sum())
+        # staged schedule: both stages carry routed work; otherwise only
+        # the routed slot does (the gather launch is empty on a hit)
+        hit_ms += (ms[~fl, 1] + ms[~fl, 2]).sum() if staged else ms[~fl, 2].sum()
     m.moe_cache_set_timing(lay.cache, False)
-    fetched2 = int((st3[2] - st2[2]) - (st3[3] - st2[3]))
     launches = K_ * L
-    adm_us, gat_us, rout_us = sums / launches * 1000.0
-    gather_bytes = fetched2 * ROW_BYTES / launches
-    gather_gbs = gather_bytes / (gat_us * 1e-6) / 1e9
-    gemv_bytes = K * ROW_BYTES + 3 * H * 2 + H * 4      # 8 experts + x, out, addend
-    gemv_gbs = gemv_bytes / (rout_us * 1e-6) / 1e9
+    adm_us = adm_ms / launches * 1000.0
+    gat_us = miss_ms / max(miss_n, 1) * 1000.0
+    gather_bytes = miss_rows * ROW_BYTES / max(miss_n, 1)
+    gather_gbs = gather_bytes / (gat_us * 1e-6) / 1e9 if miss_n else 0.0
+    rout_us = hit_ms / max(hit_n, 1) * 1000.0
+    experts = K + 1 if staged else K                   # the shared expert rides in the stages
+    gemv_bytes = experts * ROW_BYTES + 2 * H * 2 + (E * 4 + H * 4 if staged else H * 4)
+    gemv_gbs = gemv_bytes / (rout_us * 1e-6) / 1e9 if hit_n else 0.0
 
     # host-link ceiling: a pinned hipMemcpyAsync of the same size
-    nbytes = max(int(round(fetched2 / K_)), 1) * ROW_BYTES
+    nbytes = max(int(round(miss_rows / max(miss_n, 1))), 1) * ROW_BYTES
     src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     for _ in range(2):
@@ -335,18 +360,23 @@ def main():
                                "locality; one step = one token = 40 layer-steps in one hipGraph",
                    "layers": L, "experts": E, "top_k": K, "hidden": H, "ffn": F, "slots": S,
                    "batch": 1, "misses_per_token": round(fetched / K_, 2)},
-        "roofline": {"kernel": "gather_kernel (miss gather, pinned host -> device slots)",
+        "roofline": {"kernel": ("stage1_kernel (miss gather + gate/up), layer-steps with misses" if staged
+                                else "gather_kernel (miss gather, pinned host -> device slots)"),
                      "bound": "host-link", "achieved": round(gather_gbs, 2),
                      "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gather_gbs / HOST_LINK_PEAK_GBS, 4),
                      "traffic": round(gather_bytes * ratios["gather_traffic_ratio"]) if ratios else None,
                      "bytes_per_launch": round(gather_bytes), "avg_launch_us": round(gat_us, 2),
-                     "memcpy_h2d_same_size_gbs": round(h2d_gbs, 2)},
-        "roofline_gemv": {"kernel": "routed experts (up_kernel + down_fused_kernel)", "bound": "hbm",
+                     "launches": miss_n, "memcpy_h2d_same_size_gbs": round(h2d_gbs, 2)},
+        "roofline_gemv": {"kernel": ("stage1_kernel + stage2_kernel, all-hit layer-steps (8 routed + "
+                                     "shared expert)" if staged
+                                     else "routed experts (up_kernel + down_fused_kernel), all-hit layer-steps"),
+                          "bound": "hbm",
                           "achieved": round(gemv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                           "traffic": round(gemv_bytes * ratios["routed_traffic_ratio"]) if ratios else None,
-                          "bytes_per_launch": gemv_bytes, "avg_launch_us": round(rout_us, 2)},
+                          "bytes_per_launch": gemv_bytes, "avg_launch_us": round(rout_us, 2),
+                          "launches": hit_n},
         "admission_us_decode": round(adm_us, 2),
         "admission_us": adm,
         "cpu_baseline": cpu,

@@ -21,6 +21,7 @@ MOE_FMT_BF16, MOE_FMT_E2M1 = 0, 1
 MOE_MAX_BANKS = 6
 MOE_NUM_STATS = 5
 STAT_NAMES = ("calls", "met", "missed", "overflow", "invalid")
+MOE_STAT_CALLS, MOE_STAT_MET, MOE_STAT_MISSED, MOE_STAT_OVERFLOW, MOE_STAT_INVALID = range(5)
 
 
 class MoeError(RuntimeError):

@@ -15,6 +15,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # no packed fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit a*b+c fusion: kernels that must agree bit for bit round
+    # alike wherever they are inlined (explicit fmaf still fuses)
+    "-ffp-contract=off",
 ]
 
 

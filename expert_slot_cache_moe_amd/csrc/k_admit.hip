@@ -22,6 +22,14 @@
 //    step the untouched entries are compacted and the used slots appended
 //    in ascending slot order.  No per-step sort of S keys is needed;
 //  - one workgroup is the single writer of the slot map for the step.
+//  - for caches of up to 16384 slots the step runs register-resident: each
+//    thread holds a contiguous run of the LRU order (and those slots'
+//    owners) in registers, loaded once at the start, so every later pass is
+//    one workgroup prefix sum over per-thread counts with no global round
+//    trip; the layer's slot-map row sits in LDS.  The top-k of a few token
+//    rows can be fused in front (one wave per row).
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -64,12 +72,14 @@ __global__ __launch_bounds__(kThreads) void admit_kernel(AdmitParams p) {
     int32_t *vict = missl + E;      // [E] victims of the current query
     int32_t *ids_l = vict + E;      // [R] the step's ids
     uint8_t *touched = reinterpret_cast<uint8_t *>(ids_l + R);  // [S] used this step
+    uint8_t *filled = touched + S;  // [E] expert installed by this step's plan
 
     const int tid = threadIdx.x;
     const int64_t lbase = (int64_t)p.layer * E;
 
     for (int i = tid; i < E; i += kThreads) cnt[i] = 0;
     for (int i = tid; i < S; i += kThreads) touched[i] = 0;
+    for (int i = tid; i < E; i += kThreads) filled[i] = 0;
     if (tid == 0) misc[0] = 0;
     const uint32_t now = p.clock[0] + 1u;
     __syncthreads();
@@ -184,6 +194,8 @@ __global__ __launch_bounds__(kThreads) void admit_kernel(AdmitParams p) {
             p.stamp[s] = now;
             slotof[e] = s;
             touched[s] = 1;
+            filled[e] = 1;
+            cnt[e] = nplan + j;   // the histogram is written; cnt now maps expert -> plan entry
             p.plan_slot[nplan + j] = s;
             p.plan_expert[nplan + j] = e;
         }
@@ -196,7 +208,9 @@ __global__ __launch_bounds__(kThreads) void admit_kernel(AdmitParams p) {
     // Rewrite the routes in place.
     for (int i = tid; i < R; i += kThreads) {
         const int e = ids_l[i];
-        p.ids[i] = (e >= 0 && e < E) ? slotof[e] : -1;
+        const bool valid = e >= 0 && e < E;
+        p.ids[i] = valid ? slotof[e] : -1;
+        if (p.route_plan) p.route_plan[i] = (valid && filled[e]) ? cnt[e] : -1;
     }
 
     // LRU order: slots not used keep their relative order; the used ones
@@ -234,21 +248,360 @@ __global__ __launch_bounds__(kThreads) void admit_kernel(AdmitParams p) {
     }
 }
 
+
+// ------------------------------------------------------------------ register-resident admission
+
+constexpr int kFastMaxP = 16;       // slots per thread: S <= 16384
+constexpr int kTopkMaxPerLane = 16; // fused top-k: E <= 1024
+
+// Exclusive prefix sum of per-thread counts over the workgroup.
+__device__ __forceinline__ int block_scan_count(int v, int32_t *wsum, int &total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int x = wave_inclusive_sum(v);
+    if (lane == kWave - 1) wsum[wave] = x;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int c = wsum[w];
+        woff += (w < wave) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return woff + x - v;
+}
+
+// Order-preserving key of a logit: larger key = larger value; NaN sorts as
+// -infinity and -0 as +0.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Top-K of one row of E <= 1024 logits by one wave: K rounds of a wave
+// maximum over 64-bit (value key, ~index) pairs strictly below the previous
+// pick, i.e. largest first and lower expert id first among equals.  The
+// weights are the softmax over the picks (1/K each if all are -infinity).
+__device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int K,
+                                          int32_t *ids_lds, float *w_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t keys[kTopkMaxPerLane];
+#pragma unroll
+    for (int c = 0; c < kTopkMaxPerLane; ++c) {
+        const int e = lane + kWave * c;
+        keys[c] = e < E ? ((uint64_t)logit_key(row[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)
+                        : 0ull;
+    }
+    uint64_t prev = ~0ull, mine = 0ull;
+    for (int k = 0; k < K; ++k) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int c = 0; c < kTopkMaxPerLane; ++c)
+            if (keys[c] < prev && keys[c] > best) best = keys[c];
+        best = wave_max_u64(best);
+        if (lane == k) mine = best;
+        prev = best;
+    }
+    const float v = key_logit((uint32_t)(mine >> 32));
+    const float m = __shfl(v, 0, kWave);
+    float ex = 0.f;
+    if (lane < K) ex = (m == -INFINITY) ? 1.f : __expf(v - m);
+    float z = ex;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
+    if (lane < K) {
+        ids_lds[lane] = (int32_t)(0xffffffffu - (uint32_t)mine);
+        w_out[lane] = ex / z;
+    }
+}
+
+// Register-resident admission.  p.order holds (slot, owner) pairs here, so
+// the owners of victim candidates arrive with the order itself.  Every
+// write to the persistent state is deferred to the final phase: a barrier
+// waits for a wave's outstanding memory operations, so stores issued
+// between barriers would each cost a memory round trip.
+template <int P>
+__global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
+    extern __shared__ __align__(16) int32_t lds[];
+    const int E = p.E, S = p.S, R = p.R;
+    int32_t *wsum = lds;            // [32]
+    int32_t *misc = lds + 32;       // [16]: 0 invalid routes
+    int32_t *cnt = misc + 16;       // [E] routes per expert
+    int32_t *resl = cnt + E;        // [E] the layer's slot map row, kept current
+    int32_t *dlist = resl + E;      // [E] distinct valid experts, ascending
+    int32_t *missl = dlist + E;     // [E] misses of the current query
+    int32_t *pslot = missl + E;     // [E] the step's plan: slot,
+    int32_t *pold = pslot + E;      // [E]   previous owner of that slot,
+    int32_t *pexp = pold + E;       // [E]   expert installed
+    int32_t *ids_l = pexp + E;      // [R]
+    uint16_t *slot_e = reinterpret_cast<uint16_t *>(ids_l + R);  // [S] expert of a used slot
+    uint8_t *touched = reinterpret_cast<uint8_t *>(slot_e + S);    // [S] slot used this step
+    uint8_t *filled = touched + S;                                 // [E] installed this step
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int64_t lbase = (int64_t)p.layer * E;
+
+    // This thread's run of the LRU order: (slot, owner) pairs.
+    int ord[P], owner[P];
+    const int2 *pairs = reinterpret_cast<const int2 *>(p.order);
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int pos = tid * P + q;
+        const int2 v = pos < S ? pairs[pos] : make_int2(-1, -1);
+        ord[q] = v.x;
+        owner[q] = v.y;
+    }
+    for (int e = tid; e < E; e += kThreads) {
+        resl[e] = p.res[lbase + e];
+        cnt[e] = 0;
+        filled[e] = 0;
+    }
+    for (int i = tid; i < S; i += kThreads) touched[i] = 0;
+    if (tid < 16) misc[tid] = 0;
+    const uint32_t now = p.clock[0] + 1u;
+
+    if (p.logits != nullptr) {
+        for (int t = wave; t < p.T; t += kWaves)
+            wave_topk(p.logits + (int64_t)t * E, E, p.K, ids_l + t * p.K, p.w_out + (int64_t)t * p.K);
+    } else {
+        for (int i = tid; i < R; i += kThreads) ids_l[i] = p.ids[i];
+    }
+    __syncthreads();
+
+    // Histogram of the valid routes; invalid routes counted.
+    int my_invalid = 0;
+    for (int i = tid; i < R; i += kThreads) {
+        const int e = ids_l[i];
+        if (e >= 0 && e < E)
+            atomicAdd(&cnt[e], 1);
+        else
+            ++my_invalid;
+    }
+    if (my_invalid) atomicAdd(&misc[0], my_invalid);
+    __syncthreads();
+
+    // Distinct valid experts, ascending: each thread scans a run of E.
+    const int erun = (E + kThreads - 1) / kThreads;
+    int nD;
+    {
+        int c = 0;
+        for (int q = 0; q < erun; ++q) {
+            const int e = tid * erun + q;
+            c += (e < E && cnt[e] > 0);
+        }
+        int off = block_scan_count(c, wsum, nD);
+        for (int q = 0; q < erun; ++q) {
+            const int e = tid * erun + q;
+            if (e < E && cnt[e] > 0) dlist[off++] = e;
+        }
+    }
+    __syncthreads();
+
+    int qwid, nq;
+    if (R <= p.one_call) {
+        qwid = nD > 0 ? nD : 1;
+        nq = nD > 0 ? 1 : 0;
+    } else {
+        qwid = p.query_width;
+        nq = (nD + qwid - 1) / qwid;
+    }
+
+    int fetched = 0, nplan = 0, nmissed = 0, noverflow = 0;
+    for (int q = 0; q < nq; ++q) {
+        const int qs = q * qwid;
+        const int qn = min(qs + qwid, nD) - qs;
+
+        // Hits are used now; misses, ascending (each thread a run).
+        for (int i = tid; i < qn; i += kThreads) {
+            const int s = resl[dlist[qs + i]];
+            if (s >= 0) touched[s] = 1;
+        }
+        int nm;
+        {
+            const int run = (qn + kThreads - 1) / kThreads;
+            int c = 0;
+            for (int k = 0; k < run; ++k) {
+                const int i = tid * run + k;
+                c += (i < qn && resl[dlist[qs + i]] < 0);
+            }
+            int off = block_scan_count(c, wsum, nm);
+            for (int k = 0; k < run; ++k) {
+                const int i = tid * run + k;
+                if (i < qn && resl[dlist[qs + i]] < 0) missl[off++] = dlist[qs + i];
+            }
+        }
+        nmissed += nm;
+        int allowed = nm;
+        if (p.max_fetch >= 0) allowed = min(nm, max(0, p.max_fetch - fetched));
+
+        // Victims: the first entries of the LRU order not used in this step;
+        // the j-th miss takes the j-th victim.
+        if (allowed > 0) {
+            int c = 0;
+#pragma unroll
+            for (int k = 0; k < P; ++k) c += (ord[k] >= 0 && touched[ord[k]] == 0);
+            int elig;
+            int r = block_scan_count(c, wsum, elig);
+#pragma unroll
+            for (int k = 0; k < P; ++k) {
+                if (ord[k] >= 0 && touched[ord[k]] == 0) {
+                    if (r < allowed) {
+                        const int j = nplan + r;
+                        const int e = missl[r];
+                        pslot[j] = ord[k];
+                        pold[j] = owner[k];
+                        pexp[j] = e;
+                        resl[e] = ord[k];
+                        filled[e] = 1;
+                        const int old = owner[k];
+                        // an expert of this layer losing its slot may belong to a
+                        // later query of this step: it becomes a miss there
+                        if (old >= lbase && old < lbase + E) resl[old - lbase] = -1;
+                    }
+                    ++r;
+                }
+            }
+            const int nv = min(allowed, elig);
+            __syncthreads();
+            for (int j = tid; j < nv; j += kThreads) touched[pslot[nplan + j]] = 1;
+            noverflow += nm - nv;
+            nplan += nv;
+            fetched += nv;
+        } else {
+            noverflow += nm;
+        }
+        __syncthreads();
+    }
+
+    // expert -> plan entry, for the routes' plan indices
+    if (p.route_plan) {
+        for (int j = tid; j < nplan; j += kThreads) missl[pexp[j]] = j;
+        __syncthreads();
+    }
+
+    // ---- final phase: every write to the persistent state.
+    for (int i = tid; i < R; i += kThreads) {
+        const int e = ids_l[i];
+        const bool valid = e >= 0 && e < E;
+        p.ids[i] = valid ? resl[e] : -1;
+        if (p.route_plan) p.route_plan[i] = (valid && filled[e]) ? missl[e] : -1;
+    }
+    for (int e = tid; e < E; e += kThreads) p.res[lbase + e] = resl[e];
+    for (int j = tid; j < nplan; j += kThreads) {
+        const int s = pslot[j], old = pold[j], e = pexp[j];
+        if (old >= 0 && !(old >= lbase && old < lbase + E)) p.res[old] = -1;
+        p.own[s] = (int32_t)(lbase + e);
+        p.plan_slot[j] = s;
+        p.plan_expert[j] = e;
+    }
+    for (int i = tid; i < nD; i += kThreads) {
+        const int e = dlist[i];
+        const int s = resl[e];
+        if (s >= 0) {
+            p.stamp[s] = now;
+            slot_e[s] = (uint16_t)e;
+        }
+        atomicAdd(reinterpret_cast<unsigned long long *>(&p.freq[lbase + e]),
+                  (unsigned long long)cnt[e]);
+    }
+    if (tid == 0) {
+        unsigned long long *st =
+            reinterpret_cast<unsigned long long *>(p.stats + (int64_t)p.layer * MOE_NUM_STATS);
+        atomicAdd(&st[MOE_STAT_CALLS], 1ull);
+        atomicAdd(&st[MOE_STAT_MET], (unsigned long long)nD);
+        atomicAdd(&st[MOE_STAT_MISSED], (unsigned long long)nmissed);
+        atomicAdd(&st[MOE_STAT_OVERFLOW], (unsigned long long)noverflow);
+        atomicAdd(&st[MOE_STAT_INVALID], (unsigned long long)misc[0]);
+        p.clock[0] = now;
+        p.n_miss[0] = nplan;
+    }
+
+    // LRU order: the unused entries keep their order; the used slots follow
+    // in ascending slot order (they share this step's stamp), each owned by
+    // its expert of this layer.  One prefix sum counts both parts.
+    if (nD > 0) {
+        __syncthreads();   // slot_e
+        int cu = 0, ct = 0;
+#pragma unroll
+        for (int k = 0; k < P; ++k) cu += (ord[k] >= 0 && touched[ord[k]] == 0);
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int s = tid * P + k;
+            ct += (s < S && touched[s] != 0);
+        }
+        int tot;
+        const int pre = block_scan_count(cu | (ct << 16), wsum, tot);
+        const int kept = tot & 0xffff;
+        int ou = pre & 0xffff, ot = kept + (pre >> 16);
+        int2 *out = reinterpret_cast<int2 *>(p.order);
+#pragma unroll
+        for (int k = 0; k < P; ++k)
+            if (ord[k] >= 0 && touched[ord[k]] == 0) out[ou++] = make_int2(ord[k], owner[k]);
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            const int s = tid * P + k;
+            if (s < S && touched[s] != 0) out[ot++] = make_int2(s, (int)(lbase + slot_e[s]));
+        }
+    }
+}
+
+int fast_p(int S) {
+    int P = 1;
+    while (P * kThreads < S) P *= 2;
+    return P;
+}
+
 }  // namespace
 
+bool admit_order_pairs(int S) { return fast_p(S) <= kFastMaxP; }
+
+bool admit_fused_topk_supported(int E, int S, int K) {
+    return E <= kWave * kTopkMaxPerLane && K <= kWave && fast_p(S) <= kFastMaxP;
+}
+
 size_t admit_lds_bytes(int E, int S, int max_routes) {
-    size_t words = 32 + 8 + 5 * (size_t)E + (size_t)max_routes;
-    return words * 4 + (((size_t)S + 15) & ~(size_t)15);
+    // the larger of the two kernels' layouts
+    const size_t general = (32 + 8 + 5 * (size_t)E + (size_t)max_routes) * 4 + (size_t)S + (size_t)E;
+    const size_t fast =
+        (32 + 16 + 8 * (size_t)E + (size_t)max_routes) * 4 + 3 * (size_t)S + (size_t)E;
+    return (std::max(general, fast) + 15) & ~(size_t)15;
 }
 
 hipError_t admit_prepare(size_t lds_bytes) {
     if (lds_bytes <= 65536) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&admit_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    const void *kernels[] = {
+        reinterpret_cast<const void *>(&admit_kernel),
+        reinterpret_cast<const void *>(&admit_fast_kernel<1>),
+        reinterpret_cast<const void *>(&admit_fast_kernel<2>),
+        reinterpret_cast<const void *>(&admit_fast_kernel<4>),
+        reinterpret_cast<const void *>(&admit_fast_kernel<8>),
+        reinterpret_cast<const void *>(&admit_fast_kernel<16>),
+    };
+    for (const void *k : kernels) {
+        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_admit(const AdmitParams &p, size_t lds_bytes, hipStream_t s) {
-    hipLaunchKernelGGL(admit_kernel, dim3(1), dim3(kThreads), lds_bytes, s, p);
+    switch (fast_p(p.S)) {
+    case 1: hipLaunchKernelGGL(admit_fast_kernel<1>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
+    case 2: hipLaunchKernelGGL(admit_fast_kernel<2>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
+    case 4: hipLaunchKernelGGL(admit_fast_kernel<4>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
+    case 8: hipLaunchKernelGGL(admit_fast_kernel<8>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
+    case 16: hipLaunchKernelGGL(admit_fast_kernel<16>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
+    default:
+        if (p.logits != nullptr) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(admit_kernel, dim3(1), dim3(kThreads), lds_bytes, s, p);
+    }
     return hipGetLastError();
 }
 

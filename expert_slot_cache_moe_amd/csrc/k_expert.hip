@@ -41,6 +41,7 @@ namespace expert_detail {
     extern template hipError_t launch_down_fused_fmt<FMT>(const PoolView &, const int32_t *,       \
                                                           const float *, int, int,                 \
                                                           const uint16_t *, const float *,         \
+                                                          const float *, const int32_t *,          \
                                                           uint16_t *, hipStream_t);
 MOE_EXTERN_FMT(MOE_FMT_BF16)
 MOE_EXTERN_FMT(MOE_FMT_E2M1)
@@ -206,13 +207,14 @@ hipError_t launch_down_to_d(const PoolView &pool, const Items &items, int max_it
 }
 
 hipError_t launch_down_fused(const PoolView &pool, const int32_t *idx, const float *w, int T,
-                             int K, const uint16_t *h, const float *addend, uint16_t *out,
-                             hipStream_t s) {
+                             int K, const uint16_t *h, const float *addend, const float *d,
+                             const int32_t *route_plan, uint16_t *out, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     using namespace expert_detail;
     return pool.fmt == MOE_FMT_BF16
-               ? launch_down_fused_fmt<MOE_FMT_BF16>(pool, idx, w, T, K, h, addend, out, s)
-               : launch_down_fused_fmt<MOE_FMT_E2M1>(pool, idx, w, T, K, h, addend, out, s);
+               ? launch_down_fused_fmt<MOE_FMT_BF16>(pool, idx, w, T, K, h, addend, d, route_plan, out, s)
+               : launch_down_fused_fmt<MOE_FMT_E2M1>(pool, idx, w, T, K, h, addend, d, route_plan, out,
+                                                     s);
 }
 
 hipError_t launch_combine(const int32_t *idx, const float *w, int T, int K, int H, int num_rows,

@@ -10,6 +10,7 @@ template hipError_t launch_down_to_d_fmt<MOE_FMT_E2M1>(const PoolView &, const I
                                                 hipStream_t);
 template hipError_t launch_down_fused_fmt<MOE_FMT_E2M1>(const PoolView &, const int32_t *, const float *,
                                                  int, int, const uint16_t *, const float *,
-                                                 uint16_t *, hipStream_t);
+                                                 const float *, const int32_t *, uint16_t *,
+                                                 hipStream_t);
 }  // namespace expert_detail
 }  // namespace moe

@@ -90,7 +90,25 @@ RoutedWs routed_ws(int H, int F, int T, int K) {
     return w;
 }
 
+// The device image of the LRU order: slots by (stamp, slot) ascending, as
+// (slot, owner) pairs when the admission keeps pairs.  No stamps: all 0.
+std::vector<int32_t> order_image(int S, const uint32_t *stamp, const int32_t *own) {
+    std::vector<int32_t> slots(S);
+    std::iota(slots.begin(), slots.end(), 0);
+    if (stamp)
+        std::stable_sort(slots.begin(), slots.end(),
+                         [&](int32_t a, int32_t b) { return stamp[a] < stamp[b]; });
+    if (!admit_order_pairs(S)) return slots;
+    std::vector<int32_t> img(2 * (size_t)S);
+    for (int i = 0; i < S; ++i) {
+        img[2 * i] = slots[i];
+        img[2 * i + 1] = own ? own[slots[i]] : -1;
+    }
+    return img;
+}
+
 constexpr int kMaxTopK = 64;
+constexpr int kFusedTopkRows = 32;   // up to this many rows, top-k runs inside the admission
 constexpr int kMaxRoutedRoutes = 8192;
 
 // Records a timing event on `s`.  Under stream capture the event becomes an
@@ -129,8 +147,10 @@ struct moe_cache {
     // layer workspace
     void *ws = nullptr;
     int32_t *ws_ids = nullptr;
+    int32_t *ws_route_plan = nullptr;
     float *ws_w = nullptr;
     float *ws_addend = nullptr;
+    float *ws_gu = nullptr;          // [max_top_k][2F] fetched experts' gate/up dots
     uint8_t *ws_routed = nullptr;
     size_t ws_routed_bytes = 0;
     uint8_t *ws_shared = nullptr;
@@ -202,7 +222,7 @@ hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t 
         it.idx = idx;
         hipError_t e = launch_up(pv, it, n, x, h, nullptr, nullptr, s);
         if (e != hipSuccess) return e;
-        return launch_down_fused(pv, idx, w, T, K, h, addend, out, s);
+        return launch_down_fused(pv, idx, w, T, K, h, addend, nullptr, nullptr, out, s);
     }
     int32_t *ng = reinterpret_cast<int32_t *>(ws + L.ngroups);
     int32_t *grow = reinterpret_cast<int32_t *>(ws + L.grp_row);
@@ -265,9 +285,18 @@ moe_status_t check_shared(const moe_shared_t *sh, int H, int F, int *Fs) {
     return MOE_OK;
 }
 
+// With logits set, the admission computes the top-k of T rows itself
+// (R = T * K) and writes the weights to w.
 moe_status_t launch_admit_checked(moe_cache *c, int layer, int32_t *ids, int R, int max_fetch,
-                                  hipStream_t s) {
+                                  hipStream_t s, int32_t *route_plan = nullptr,
+                                  const float *logits = nullptr, int T = 0, int K = 0,
+                                  float *w = nullptr) {
     AdmitParams p{};
+    p.route_plan = route_plan;
+    p.logits = logits;
+    p.T = T;
+    p.K = K;
+    p.w_out = w;
     p.ids = ids;
     p.R = R;
     p.layer = layer;
@@ -291,8 +320,7 @@ moe_status_t launch_admit_checked(moe_cache *c, int layer, int32_t *ids, int R, 
     return MOE_OK;
 }
 
-moe_status_t launch_gather_checked(moe_cache *c, hipStream_t s) {
-    if (c->nb == 0) return MOE_OK;
+GatherParams gather_params(const moe_cache *c) {
     GatherParams g{};
     g.n_miss = c->n_miss;
     g.plan_slot = c->plan_slot;
@@ -309,7 +337,12 @@ moe_status_t launch_gather_checked(moe_cache *c, hipStream_t s) {
     }
     g.unit_start[c->nb] = units;
     g.units_per_entry = units;
-    HIP_TRY(launch_gather(g, c->gather_wg, s), "gather launch");
+    return g;
+}
+
+moe_status_t launch_gather_checked(moe_cache *c, hipStream_t s) {
+    if (c->nb == 0) return MOE_OK;
+    HIP_TRY(launch_gather(gather_params(c), c->gather_wg, s), "gather launch");
     return MOE_OK;
 }
 
@@ -375,8 +408,8 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     if (d->one_call_width < 1 || d->query_width < 1)
         return fail(MOE_INVALID_ARG, "one_call_width and query_width must be >= 1");
     if (d->max_routes < 1) return fail(MOE_INVALID_ARG, "max_routes must be >= 1");
-    if (d->overlap != 0 && d->overlap != 1)
-        return fail(MOE_INVALID_ARG, "overlap must be 0 or 1, got %d", d->overlap);
+    if (d->overlap < 0 || d->overlap > 2)
+        return fail(MOE_INVALID_ARG, "overlap must be 0, 1 or 2, got %d", d->overlap);
     if (d->max_tokens < 0 || d->max_top_k < 0)
         return fail(MOE_INVALID_ARG, "max_tokens/max_top_k must be >= 0");
     if (d->gather_workgroups < 0) return fail(MOE_INVALID_ARG, "gather_workgroups < 0");
@@ -386,7 +419,7 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     moe_cache *c = new moe_cache();
     c->d = *d;
     c->d.host_banks_host = nullptr;
-    c->gather_wg = d->gather_workgroups > 0 ? d->gather_workgroups : 64;
+    c->gather_wg = d->gather_workgroups > 0 ? d->gather_workgroups : 16;
     auto bail = [&](moe_status_t s) {
         moe_cache_destroy(c);
         return s;
@@ -447,7 +480,7 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     const size_t o_res = off; off += align_up(L * E * 4);
     const size_t o_own = off; off += align_up(S * 4);
     const size_t o_stamp = off; off += align_up(S * 4);
-    const size_t o_order = off; off += align_up(S * 4);
+    const size_t o_order = off; off += align_up(S * 8);
     const size_t o_clock = off; off += align_up(4);
     const size_t o_stats = off; off += align_up(L * MOE_NUM_STATS * 8);
     const size_t o_freq = off; off += align_up(L * E * 8);
@@ -477,9 +510,9 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
         hipError_t e = hipMemset(c->state, 0, off);
         if (e == hipSuccess) e = hipMemset(c->res, 0xff, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->own, 0xff, S * 4);
-        std::vector<int32_t> order(S);
-        std::iota(order.begin(), order.end(), 0);
-        if (e == hipSuccess) e = hipMemcpy(c->order, order.data(), S * 4, hipMemcpyHostToDevice);
+        const std::vector<int32_t> order = order_image(S, nullptr, nullptr);
+        if (e == hipSuccess)
+            e = hipMemcpy(c->order, order.data(), order.size() * 4, hipMemcpyHostToDevice);
         if (e != hipSuccess) s = hip_fail(e, "cache state init");
         if (s != MOE_OK) return bail(s);
     }
@@ -497,8 +530,10 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
         const RoutedWs sw = routed_ws((int)H, c->shared_ffn_cap, (int)T, 1);
         size_t o = 0;
         const size_t o_ids = o; o += align_up(T * K * 4);
+        const size_t o_plan = o; o += align_up(T * K * 4);
         const size_t o_w = o; o += align_up(T * K * 4);
         const size_t o_add = o; o += align_up(T * H * 4);
+        const size_t o_gu = o; o += align_up(K * 2 * (size_t)F * 4);
         const size_t o_r = o; o += rw.total;
         const size_t o_s = o; o += sw.total;
         hipError_t e = hipMalloc(&c->ws, o);
@@ -508,8 +543,10 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
         }
         uint8_t *wb = static_cast<uint8_t *>(c->ws);
         c->ws_ids = reinterpret_cast<int32_t *>(wb + o_ids);
+        c->ws_route_plan = reinterpret_cast<int32_t *>(wb + o_plan);
         c->ws_w = reinterpret_cast<float *>(wb + o_w);
         c->ws_addend = reinterpret_cast<float *>(wb + o_add);
+        c->ws_gu = reinterpret_cast<float *>(wb + o_gu);
         c->ws_routed = wb + o_r;
         c->ws_routed_bytes = rw.total;
         c->ws_shared = wb + o_s;
@@ -669,13 +706,56 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
     const bool timing = c->timing != 0;
     hipEvent_t *tev = timing ? &c->tev[(size_t)layer * 6] : nullptr;
 
-    HIP_TRY(launch_topk(logits, T, c->d.num_experts, K, ids, w, s), "top-k launch");
+    // Few token rows: the top-k runs inside the admission kernel.
+    const bool fused_topk =
+        T <= kFusedTopkRows && admit_fused_topk_supported(c->d.num_experts, c->d.num_slots, K);
+    if (!fused_topk) HIP_TRY(launch_topk(logits, T, c->d.num_experts, K, ids, w, s), "top-k launch");
     if (timing) HIP_TRY(record_timing(tev[0], s), "timing");
-    moe_status_t st = launch_admit_checked(c, layer, ids, R, max_fetch, s);
+    moe_status_t st = fused_topk ? launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan,
+                                                        logits, T, K, w)
+                                 : launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan);
     if (st != MOE_OK) return st;
     if (timing) HIP_TRY(record_timing(tev[1], s), "timing");
+    if (c->d.overlap == 2 && T == 1 && stage_supported(c->d.weight_format, c->d.hidden, c->d.ffn) &&
+        (!shared || Fs == c->d.ffn)) {
+        // One stream, two launches: the gather overlaps the shared expert and
+        // the resident routes inside stage 1.
+        const PoolView pv = slot_pool_view(c);
+        const RoutedWs rw = routed_ws(pv.H, pv.F, T, K);
+        PoolView spv{};
+        uint16_t *hs = nullptr;
+        float *gamma = nullptr;
+        if (shared) {
+            spv.fmt = MOE_FMT_BF16;
+            spv.H = c->d.hidden;
+            spv.F = Fs;
+            spv.num_rows = 1;
+            spv.bank[0] = static_cast<const uint8_t *>(shared->w13_dev);
+            spv.bank[1] = static_cast<const uint8_t *>(shared->w2_dev);
+            spv.rb[0] = (int64_t)4 * Fs * c->d.hidden;
+            spv.rb[1] = (int64_t)2 * c->d.hidden * Fs;
+            const RoutedWs sw = routed_ws(c->d.hidden, Fs, T, 1);
+            hs = reinterpret_cast<uint16_t *>(c->ws_shared + sw.h);
+            gamma = reinterpret_cast<float *>(c->ws_shared + sw.d);
+        }
+        for (int which = 1; which <= 2; ++which) {
+            if (timing) HIP_TRY(record_timing(tev[2 * which], s), "timing");
+            HIP_TRY(launch_stages(gather_params(c), c->gather_wg, c->ws_gu, pv, ids, w,
+                                  c->ws_route_plan, K, static_cast<const uint16_t *>(x),
+                                  reinterpret_cast<uint16_t *>(c->ws_routed + rw.h),
+                                  shared ? &spv : nullptr, hs,
+                                  shared ? static_cast<const uint16_t *>(shared->gate_dev)
+                                         : nullptr,
+                                  gamma, static_cast<uint16_t *>(out), which, s),
+                    "stage launch");
+            if (timing) HIP_TRY(record_timing(tev[2 * which + 1], s), "timing");
+        }
+        if (timing) c->trecorded[layer] = 1;
+        return MOE_OK;
+    }
+    const bool two_streams = c->d.overlap == 1;
     hipStream_t gs = s;
-    if (c->d.overlap) {
+    if (two_streams) {
         HIP_TRY(hipEventRecord(c->ready, s), "record ready");
         HIP_TRY(hipStreamWaitEvent(c->side, c->ready, 0), "side waits ready");
         gs = c->side;
@@ -684,27 +764,51 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
     st = launch_gather_checked(c, gs);
     if (st != MOE_OK) return st;
     if (timing) HIP_TRY(record_timing(tev[3], gs), "timing");
-    if (c->d.overlap) HIP_TRY(hipEventRecord(c->done, c->side), "record done");
+    if (two_streams) HIP_TRY(hipEventRecord(c->done, c->side), "record done");
 
-    // Shared expert and gate on the compute stream, between fork and join.
+    // Between fork and join, on the compute stream: the shared expert and
+    // its gate, and (single token) the routed experts whose slots were
+    // already resident -- none of these reads a slot the gather writes.
+    const PoolView pv = slot_pool_view(c);
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    const bool split = two_streams && T == 1;
+    const RoutedWs rw = routed_ws(pv.H, pv.F, T, K);
+    uint16_t *h = reinterpret_cast<uint16_t *>(c->ws_routed + rw.h);
+    float *dr = reinterpret_cast<float *>(c->ws_routed + rw.d);
     hipError_t e = hipSuccess;
-    if (shared)
-        e = shared_sequence(shared, c->d.hidden, Fs, static_cast<const uint16_t *>(x), T,
-                            c->ws_addend, c->ws_shared, s);
-    // The join is issued even if the shared launch failed, so the side
-    // stream never outlives the step.
-    if (c->d.overlap) {
+    if (shared) e = shared_sequence(shared, c->d.hidden, Fs, xb, T, c->ws_addend, c->ws_shared, s);
+    Items it{};
+    it.mode = ITEM_ROUTE;
+    it.K = K;
+    it.n = R;
+    it.idx = ids;
+    it.route_plan = c->ws_route_plan;
+    if (split && e == hipSuccess) {
+        it.want_fresh = 0;
+        e = launch_up(pv, it, R, xb, h, nullptr, nullptr, s);
+        if (e == hipSuccess) e = launch_down_to_d(pv, it, R, h, dr, nullptr, s);
+    }
+    // The join is issued even if a launch above failed, so the side stream
+    // never outlives the step.
+    if (two_streams) {
         hipError_t je = hipStreamWaitEvent(s, c->done, 0);
         if (e == hipSuccess) e = je;
     }
-    if (e != hipSuccess) return hip_fail(e, "shared expert / join");
+    if (e != hipSuccess) return hip_fail(e, "shared expert / resident routes / join");
 
     if (timing) HIP_TRY(record_timing(tev[4], s), "timing");
-    const PoolView pv = slot_pool_view(c);
-    HIP_TRY(routed_sequence(pv, static_cast<const uint16_t *>(x), ids, w, T, K,
-                            shared ? c->ws_addend : nullptr, static_cast<uint16_t *>(out),
-                            c->ws_routed, s),
-            "routed launch");
+    const float *add = shared ? c->ws_addend : nullptr;
+    if (split) {
+        it.want_fresh = 1;
+        HIP_TRY(launch_up(pv, it, R, xb, h, nullptr, nullptr, s), "routed launch");
+        HIP_TRY(launch_down_fused(pv, ids, w, T, K, h, add, dr, c->ws_route_plan,
+                                  static_cast<uint16_t *>(out), s),
+                "routed launch");
+    } else {
+        HIP_TRY(routed_sequence(pv, xb, ids, w, T, K, add, static_cast<uint16_t *>(out),
+                                c->ws_routed, s),
+                "routed launch");
+    }
     if (timing) {
         HIP_TRY(record_timing(tev[5], s), "timing");
         c->trecorded[layer] = 1;
@@ -738,7 +842,12 @@ moe_status_t moe_cache_read_state(moe_cache_t *c, int32_t *res, int32_t *own, ui
     if (clock) HIP_TRY(hipMemcpy(clock, c->clock, 4, hipMemcpyDeviceToHost), "copy clock");
     if (stats) HIP_TRY(hipMemcpy(stats, c->stats, L * MOE_NUM_STATS * 8, hipMemcpyDeviceToHost), "copy stats");
     if (freq) HIP_TRY(hipMemcpy(freq, c->freq, L * E * 8, hipMemcpyDeviceToHost), "copy freq");
-    if (order) HIP_TRY(hipMemcpy(order, c->order, S * 4, hipMemcpyDeviceToHost), "copy order");
+    if (order) {
+        std::vector<int32_t> img(admit_order_pairs((int)S) ? 2 * S : S);
+        HIP_TRY(hipMemcpy(img.data(), c->order, img.size() * 4, hipMemcpyDeviceToHost), "copy order");
+        const size_t stride = img.size() / S;
+        for (size_t i = 0; i < S; ++i) order[i] = img[i * stride];
+    }
     return MOE_OK;
 }
 
@@ -755,15 +864,13 @@ moe_status_t moe_cache_write_state(moe_cache_t *c, const int32_t *res, const int
         if (res[i] < -1 || res[i] >= (int32_t)S) return fail(MOE_INVALID_ARG, "res[%zu] out of range", i);
         if (res[i] >= 0 && own[res[i]] != (int32_t)i) return fail(MOE_INVALID_ARG, "res/own disagree at %zu", i);
     }
-    std::vector<int32_t> order(S);
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return stamp[a] < stamp[b]; });
+    const std::vector<int32_t> order = order_image((int)S, stamp, own);
     HIP_TRY(hipDeviceSynchronize(), "sync");
     HIP_TRY(hipMemcpy(c->res, res, L * E * 4, hipMemcpyHostToDevice), "write res");
     HIP_TRY(hipMemcpy(c->own, own, S * 4, hipMemcpyHostToDevice), "write own");
     HIP_TRY(hipMemcpy(c->stamp, stamp, S * 4, hipMemcpyHostToDevice), "write stamp");
     HIP_TRY(hipMemcpy(c->clock, &clock, 4, hipMemcpyHostToDevice), "write clock");
-    HIP_TRY(hipMemcpy(c->order, order.data(), S * 4, hipMemcpyHostToDevice), "write order");
+    HIP_TRY(hipMemcpy(c->order, order.data(), order.size() * 4, hipMemcpyHostToDevice), "write order");
     return MOE_OK;
 }
 

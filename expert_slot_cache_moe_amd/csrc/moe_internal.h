@@ -63,6 +63,57 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// ------------------------------------------------------------------ DPP lane operations
+
+// DPP (data-parallel primitives) moves: a lane reads another lane's VGPR
+// inside one VALU instruction.  Lanes whose source is out of range, or
+// whose row is masked off, read 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sum of x over the 64 lanes of a wave: shifts by 1, 2,
+// 4, 8 within each 16-lane row, then the row totals carried forward with
+// the two row broadcasts.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    uint32_t v = (uint32_t)x;
+    v += dpp_or_zero<kDppRowShr1>(v);
+    v += dpp_or_zero<kDppRowShr2>(v);
+    v += dpp_or_zero<kDppRowShr4>(v);
+    v += dpp_or_zero<kDppRowShr8>(v);
+    v += dpp_or_zero<kDppRowBcast15, 0xa>(v);
+    v += dpp_or_zero<kDppRowBcast31, 0xc>(v);
+    return (int)v;
+}
+
+// Maximum of a 64-bit value over the wave, returned to every lane: the same
+// shift/broadcast pattern as a max-scan (lane 63 ends with the maximum),
+// then read back from lane 63.  Values must be >= 0 (0 fills the gaps).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+#define MOE_MAX_STEP(CTRL, RM)                                   \
+    {                                                            \
+        const uint32_t l2 = dpp_or_zero<CTRL, RM>(lo);           \
+        const uint32_t h2 = dpp_or_zero<CTRL, RM>(hi);           \
+        const bool gt = h2 > hi || (h2 == hi && l2 > lo);        \
+        lo = gt ? l2 : lo;                                       \
+        hi = gt ? h2 : hi;                                       \
+    }
+    MOE_MAX_STEP(kDppRowShr1, 0xf)
+    MOE_MAX_STEP(kDppRowShr2, 0xf)
+    MOE_MAX_STEP(kDppRowShr4, 0xf)
+    MOE_MAX_STEP(kDppRowShr8, 0xf)
+    MOE_MAX_STEP(kDppRowBcast15, 0xa)
+    MOE_MAX_STEP(kDppRowBcast31, 0xc)
+#undef MOE_MAX_STEP
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+    hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // ------------------------------------------------------------------ kernel parameters
 
 struct AdmitParams {
@@ -75,13 +126,22 @@ struct AdmitParams {
     int32_t *res;          // [L*E]
     int32_t *own;          // [S]
     uint32_t *stamp;       // [S]
-    int32_t *order;        // [S] slots, least recently used first
+    int32_t *order;        // LRU order, least recently used first: [S] slots, or, when
+                           // admit_order_pairs(S), [S] (slot, owner) pairs
     uint32_t *clock;       // [1]
     int64_t *stats;        // [L*5]
     int64_t *freq;         // [L*E]
     int32_t *plan_slot;    // [min(max_routes, E)]
     int32_t *plan_expert;
     int32_t *n_miss;       // [1]
+    int32_t *route_plan;   // [R] or NULL: the plan entry filling the route's slot in this
+                           // step, or -1 (the route's expert was already resident)
+    // Optional fused top-k: with logits set, the step's expert ids are the
+    // top-K of each of T rows of logits [T][E] (R = T*K), the weights go to
+    // w_out [T][K], and ids is output only.
+    const float *logits;
+    int32_t T, K;
+    float *w_out;
 };
 
 struct GatherParams {
@@ -105,6 +165,8 @@ enum ItemMode : int32_t {
 
 struct Items {
     int32_t mode;
+    const int32_t *route_plan;  // ITEM_ROUTE filter: NULL = every route, else routes whose
+    int32_t want_fresh;         //   (route_plan[r] >= 0) == want_fresh
     int32_t K;                  // routes per token (ITEM_ROUTE)
     int32_t n;                  // routes (ITEM_ROUTE / ITEM_ALL)
     const int32_t *idx;         // [routes] pool rows (ITEM_ROUTE)
@@ -126,9 +188,14 @@ struct PoolView {
 
 hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
                        hipStream_t s);
+// Admission.  admit_lds_bytes sizes the launch for the largest step;
+// admit_prepare raises the kernels' LDS limit once; launch_admit picks the
+// register-resident kernel when the slot count allows it.
 hipError_t launch_admit(const AdmitParams &p, size_t lds_bytes, hipStream_t s);
 size_t admit_lds_bytes(int E, int S, int max_routes);
 hipError_t admit_prepare(size_t lds_bytes);
+bool admit_fused_topk_supported(int E, int S, int K);
+bool admit_order_pairs(int S);
 hipError_t launch_gather(const GatherParams &p, int workgroups, hipStream_t s);
 int gather_unit_bytes();
 
@@ -142,11 +209,23 @@ hipError_t launch_up(const PoolView &pool, const Items &items, int max_items, co
                      uint16_t *h, const uint16_t *gate_vec, float *gamma, hipStream_t s);
 hipError_t launch_down_to_d(const PoolView &pool, const Items &items, int max_items,
                             const uint16_t *h, float *d, const float *gamma, hipStream_t s);
+// d/route_plan optional (both or neither): routes with route_plan < 0 read
+// their down projection from d instead of computing it.
 hipError_t launch_down_fused(const PoolView &pool, const int32_t *idx, const float *w, int T,
-                             int K, const uint16_t *h, const float *addend, uint16_t *out,
-                             hipStream_t s);
+                             int K, const uint16_t *h, const float *addend, const float *d,
+                             const int32_t *route_plan, uint16_t *out, hipStream_t s);
 hipError_t launch_combine(const int32_t *idx, const float *w, int T, int K, int H, int num_rows,
                           const float *d, const float *addend, uint16_t *out, hipStream_t s);
+
+// The single-token layer step in two launches (bf16): stage 1 = miss gather
+// (+ the fetched experts' gate/up dots into gu [plan][2F]) | shared gate/up
+// | resident routes' gate/up; stage 2 = all down projections + combine.
+bool stage_supported(int fmt, int H, int F);
+hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, const PoolView &slots,
+                         const int32_t *idx, const float *w, const int32_t *route_plan, int K,
+                         const uint16_t *x, uint16_t *h, const PoolView *shared, uint16_t *hs,
+                         const uint16_t *gate_vec, float *gamma, uint16_t *out, int which,
+                         hipStream_t s);   // which: 1 stage 1, 2 stage 2, 3 both
 
 // Shape support of the expert kernels for one matrix width.
 bool expert_shape_supported(int fmt, int H, int F);

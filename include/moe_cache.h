@@ -98,10 +98,18 @@ typedef struct {
     int32_t max_routes;       /* upper bound on routes per admission step       */
     int32_t max_tokens;       /* upper bound on T for moe_layer_decode (0: no layer calls) */
     int32_t max_top_k;        /* upper bound on K for moe_layer_decode          */
-    int32_t overlap;          /* 1: gather on the library's side stream, forked
-                                 and joined by events around the shared expert;
-                                 0: everything serial on the compute stream.
-                                 Other values are an error. [P2] */
+    int32_t overlap;          /* schedule of moe_layer_decode:
+                                 0: serial on the compute stream [P2];
+                                 1: gather on the library's side stream, forked
+                                    and joined by events around the shared
+                                    expert and the resident routes [P2];
+                                 2: one stream, two launches: the gather, the
+                                    shared expert and the resident routes run
+                                    as disjoint workgroups of one kernel, the
+                                    down projections and combine in a second
+                                    (single-token bf16 steps; other steps run
+                                    as 0).  Results are bit-identical in all
+                                    three.  Other values are an error. */
     int32_t num_banks;        /* 0 (admission only: no gather, no experts) or
                                  the format's bank count (2 or 6)                */
     int32_t gather_workgroups;/* workgroups of the gather kernel; 0 = default   */
@@ -243,11 +251,15 @@ moe_status_t moe_shared_expert(const moe_shared_t *shared, int32_t hidden, const
 
 /* The whole layer step, (1)-(5), ordered as on [P2 "What we changed"]:
  * compute stream: top-k -> admission -> record(ready) -> shared expert
- * and gate -> wait(done) -> routed experts -> routed + shared; side
- * stream (overlap = 1): wait(ready) -> gather -> record(done).  With
- * overlap = 0 the gather runs on the compute stream right after the
- * admission.  The node set does not depend on the hit pattern, so the
- * call captures into one hipGraph and replays with device-side counts.
+ * and gate (+ routed experts already resident, single token) -> wait(done)
+ * -> routed experts -> routed + shared; side stream (overlap = 1):
+ * wait(ready) -> gather -> record(done).  overlap = 0 runs the gather on
+ * the compute stream right after the admission; overlap = 2 runs the
+ * gather, the shared expert and the resident routes inside one launch
+ * after the admission, then the down projections and the combine.  With
+ * a few token rows the top-k runs inside the admission kernel.  The node
+ * set does not depend on the hit pattern, so the call captures into one
+ * hipGraph and replays with device-side counts.
  * x_dev: bf16 [T][H]; logits_dev: fp32 [T][E]; shared: NULL for a layer
  * without a shared expert; out_dev: bf16 [T][H]; ids_out_dev: int32
  * [T][K] slot ids (or NULL); w_out_dev: fp32 [T][K] (or NULL).

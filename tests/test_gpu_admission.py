@@ -153,3 +153,12 @@ def test_bad_arguments_launch_nothing():
         assert m.moe_cache_read_state(gc)["clock"] == 0
     finally:
         m.moe_cache_destroy(gc)
+
+
+def test_large_cache_uses_the_general_kernel():
+    """More than 16384 slots: the global-memory admission kernel."""
+    g = np.random.default_rng(13)
+    L, E, S = 40, 640, 20000
+    steps = [(int(g.integers(0, L)), g.integers(-1, E, int(g.integers(1, 700))), int(g.choice([-1, 5])))
+             for _ in range(60)]
+    _run(L, E, S, steps, check_every=10)

@@ -174,7 +174,7 @@ def _oracle_layer(oc, host, sh, layer, x, lg, K, fmt, H, F, max_fetch=-1):
     return ref, slots, w
 
 
-@pytest.mark.parametrize("overlap", [0, 1])
+@pytest.mark.parametrize("overlap", [0, 1, 2])
 @pytest.mark.parametrize("shared", [False, True])
 def test_tiny_layer_decode_32_steps(overlap, shared):
     lay, host, sh = _tiny_layers(overlap, shared)
@@ -254,11 +254,12 @@ def test_wide_step_cached_equals_streamed_bit_for_bit(fmt, H, F, E, S, T, K, one
         lay.close()
 
 
-def test_graph_replay_matches_eager_over_changing_routes():
+@pytest.mark.parametrize("overlap", [1, 2])
+def test_graph_replay_matches_eager_over_changing_routes(overlap):
     """A whole token (3 layers) captured as one graph and replayed over 40
     steps with changing routes equals the same steps run eagerly."""
     L, E, S, H, F, K = 3, 16, 10, 64, 128, 2
-    mk = lambda: _tiny_layers(1, True, seed=3, L=L, E=E, S=S)[0]
+    mk = lambda: _tiny_layers(overlap, True, seed=3, L=L, E=E, S=S)[0]
     graph_l, eager_l = mk(), mk()
     g = W.rng(3, "graph")
     steps = 40
@@ -322,5 +323,89 @@ def test_kernel_timing_events_eager_and_captured():
             ms = m.moe_cache_timing(lay.cache)
             assert (ms >= 0).all() and (ms < 1000).all()
         m.moe_cache_set_timing(lay.cache, False)
+    finally:
+        lay.close()
+
+
+def test_all_schedules_are_bit_identical():
+    """Serial, two-stream and single-stream staged steps give the same bytes
+    at every step (the staged one rebuilds fetched experts' gate/up dots
+    inside the gather with the same reduction trees)."""
+    L, E, S, H = 2, 32, 12, 64
+    lays = [_tiny_layers(ov, True, seed=9, L=L, E=E, S=S)[0] for ov in (0, 1, 2)]
+    g = W.rng(9, "serial")
+    outs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in lays]
+    try:
+        for t in range(30):
+            for l in range(L):
+                x = _dev_u16(W.normal_bf16(g, (1, H)))
+                lg = torch.from_numpy(W.zipf_logits(g, 1, E, 0.5)).cuda()
+                for lay, o in zip(lays, outs):
+                    lay.decode(l, x, lg, 2, o)
+                torch.cuda.synchronize()
+                assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]), (t, l)
+        assert m.moe_cache_stats(lays[0].cache)[2] > 20      # the trace does miss
+    finally:
+        for lay in lays:
+            lay.close()
+
+
+def test_shared_expert_decode_shape_staged():
+    """H 2048, F 512, top-8 of 256 + gated shared expert, 2 layers over a
+    small cache (many misses): the staged schedule equals the serial one bit
+    for bit and the oracle within tolerance."""
+    L, E, S, H, F, K = 2, 256, 24, 2048, 512, 8
+    g = W.rng(15, "c3-shape")
+    host = [_replicated_rows(0, g, E, H, F, 8) for _ in range(L)]
+    sh = [(W.normal_bf16(g, 2 * F * H, 0.02), W.normal_bf16(g, H * F, 0.02), W.normal_bf16(g, H, 0.02))
+          for _ in range(L)]
+    lays = [SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, host_rows=host, shared=sh,
+                            max_tokens=1, max_top_k=K, overlap=ov) for ov in (2, 0)]
+    oc = oracle.OracleCache(L, E, S)
+    tr = W.DecodeTrace(15, L, E, K, stay=0.5)
+    outs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in lays]
+    try:
+        for t in range(10):
+            sets = tr.step_sets()
+            lgs = tr.logits(sets)
+            for l in range(L):
+                x = W.normal_bf16(g, (1, H))
+                for lay, o in zip(lays, outs):
+                    lay.decode(l, _dev_u16(x), torch.from_numpy(lgs[l:l + 1]).cuda(), K, o)
+                torch.cuda.synchronize()
+                assert torch.equal(outs[0], outs[1]), (t, l)
+                ref, _, _ = _oracle_layer(oc, host, sh, l, x, lgs[l:l + 1], K, 0, H, F)
+                _close(_bf16_to_f64(outs[0]), ref, f"token {t} layer {l}")
+        assert m.moe_cache_stats(lays[0].cache)[2] > 40
+    finally:
+        for lay in lays:
+            lay.close()
+
+
+def test_fused_topk_in_the_layer_step_handles_ties_and_nan():
+    """Few rows: the layer step's top-k runs inside the admission kernel;
+    equal logits take the lower expert, NaN counts as -infinity."""
+    E, S, H, K, T = 64, 40, 64, 4, 5
+    g = W.rng(14, "fused-topk")
+    host = [W.bf16_expert_rows(g, E, H, 128)]
+    lay = SlotCacheLayers(layers=1, experts=E, slots=S, hidden=H, ffn=128, host_rows=host,
+                          max_tokens=T, max_top_k=K)
+    oc = oracle.OracleCache(1, E, S)
+    try:
+        for step in range(6):
+            lg = np.round(g.standard_normal((T, E)), 1).astype(np.float32)   # many ties
+            lg[0, 3] = np.nan
+            lg[1, :] = 0.0
+            lg[2, 5] = -0.0
+            x = W.normal_bf16(g, (T, H))
+            out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+            ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+            w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+            lay.decode(0, _dev_u16(x), torch.from_numpy(lg).cuda(), K, out, ids_out=ids, w_out=w)
+            torch.cuda.synchronize()
+            ref, slots, ow = _oracle_layer(oc, host, None, 0, x, lg, K, 0, H, 128)
+            np.testing.assert_array_equal(ids.cpu().numpy(), slots)
+            np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=1e-5)
+            _close(_bf16_to_f64(out), ref, f"step {step}")
     finally:
         lay.close()
