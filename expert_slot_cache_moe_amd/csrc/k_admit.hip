@@ -292,11 +292,16 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 __device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int K,
                                           int32_t *ids_lds, float *w_out) {
     const int lane = threadIdx.x & (kWave - 1);
+    // All of the row's loads in flight together (clamped in-range indices),
+    // then the keys.
+    float lv[kTopkMaxPerLane];
+#pragma unroll
+    for (int c = 0; c < kTopkMaxPerLane; ++c) lv[c] = row[min(lane + kWave * c, E - 1)];
     uint64_t keys[kTopkMaxPerLane];
 #pragma unroll
     for (int c = 0; c < kTopkMaxPerLane; ++c) {
         const int e = lane + kWave * c;
-        keys[c] = e < E ? ((uint64_t)logit_key(row[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)
+        keys[c] = e < E ? ((uint64_t)logit_key(lv[c]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)
                         : 0ull;
     }
     uint64_t prev = ~0ull, mine = 0ull;
@@ -310,12 +315,10 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, 
         prev = best;
     }
     const float v = key_logit((uint32_t)(mine >> 32));
-    const float m = __shfl(v, 0, kWave);
+    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
     float ex = 0.f;
     if (lane < K) ex = (m == -INFINITY) ? 1.f : __expf(v - m);
-    float z = ex;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
+    const float z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_total<kWave>(ex)), kWave - 1));
     if (lane < K) {
         ids_lds[lane] = (int32_t)(0xffffffffu - (uint32_t)mine);
         w_out[lane] = ex / z;
@@ -348,20 +351,46 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     const int wave = tid / kWave;
     const int64_t lbase = (int64_t)p.layer * E;
 
-    // This thread's run of the LRU order: (slot, owner) pairs.
+    // This thread's run of the LRU order: (slot, owner) pairs.  The order
+    // buffer holds kThreads * P pairs (admit_order_bytes), so the loads are
+    // unconditional 16-byte ones, all in flight together; positions past S
+    // are masked afterwards.
     int ord[P], owner[P];
-    const int2 *pairs = reinterpret_cast<const int2 *>(p.order);
+    if constexpr (P == 1) {
+        const int2 v = reinterpret_cast<const int2 *>(p.order)[tid];
+        ord[0] = v.x;
+        owner[0] = v.y;
+    } else {
+        const int4 *q4 = reinterpret_cast<const int4 *>(p.order) + tid * (P / 2);
+        int4 v[P / 2];
 #pragma unroll
-    for (int q = 0; q < P; ++q) {
-        const int pos = tid * P + q;
-        const int2 v = pos < S ? pairs[pos] : make_int2(-1, -1);
-        ord[q] = v.x;
-        owner[q] = v.y;
+        for (int q = 0; q < P / 2; ++q) v[q] = q4[q];
+#pragma unroll
+        for (int q = 0; q < P / 2; ++q) {
+            ord[2 * q] = v[q].x;
+            owner[2 * q] = v[q].y;
+            ord[2 * q + 1] = v[q].z;
+            owner[2 * q + 1] = v[q].w;
+        }
     }
-    for (int e = tid; e < E; e += kThreads) {
-        resl[e] = p.res[lbase + e];
-        cnt[e] = 0;
-        filled[e] = 0;
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+        if (tid * P + q >= S) ord[q] = owner[q] = -1;
+    // The layer's slot map row into LDS: loads of a batch issued together
+    // (clamped in-range indices), stores after.
+    for (int e0 = 0; e0 < E; e0 += 4 * kThreads) {
+        int32_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = p.res[lbase + min(e0 + tid + j * kThreads, E - 1)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + tid + j * kThreads;
+            if (e < E) {
+                resl[e] = v[j];
+                cnt[e] = 0;
+                filled[e] = 0;
+            }
+        }
     }
     for (int i = tid; i < S; i += kThreads) touched[i] = 0;
     if (tid < 16) misc[tid] = 0;
@@ -561,6 +590,10 @@ int fast_p(int S) {
 }  // namespace
 
 bool admit_order_pairs(int S) { return fast_p(S) <= kFastMaxP; }
+
+size_t admit_order_bytes(int S) {
+    return admit_order_pairs(S) ? (size_t)kThreads * fast_p(S) * 8 : (size_t)S * 4;
+}
 
 bool admit_fused_topk_supported(int E, int S, int K) {
     return E <= kWave * kTopkMaxPerLane && K <= kWave && fast_p(S) <= kFastMaxP;

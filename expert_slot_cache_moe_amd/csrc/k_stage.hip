@@ -77,9 +77,10 @@ __device__ __forceinline__ void up_rows(const PoolView &pool, int64_t prow, int 
     wu.load(pool, prow, 0, F + jj, li, LPR);
     XSeg<MOE_FMT_BF16, NCH> xs;
     xs.load(x, li, LPR);
-    const float g = group_sum<LPR>(seg_dot(wg, xs)) * wg.glob(pool, prow, 0);
-    const float u = group_sum<LPR>(seg_dot(wu, xs)) * wg.glob(pool, prow, 0);
-    if (jok && li == 0) h[j] = f32_to_bf16(silu_mul(g, u));
+    __builtin_amdgcn_sched_barrier(0);  // all of the row pair's loads issue before any math
+    const float g = group_total<LPR>(seg_dot(wg, xs)) * wg.glob(pool, prow, 0);
+    const float u = group_total<LPR>(seg_dot(wu, xs)) * wg.glob(pool, prow, 0);
+    if (jok && li == LPR - 1) h[j] = f32_to_bf16(silu_mul(g, u));
 }
 
 template <int LPRH, int NCHH>
@@ -135,15 +136,11 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
             const int sub = lane / LPRH, li = lane % LPRH;
             for (int r0 = 0; r0 < rows; r0 += kWavesPerBlock * RPW) {
                 const int r = r0 + wave * RPW + sub;
-                if (r < rows) {
-                    float q[NCHH];
+                float q[NCHH];
 #pragma unroll
-                    for (int i = 0; i < NCHH; ++i) q[i] = part[r * C + li + LPRH * i];
-                    const float s = group_sum<LPRH>(tree_sum<NCHH>(q));
-                    if (li == 0) p.gu[(int64_t)entry * 2 * F + row0 + r] = s;
-                } else {
-                    group_sum<LPRH>(0.f);
-                }
+                for (int i = 0; i < NCHH; ++i) q[i] = r < rows ? part[r * C + li + LPRH * i] : 0.f;
+                const float s = group_total<LPRH>(tree_sum<NCHH>(q));
+                if (r < rows && li == LPRH - 1) p.gu[(int64_t)entry * 2 * F + row0 + r] = s;
             }
             __syncthreads();
         }
@@ -162,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
                 const u32x4 gv = *reinterpret_cast<const u32x4 *>(p.gate_vec + 8 * c);
                 z = dot8_bf16(gv, a, z);
             }
-            z = group_sum<kWave>(z);
-            if (lane == 0) p.gamma[0] = 1.f / (1.f + __expf(-z));
+            z = group_total<kWave>(z);
+            if (lane == kWave - 1) p.gamma[0] = 1.f / (1.f + __expf(-z));
         }
         return;
     }
@@ -171,7 +168,8 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
     const int k = b / p.a_tiles;
     const int tile = b - k * p.a_tiles;
     const int s = p.idx[k];
-    if (s < 0 || s >= p.slots.num_rows || p.route_plan[k] >= 0) return;
+    const int plan = p.route_plan[k];
+    if ((s < 0) | (s >= p.slots.num_rows) | (plan >= 0)) return;
     up_rows<LPRH, NCHH>(p.slots, s, tile * JT + wave * (kWave / LPRH) + sub, li, p.x,
                         p.h + (int64_t)k * F);
 }
@@ -183,73 +181,97 @@ __device__ __forceinline__ void h_from_gu(const float *gu, int F, int li, int lp
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int j0 = (li + c * lpr) * 8;
+        const u32x4 *g4 = reinterpret_cast<const u32x4 *>(gu + j0);
+        const u32x4 *u4 = reinterpret_cast<const u32x4 *>(gu + F + j0);
+        const u32x4 ga = g4[0], gb = g4[1], ua = u4[0], ub = u4[1];
+        float gv[8], uv[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            gv[q] = __uint_as_float(ga[q]);
+            gv[4 + q] = __uint_as_float(gb[q]);
+            uv[q] = __uint_as_float(ua[q]);
+            uv[4 + q] = __uint_as_float(ub[q]);
+        }
         u32x4 v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = f32_to_bf16(silu_mul(gu[j0 + 2 * q], gu[F + j0 + 2 * q]));
-            const uint32_t hi = f32_to_bf16(silu_mul(gu[j0 + 2 * q + 1], gu[F + j0 + 2 * q + 1]));
+            const uint32_t lo = f32_to_bf16(silu_mul(gv[2 * q], uv[2 * q]));
+            const uint32_t hi = f32_to_bf16(silu_mul(gv[2 * q + 1], uv[2 * q + 1]));
             v[q] = lo | (hi << 16);
         }
         hs.x[c][0] = v;
     }
 }
 
+// One batch of up to kDownBatch routes of stage 2, loads first, math after:
+// the routes' slot ids and plan entries (scalar loads, issued together),
+// then every W2 row and activation chunk, and with the first batch the
+// shared expert's.  Routes that contribute nothing read row 0 and route 0
+// as in-range stand-ins, and without a shared expert the shared view points
+// at valid memory too (set by the launcher), so every load is
+// unconditional and none waits for another.
+template <int LPRF, int NCHF, bool FIRST>
+__device__ __forceinline__ void stage2_batch(const Stage2Params &p, int k0, int ii, int li,
+                                             float &acc, float &vs) {
+    const int F = p.slots.F;
+    int sl[kDownBatch], pe[kDownBatch];
+#pragma unroll
+    for (int q = 0; q < kDownBatch; ++q) {
+        const int kk = min(k0 + q, p.K - 1);
+        sl[q] = p.idx[kk];
+        pe[q] = p.route_plan[kk];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    WSeg<MOE_FMT_BF16, NCHF> w2[kDownBatch];
+    XSeg<MOE_FMT_BF16, NCHF> hs[kDownBatch];
+    int rows[kDownBatch];
+#pragma unroll
+    for (int q = 0; q < kDownBatch; ++q) {
+        const int k = k0 + q;
+        const bool ok = k < p.K && sl[q] >= 0 && sl[q] < p.slots.num_rows;
+        rows[q] = ok ? sl[q] : -1;
+        w2[q].load(p.slots, ok ? sl[q] : 0, 1, ii, li, LPRF);
+        hs[q].load(p.h + (int64_t)min(k, p.K - 1) * F, li, LPRF);
+    }
+    WSeg<MOE_FMT_BF16, NCHF> w2s;
+    XSeg<MOE_FMT_BF16, NCHF> hss;
+    if constexpr (FIRST) {
+        w2s.load(p.shared, 0, 1, ii, li, LPRF);
+        hss.load(p.hs, li, LPRF);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < kDownBatch; ++q) {
+        if (rows[q] < 0) continue;
+        if (pe[q] >= 0) h_from_gu<NCHF>(p.gu + (int64_t)pe[q] * 2 * F, F, li, LPRF, hs[q]);
+        const float v = group_total<LPRF>(seg_dot(w2[q], hs[q])) * w2[q].glob(p.slots, rows[q], 1);
+        acc = fmaf(p.w[k0 + q], v, acc);
+    }
+    if constexpr (FIRST) vs = group_total<LPRF>(seg_dot(w2s, hss)) * w2s.glob(p.shared, 0, 1);
+}
+
 template <int LPRF, int NCHF>
 __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
     constexpr int RPW = kWave / LPRF;
     constexpr int IT = kWavesPerBlock * RPW;
-    const int H = p.slots.H, F = p.slots.F;
+    const int H = p.slots.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int sub = lane / LPRF, li = lane % LPRF;
     const int i = blockIdx.x * IT + wave * RPW + sub;
     const bool iok = i < H;
     const int ii = iok ? i : H - 1;
 
-    // Every load of the step is issued before any reduction: the W2 rows of
-    // the routes and of the shared expert, and the activations (for a
-    // fetched route its h chunks come from its gate/up dots).
-    WSeg<MOE_FMT_BF16, NCHF> w2s;
-    XSeg<MOE_FMT_BF16, NCHF> hss;
-    if (p.has_shared) {
-        w2s.load(p.shared, 0, 1, ii, li, LPRF);
-        hss.load(p.hs, li, LPRF);
-    }
-    float acc = 0.f;
-    for (int k0 = 0; k0 < p.K; k0 += kDownBatch) {
-        WSeg<MOE_FMT_BF16, NCHF> w2[kDownBatch];
-        XSeg<MOE_FMT_BF16, NCHF> hs[kDownBatch];
-        int rows[kDownBatch];
-#pragma unroll
-        for (int q = 0; q < kDownBatch; ++q) {
-            const int k = k0 + q;
-            rows[q] = -1;
-            if (k < p.K) {
-                const int s = p.idx[k];
-                if (s >= 0 && s < p.slots.num_rows) {
-                    rows[q] = s;
-                    w2[q].load(p.slots, s, 1, ii, li, LPRF);
-                    if (p.route_plan[k] < 0) hs[q].load(p.h + (int64_t)k * F, li, LPRF);
-                }
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < kDownBatch; ++q) {
-            if (rows[q] < 0) continue;
-            const int k = k0 + q;
-            const int pe = p.route_plan[k];
-            if (pe >= 0) h_from_gu<NCHF>(p.gu + (int64_t)pe * 2 * F, F, li, LPRF, hs[q]);
-            const float v = group_sum<LPRF>(seg_dot(w2[q], hs[q])) * w2[q].glob(p.slots, rows[q], 1);
-            acc = fmaf(p.w[k], v, acc);
-        }
-    }
+    float acc = 0.f, vs = 0.f;
+    stage2_batch<LPRF, NCHF, true>(p, 0, ii, li, acc, vs);
+    for (int k0 = kDownBatch; k0 < p.K; k0 += kDownBatch)
+        stage2_batch<LPRF, NCHF, false>(p, k0, ii, li, acc, vs);
     float res = acc;
     if (p.has_shared) {
-        const float v = group_sum<LPRF>(seg_dot(w2s, hss)) * w2s.glob(p.shared, 0, 1);
-        // gamma * v is rounded on its own (the library builds without fp
+        // gamma * vs is rounded on its own (the library builds without fp
         // contraction), as the serial path rounds it when storing it
-        res = acc + p.gamma[0] * v;
+        res = acc + p.gamma[0] * vs;
     }
-    if (iok && li == 0) p.out[i] = f32_to_bf16(res);
+    if (iok && li == LPRF - 1) p.out[i] = f32_to_bf16(res);
 }
 
 template <int LPRH, int NCHH, int LPRF, int NCHF>
@@ -332,6 +354,11 @@ hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, co
         b.has_shared = 1;
         b.hs = hs;
         b.gamma = gamma;
+    } else {
+        // stage 2 loads the shared view unconditionally: point it at row 0
+        // of the routed pool and at the routed activations (never used)
+        b.shared = slots;
+        b.hs = h;
     }
     b.out = out;
     const int ch = slots.H / 8, cf = slots.F / 8;

@@ -65,9 +65,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void topk_kernel(const float
     const float m = __shfl(mine, 0, kWave);
     float ex = 0.f;
     if (lane < K) ex = (m == -INFINITY) ? 1.f : __expf(mine - m);
-    float z = ex;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
+    // the same sum, in the same order, as the top-k fused into admission
+    const float z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(group_total<kWave>(ex)), kWave - 1));
     if (lane < K) {
         ids[(int64_t)row * K + lane] = mine_i;
         w[(int64_t)row * K + lane] = ex / z;

@@ -480,7 +480,7 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     const size_t o_res = off; off += align_up(L * E * 4);
     const size_t o_own = off; off += align_up(S * 4);
     const size_t o_stamp = off; off += align_up(S * 4);
-    const size_t o_order = off; off += align_up(S * 8);
+    const size_t o_order = off; off += align_up(admit_order_bytes((int)S));
     const size_t o_clock = off; off += align_up(4);
     const size_t o_stats = off; off += align_up(L * MOE_NUM_STATS * 8);
     const size_t o_freq = off; off += align_up(L * E * 8);

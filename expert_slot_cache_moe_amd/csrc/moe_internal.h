@@ -89,6 +89,26 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
     return (int)v;
 }
 
+// Sum of v over each aligned group of WIDTH lanes (a power of two, at most
+// the wave), valid in the group's last lane only.  The tree is pairwise,
+// lanes paired by their low index bits first: row shifts by 1, 2, 4, 8,
+// then the two row broadcasts.  The group's last lane reads only lanes of
+// its own group, so groups may sit in divergent branches.
+template <int WIDTH>
+__device__ __forceinline__ float group_total(float v) {
+    static_assert(WIDTH >= 1 && WIDTH <= kWave && (WIDTH & (WIDTH - 1)) == 0, "group width");
+    uint32_t u = __float_as_uint(v);
+#define MOE_ADD_STEP(CTRL, RM) u = __float_as_uint(__uint_as_float(u) + __uint_as_float(dpp_or_zero<CTRL, RM>(u)));
+    if constexpr (WIDTH >= 2) MOE_ADD_STEP(kDppRowShr1, 0xf)
+    if constexpr (WIDTH >= 4) MOE_ADD_STEP(kDppRowShr2, 0xf)
+    if constexpr (WIDTH >= 8) MOE_ADD_STEP(kDppRowShr4, 0xf)
+    if constexpr (WIDTH >= 16) MOE_ADD_STEP(kDppRowShr8, 0xf)
+    if constexpr (WIDTH >= 32) MOE_ADD_STEP(kDppRowBcast15, 0xa)
+    if constexpr (WIDTH >= 64) MOE_ADD_STEP(kDppRowBcast31, 0xc)
+#undef MOE_ADD_STEP
+    return __uint_as_float(u);
+}
+
 // Maximum of a 64-bit value over the wave, returned to every lane: the same
 // shift/broadcast pattern as a max-scan (lane 63 ends with the maximum),
 // then read back from lane 63.  Values must be >= 0 (0 fills the gaps).
@@ -195,6 +215,8 @@ hipError_t launch_admit(const AdmitParams &p, size_t lds_bytes, hipStream_t s);
 size_t admit_lds_bytes(int E, int S, int max_routes);
 hipError_t admit_prepare(size_t lds_bytes);
 bool admit_fused_topk_supported(int E, int S, int K);
+// Bytes of the LRU order buffer for S slots (padded for whole-vector loads).
+size_t admit_order_bytes(int S);
 bool admit_order_pairs(int S);
 hipError_t launch_gather(const GatherParams &p, int workgroups, hipStream_t s);
 int gather_unit_bytes();
