@@ -145,6 +145,8 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t *__r
     for (int g = tid; g < ng; g += kGroupThreads)
         grp_count[g] = (g + 1 < ng ? gstart[g + 1] : nvalid) - gstart[g];
     for (int i = tid; i < nvalid; i += kGroupThreads) grp_routes[i] = sroute[i];
+    // group slots past the last group read as "no row"
+    for (int g = ng + tid; g < min(n, num_rows); g += kGroupThreads) grp_row[g] = -1;
     if (tid == 0) *n_groups = ng;
 }
 

@@ -1,0 +1,471 @@
+// Wide steps: routes grouped by pool row, each group's expert applied to
+// all of its tokens with MFMA (gfx950 v_mfma_f32_16x16x32_bf16).
+//
+// What is computed is the routed expert of FreeToken issue #753 (section
+// "What we changed") over pool rows, as in the single-token kernels:
+//   g = W1[r] x, u = W3[r] x (fp32 accumulation), h = bf16(silu(g) * u),
+//   d = W2[r] h (fp32), combined later as sum_k w[t][k] d[t][k].
+// A group is the set of routes of one step that share a pool row (one
+// expert), so its weights stream from HBM once per step and meet every
+// token of the group in the matrix cores: weights are the MFMA A operand
+// (16 rows x 32 contraction elements), tokens the B operand (16 columns).
+//
+// Tiling on CDNA4: a wave owns 16 output rows and sweeps the contraction
+// dimension in slabs of 128 elements.  Lane l = 16 q + c loads 32
+// consecutive elements [k0 + 32 q, k0 + 32 q + 32) of weight row c (64
+// bytes of bf16, or 16 bytes of 4-bit codes and two scales) and the same
+// element range of token column c, and feeds them to four MFMAs: the
+// contraction index is permuted identically on both operands, which leaves
+// the sum unchanged and makes every load a full 16-byte vector.
+//
+// 4-bit weights (OCP E2M1 with one E4M3 scale per 16 elements, FreeToken
+// PR #491 section 5) are expanded to bf16 in registers: the product of an
+// E2M1 value and an E4M3 scale has at most six significant bits, so it is
+// exact in bf16, and the MFMA sees exactly the dequantized weights.
+#include "k_expert.inc"
+
+namespace moe {
+namespace mfma_detail {
+
+using namespace expert_detail;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTile = 16;                       // rows and tokens of one MFMA tile
+constexpr int kSlab = 128;                      // contraction elements per sweep step
+constexpr int kMWaves = 4;
+constexpr int kMThreads = kMWaves * kWave;
+constexpr int kTT = 2;                          // token tiles per pass over the weights
+constexpr int kRowsPerBlock = kMWaves * kTile;  // output rows of one workgroup
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One lane's 32 weights of one row for one slab, as four MFMA operands.
+template <int FMT> struct ASlab;
+
+template <> struct ASlab<MOE_FMT_BF16> {
+    u32x4 v[4];
+    // m: 0 = gate/up matrix, 1 = down matrix; row r of pool row prow.
+    __device__ __forceinline__ void load(const PoolView &p, int64_t prow, int m, int r, int e0) {
+        const int ncols = m == 0 ? p.H : p.F;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(p.bank[m] + prow * p.rb[m] +
+                                                           ((int64_t)r * ncols + e0) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = src[i];
+    }
+    __device__ __forceinline__ void expand(u32x4 (&a)[4]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = v[i];
+    }
+};
+
+template <> struct ASlab<MOE_FMT_E2M1> {
+    u32x4 codes;   // 32 nibbles, element 2b in the low nibble of byte b
+    uint32_t sc;   // two E4M3 scales (elements 0-15, 16-31)
+    __device__ __forceinline__ void load(const PoolView &p, int64_t prow, int m, int r, int e0) {
+        const int ncols = m == 0 ? p.H : p.F;
+        const int b = 3 * m;
+        codes = *reinterpret_cast<const u32x4 *>(p.bank[b] + prow * p.rb[b] +
+                                                 (int64_t)r * (ncols / 2) + e0 / 2);
+        sc = *reinterpret_cast<const uint16_t *>(p.bank[b + 1] + prow * p.rb[b + 1] +
+                                                 (int64_t)r * (ncols / 16) + e0 / 16);
+    }
+    // codes * scale as bf16 pairs (exact): the hardware converts two codes
+    // to fp32, the scale multiplies in fp32, and the upper halves are kept.
+    __device__ __forceinline__ void expand(u32x4 (&a)[4]) const {
+        const float s0 = e4m3_f(sc & 0xffu), s1 = e4m3_f(sc >> 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t word = codes[i];
+            const float s = i < 2 ? s0 : s1;
+            u32x4 o;
+#define MOE_EXPAND_BYTE(B)                                                                \
+    {                                                                                     \
+        const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, B);          \
+        o[B] = __builtin_amdgcn_perm(__float_as_uint(f.y * s), __float_as_uint(f.x * s),  \
+                                     0x07060302u);                                        \
+    }
+            MOE_EXPAND_BYTE(0)
+            MOE_EXPAND_BYTE(1)
+            MOE_EXPAND_BYTE(2)
+            MOE_EXPAND_BYTE(3)
+#undef MOE_EXPAND_BYTE
+            a[i] = o;
+        }
+    }
+};
+
+template <int FMT>
+__device__ __forceinline__ float matrix_glob(const PoolView &p, int64_t prow, int m) {
+    if constexpr (FMT == MOE_FMT_E2M1) {
+        const int b = 3 * m + 2;
+        return *reinterpret_cast<const float *>(p.bank[b] + prow * p.rb[b]);
+    } else {
+        return 1.f;
+    }
+}
+
+// Group g of the step: its pool row, route count and route list, read with
+// three independent loads (slots past the last group hold row -1).
+__device__ __forceinline__ bool group_of(const Items &items, int g, int num_rows, ItemRef &r) {
+    const int row = items.grp_row[g];
+    const int count = items.grp_count[g];
+    const int start = items.grp_start[g];
+    r.row = row;
+    r.count = count;
+    r.first = 0;
+    r.list = items.grp_routes + start;
+    r.K = items.K;
+    // one branch on all three values, so the three loads issue together
+    return !((row < 0) | (row >= num_rows) | (count <= 0) | (start < 0));
+}
+
+// 32 bf16 activations of one token row for one slab.
+__device__ __forceinline__ void load_b(const uint16_t *row, int e0, u32x4 (&b)[4]) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(row + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = src[i];
+}
+
+// Slabs whose loads are issued together before any of them is used: deep
+// enough that a wave keeps 8-16 KB in flight, shallow enough for the
+// register file (4-bit rows are a quarter of the bytes of bf16 rows).
+template <int FMT> struct Depth { static constexpr int v = FMT == MOE_FMT_BF16 ? 2 : 4; };
+
+// gate/up + SwiGLU for one group and 64 rows j per workgroup:
+// h[route][j] = bf16(silu(g) * u) for every route of the group.  The first
+// weights are requested as soon as the group's row is known, before the
+// route list and token rows (two more dependent loads) are read.
+template <int FMT>
+__global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, Items items,
+                                                               const uint16_t *__restrict__ x,
+                                                               uint16_t *__restrict__ h) {
+    constexpr int D = Depth<FMT>::v;
+    ItemRef it;
+    if (!group_of(items, blockIdx.y, pool.num_rows, it)) return;
+    const int H = pool.H, F = pool.F;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int c = lane & (kTile - 1), q = lane / kTile;
+    const int j0 = blockIdx.x * kRowsPerBlock + wave * kTile;
+    if (j0 >= F) return;
+
+    // the weights of D slabs at once (slabs past H repeat the last one, in range)
+    ASlab<FMT> wg[D], wu[D];
+    auto load_chunk = [&](int k0) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int e0 = min(k0 + d * kSlab, H - kSlab) + 32 * q;
+            wg[d].load(pool, it.row, 0, j0 + c, e0);
+            wu[d].load(pool, it.row, 0, F + j0 + c, e0);
+        }
+    };
+    load_chunk(0);
+    const float glob = matrix_glob<FMT>(pool, it.row, 0);
+
+    for (int base = 0; base < it.count; base += kTile * kTT) {
+        if (base > 0) load_chunk(0);
+        const int ntile = min(kTT, (it.count - base + kTile - 1) / kTile);
+        const uint16_t *xr[kTT];
+#pragma unroll
+        for (int t = 0; t < kTT; ++t) {
+            const int n = min(base + t * kTile + c, it.count - 1);
+            xr[t] = x + (int64_t)it.token(n) * H;
+        }
+        f32x4 ag[kTT], au[kTT];
+#pragma unroll
+        for (int t = 0; t < kTT; ++t) ag[t] = au[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < H; k0 += D * kSlab) {
+            if (k0 > 0) load_chunk(k0);
+            // the activations one slab ahead of their use
+            u32x4 xb[2][kTT][4];
+#pragma unroll
+            for (int t = 0; t < kTT; ++t)
+                if (t < ntile) load_b(xr[t], k0 + 32 * q, xb[0][t]);
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                if (k0 + d * kSlab >= H) break;
+                if (d + 1 < D && k0 + (d + 1) * kSlab < H) {
+#pragma unroll
+                    for (int t = 0; t < kTT; ++t)
+                        if (t < ntile) load_b(xr[t], k0 + (d + 1) * kSlab + 32 * q, xb[(d + 1) & 1][t]);
+                }
+                u32x4 ga[4], ua[4];
+                wg[d].expand(ga);
+                wu[d].expand(ua);
+#pragma unroll
+                for (int t = 0; t < kTT; ++t) {
+                    if (t < ntile) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            ag[t] = mfma(ga[i], xb[d & 1][t][i], ag[t]);
+                            au[t] = mfma(ua[i], xb[d & 1][t][i], au[t]);
+                        }
+                    }
+                }
+            }
+        }
+        // lane holds rows j0 + 4q + i (i < 4) of token column c
+#pragma unroll
+        for (int t = 0; t < kTT; ++t) {
+            const int n = base + t * kTile + c;
+            if (t < ntile && n < it.count) {
+                const int64_t r = it.route(n);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float g = ag[t][i] * glob, u = au[t][i] * glob;
+                    h[r * F + j0 + 4 * q + i] = f32_to_bf16(silu_mul(g, u));
+                }
+            }
+        }
+    }
+}
+
+// Row tiles per wave of the down projection: its contraction (F) is short,
+// so a wave takes several row tiles to keep enough bytes in flight; the
+// activation operand is shared by all of them.
+template <int FMT> struct DownTiles { static constexpr int v = FMT == MOE_FMT_BF16 ? 2 : 4; };
+
+template <int FMT>
+constexpr int down_rows_per_block() { return kMWaves * kTile * DownTiles<FMT>::v; }
+
+// down projection for one group and 16 * RT rows i per wave:
+// d[route][i] = (W2 h[route])_i, fp32.
+template <int FMT>
+__global__ __launch_bounds__(kMThreads, 2) void down_mfma_kernel(PoolView pool, Items items,
+                                                              const uint16_t *__restrict__ h,
+                                                              float *__restrict__ d) {
+    constexpr int D = 2;
+    constexpr int RT = DownTiles<FMT>::v;
+    ItemRef it;
+    if (!group_of(items, blockIdx.y, pool.num_rows, it)) return;
+    const int H = pool.H, F = pool.F;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int c = lane & (kTile - 1), q = lane / kTile;
+    const int i0 = (blockIdx.x * kMWaves + wave) * RT * kTile;
+    if (i0 >= H) return;
+    ASlab<FMT> w2[D][RT];
+    auto load_chunk = [&](int k0) {
+#pragma unroll
+        for (int dd = 0; dd < D; ++dd) {
+            const int e0 = min(k0 + dd * kSlab, F - kSlab) + 32 * q;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                w2[dd][rt].load(pool, it.row, 1, min(i0 + rt * kTile, H - kTile) + c, e0);
+        }
+    };
+    load_chunk(0);
+    const float glob = matrix_glob<FMT>(pool, it.row, 1);
+
+    for (int base = 0; base < it.count; base += kTile * kTT) {
+        if (base > 0) load_chunk(0);
+        const int ntile = min(kTT, (it.count - base + kTile - 1) / kTile);
+        const uint16_t *hr[kTT];
+#pragma unroll
+        for (int t = 0; t < kTT; ++t) {
+            const int n = min(base + t * kTile + c, it.count - 1);
+            hr[t] = h + (int64_t)it.route(n) * F;
+        }
+        f32x4 acc[RT][kTT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int t = 0; t < kTT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < F; k0 += D * kSlab) {
+            if (k0 > 0) load_chunk(k0);
+            u32x4 hb[D][kTT][4];
+#pragma unroll
+            for (int dd = 0; dd < D; ++dd) {
+                const int e0 = min(k0 + dd * kSlab, F - kSlab) + 32 * q;
+#pragma unroll
+                for (int t = 0; t < kTT; ++t)
+                    if (t < ntile) load_b(hr[t], e0, hb[dd][t]);
+            }
+#pragma unroll
+            for (int dd = 0; dd < D; ++dd) {
+                if (k0 + dd * kSlab >= F) break;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    u32x4 wa[4];
+                    w2[dd][rt].expand(wa);
+#pragma unroll
+                    for (int t = 0; t < kTT; ++t) {
+                        if (t < ntile) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[rt][t] = mfma(wa[i], hb[dd][t][i], acc[rt][t]);
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kTT; ++t) {
+            const int n = base + t * kTile + c;
+            if (t < ntile && n < it.count) {
+                const int64_t r = it.route(n);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const int ib = i0 + rt * kTile;
+                    if (ib < H) {
+                        float4 v;
+                        v.x = acc[rt][t][0] * glob;
+                        v.y = acc[rt][t][1] * glob;
+                        v.z = acc[rt][t][2] * glob;
+                        v.w = acc[rt][t][3] * glob;
+                        *reinterpret_cast<float4 *>(d + r * H + ib + 4 * q) = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ grouping
+
+// Routes grouped by pool row with a counting sort in LDS: per-row counts
+// (atomics), one prefix sum over the rows numbers the groups in ascending
+// row order, and each route lands at its row's start plus its arrival
+// rank.  The order of routes inside a group is therefore not fixed; every
+// consumer computes each route independently of its position.
+constexpr int kCountThreads = 1024;
+constexpr int kCountWaves = kCountThreads / kWave;
+constexpr int kCountRoutesPerThread = 8;   // up to 8192 routes
+
+__global__ __launch_bounds__(kCountThreads) void group_count_kernel(
+    const int32_t *__restrict__ idx, int n, int num_rows, int32_t *__restrict__ n_groups,
+    int32_t *__restrict__ grp_row, int32_t *__restrict__ grp_start, int32_t *__restrict__ grp_count,
+    int32_t *__restrict__ grp_routes) {
+    extern __shared__ __align__(16) int32_t lds[];
+    int32_t *wsum = lds;          // [kCountWaves]
+    int32_t *cnt = lds + 32;      // [num_rows] counts, then starts
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+
+    for (int r = tid; r < num_rows; r += kCountThreads) cnt[r] = 0;
+    __syncthreads();
+    int row[kCountRoutesPerThread], pos[kCountRoutesPerThread];
+#pragma unroll
+    for (int k = 0; k < kCountRoutesPerThread; ++k) {
+        const int i = tid + k * kCountThreads;
+        const int r = i < n ? idx[i] : -1;
+        row[k] = (r >= 0 && r < num_rows) ? r : -1;
+        pos[k] = row[k] >= 0 ? atomicAdd(&cnt[row[k]], 1) : 0;
+    }
+    __syncthreads();
+
+    // Each thread owns a run of rows: counts and non-empty rows, then one
+    // block prefix sum of both (packed: routes in the low 16 bits, groups
+    // in the high 16; both are at most 8192).
+    const int run = (num_rows + kCountThreads - 1) / kCountThreads;
+    const int r0 = tid * run;
+    int routes = 0, groups = 0;
+    for (int k = 0; k < run; ++k) {
+        const int r = r0 + k;
+        if (r < num_rows) {
+            const int v = cnt[r];
+            routes += v;
+            groups += v > 0;
+        }
+    }
+    const int packed = routes | (groups << 16);
+    const int incl = wave_inclusive_sum(packed);
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kCountWaves; ++w) {
+        const int v = wsum[w];
+        woff += w < wave ? v : 0;
+        tot += v;
+    }
+    int pre = woff + incl - packed;
+    int start = pre & 0xffff, g = pre >> 16;
+    for (int k = 0; k < run; ++k) {
+        const int r = r0 + k;
+        if (r < num_rows) {
+            const int v = cnt[r];
+            if (v > 0) {
+                grp_row[g] = r;
+                grp_start[g] = start;
+                grp_count[g] = v;
+                ++g;
+            }
+            cnt[r] = start;
+            start += v;
+        }
+    }
+    if (tid == 0) n_groups[0] = tot >> 16;
+    // group slots past the last group read as "no row"
+    for (int gg = (tot >> 16) + tid; gg < min(n, num_rows); gg += kCountThreads) grp_row[gg] = -1;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kCountRoutesPerThread; ++k) {
+        const int i = tid + k * kCountThreads;
+        if (row[k] >= 0) grp_routes[cnt[row[k]] + pos[k]] = i;
+    }
+}
+
+}  // namespace mfma_detail
+
+// ------------------------------------------------------------------ launchers
+
+bool group_mfma_supported(int fmt, int H, int F) {
+    (void)fmt;
+    return H >= mfma_detail::kSlab && F >= mfma_detail::kSlab && H % mfma_detail::kSlab == 0 &&
+           F % mfma_detail::kSlab == 0;
+}
+
+hipError_t launch_up_mfma(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
+                          uint16_t *h, hipStream_t s) {
+    using namespace mfma_detail;
+    if (max_items <= 0) return hipSuccess;
+    const dim3 grid((pool.F + kRowsPerBlock - 1) / kRowsPerBlock, max_items);
+    if (pool.fmt == MOE_FMT_BF16)
+        hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_BF16>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
+    else
+        hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_E2M1>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_mfma(const PoolView &pool, const Items &items, int max_items, const uint16_t *h,
+                            float *d, hipStream_t s) {
+    using namespace mfma_detail;
+    if (max_items <= 0) return hipSuccess;
+    if (pool.fmt == MOE_FMT_BF16) {
+        constexpr int rows = down_rows_per_block<MOE_FMT_BF16>();
+        const dim3 grid((pool.H + rows - 1) / rows, max_items);
+        hipLaunchKernelGGL(down_mfma_kernel<MOE_FMT_BF16>, grid, dim3(kMThreads), 0, s, pool, items, h, d);
+    } else {
+        constexpr int rows = down_rows_per_block<MOE_FMT_E2M1>();
+        const dim3 grid((pool.H + rows - 1) / rows, max_items);
+        hipLaunchKernelGGL(down_mfma_kernel<MOE_FMT_E2M1>, grid, dim3(kMThreads), 0, s, pool, items, h, d);
+    }
+    return hipGetLastError();
+}
+
+size_t group_count_lds_bytes(int num_rows) { return (32 + (size_t)num_rows) * 4; }
+
+bool group_count_supported(int num_rows, int routes) {
+    return routes <= mfma_detail::kCountThreads * mfma_detail::kCountRoutesPerThread &&
+           group_count_lds_bytes(num_rows) <= (size_t)kGroupCountMaxLds;
+}
+
+hipError_t group_count_prepare() {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_detail::group_count_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kGroupCountMaxLds);
+}
+
+hipError_t launch_group_count(const int32_t *idx, int routes, int num_rows, int32_t *n_groups,
+                              int32_t *grp_row, int32_t *grp_start, int32_t *grp_count,
+                              int32_t *grp_routes, hipStream_t s) {
+    using namespace mfma_detail;
+    hipLaunchKernelGGL(group_count_kernel, dim3(1), dim3(kCountThreads), group_count_lds_bytes(num_rows),
+                       s, idx, routes, num_rows, n_groups, grp_row, grp_start, grp_count, grp_routes);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -230,7 +230,9 @@ hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t 
     int32_t *gcount = reinterpret_cast<int32_t *>(ws + L.grp_count);
     int32_t *groutes = reinterpret_cast<int32_t *>(ws + L.grp_routes);
     float *d = reinterpret_cast<float *>(ws + L.d);
-    hipError_t e = launch_group_routes(idx, n, pv.num_rows, ng, grow, gstart, gcount, groutes, s);
+    hipError_t e = group_count_supported(pv.num_rows, n)
+                       ? launch_group_count(idx, n, pv.num_rows, ng, grow, gstart, gcount, groutes, s)
+                       : launch_group_routes(idx, n, pv.num_rows, ng, grow, gstart, gcount, groutes, s);
     if (e != hipSuccess) return e;
     Items it{};
     it.mode = ITEM_GROUP;
@@ -242,9 +244,15 @@ hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t 
     it.grp_count = gcount;
     it.grp_routes = groutes;
     const int max_items = std::min(n, pv.num_rows);
-    e = launch_up(pv, it, max_items, x, h, nullptr, nullptr, s);
-    if (e != hipSuccess) return e;
-    e = launch_down_to_d(pv, it, max_items, h, d, nullptr, s);
+    if (group_mfma_supported(pv.fmt, pv.H, pv.F)) {
+        e = launch_up_mfma(pv, it, max_items, x, h, s);
+        if (e != hipSuccess) return e;
+        e = launch_down_mfma(pv, it, max_items, h, d, s);
+    } else {
+        e = launch_up(pv, it, max_items, x, h, nullptr, nullptr, s);
+        if (e != hipSuccess) return e;
+        e = launch_down_to_d(pv, it, max_items, h, d, nullptr, s);
+    }
     if (e != hipSuccess) return e;
     return launch_combine(idx, w, T, K, pv.H, pv.num_rows, d, addend, out, s);
 }
@@ -554,6 +562,7 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
         const size_t glds = group_lds_bytes((int)(T * K));
         if (glds > (size_t)max_lds) return bail(fail(MOE_UNSUPPORTED, "route grouping LDS too large"));
         HIP_TRY(group_prepare(glds), "grouping LDS attribute");
+        HIP_TRY(group_count_prepare(), "grouping LDS attribute");
         if ((int64_t)T * K > d->max_routes)
             return bail(fail(MOE_INVALID_ARG, "max_tokens * max_top_k > max_routes"));
     }
@@ -651,6 +660,7 @@ moe_status_t moe_routed_decode(const moe_pool_t *pool, const void *x, const int3
         const size_t glds = group_lds_bytes(T * K);
         if (glds > (size_t)max_lds) return fail(MOE_UNSUPPORTED, "too many routes to group");
         HIP_TRY(group_prepare(glds), "grouping LDS attribute");
+        HIP_TRY(group_count_prepare(), "grouping LDS attribute");
     }
     HIP_TRY(routed_sequence(pv, static_cast<const uint16_t *>(x), idx, w, T, K, addend,
                             static_cast<uint16_t *>(out), static_cast<uint8_t *>(ws),

@@ -191,7 +191,7 @@ struct Items {
     int32_t n;                  // routes (ITEM_ROUTE / ITEM_ALL)
     const int32_t *idx;         // [routes] pool rows (ITEM_ROUTE)
     const int32_t *n_groups;    // [1] (ITEM_GROUP)
-    const int32_t *grp_row;     // [groups]
+    const int32_t *grp_row;     // [min(routes, rows)] pool row per group, -1 past the last
     const int32_t *grp_start;   // [groups]
     const int32_t *grp_count;   // [groups]
     const int32_t *grp_routes;  // [routes] route ids sorted by group
@@ -251,5 +251,19 @@ hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, co
 
 // Shape support of the expert kernels for one matrix width.
 bool expert_shape_supported(int fmt, int H, int F);
+
+// Wide steps (k_group.hip): counting-sort grouping and the MFMA group kernels.
+constexpr int kGroupCountMaxLds = 4 * (32 + 32768);  // pools of up to 32768 rows
+size_t group_count_lds_bytes(int num_rows);
+bool group_count_supported(int num_rows, int routes);
+hipError_t group_count_prepare();
+hipError_t launch_group_count(const int32_t *idx, int routes, int num_rows, int32_t *n_groups,
+                              int32_t *grp_row, int32_t *grp_start, int32_t *grp_count,
+                              int32_t *grp_routes, hipStream_t s);
+bool group_mfma_supported(int fmt, int H, int F);
+hipError_t launch_up_mfma(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
+                          uint16_t *h, hipStream_t s);
+hipError_t launch_down_mfma(const PoolView &pool, const Items &items, int max_items, const uint16_t *h,
+                            float *d, hipStream_t s);
 
 }  // namespace moe

@@ -103,6 +103,26 @@ def test_routed_matches_oracle(fmt, H, F, rows, T, K):
     _close(_bf16_to_f64(out), ref, f"fmt{fmt} H{H} T{T}")
 
 
+@pytest.mark.parametrize("fmt,rows", [(0, 6), (1, 6), (0, 2), (1, 2)])
+def test_grouped_routes_do_not_depend_on_their_place_in_the_group(fmt, rows):
+    """Wide steps put a group's routes in arrival order; a token's output
+    must not depend on it.  Permuting the tokens permutes the output bit
+    for bit -- with groups of about 13 routes (one MFMA token tile) and of
+    about 40 (two passes of two tiles)."""
+    H, F, T, K = 1024, 256, 40, 2
+    g = W.rng(9, "place", fmt, rows)
+    _, pool, opool = _pool_pair(fmt, rows, H, F, 10)
+    x = W.normal_bf16(g, (T, H))
+    idx = np.stack([g.choice(rows, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = g.random((T, K))
+    a = _routed_gpu(pool, x, idx, w, H)
+    perm = g.permutation(T)
+    b = _routed_gpu(pool, x[perm], idx[perm], w[perm], H)
+    assert torch.equal(b, a[torch.from_numpy(perm).cuda()])
+    ref = oracle.routed(opool, idx, w.astype(np.float32).astype(np.float64), x)
+    _close(_bf16_to_f64(a), ref, f"fmt{fmt} rows{rows}")
+
+
 def test_routed_skips_minus_one_and_rows_outside_the_pool():
     """[P1 section 5] a -1 route adds nothing; rows >= num_rows are treated
     the same way."""
