@@ -289,30 +289,41 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 // maximum over 64-bit (value key, ~index) pairs strictly below the previous
 // pick, i.e. largest first and lower expert id first among equals.  The
 // weights are the softmax over the picks (1/K each if all are -infinity).
-__device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int K,
-                                          int32_t *ids_lds, float *w_out) {
+// Top-K of one row of E logits by one wave.  Each lane holds the keys of
+// experts lane, lane + 64, ... (NC of them) and its best key not yet taken;
+// a round takes the wave's maximum of those (two 32-bit DPP max passes:
+// value, then id among the lanes holding that value), and only the lane
+// that held it looks for its next best.
+template <int NC>
+__device__ __forceinline__ void wave_topk_nc(const float *__restrict__ row, int E, int K,
+                                             int32_t *ids_lds, float *w_out) {
     const int lane = threadIdx.x & (kWave - 1);
-    // All of the row's loads in flight together (clamped in-range indices),
-    // then the keys.
-    float lv[kTopkMaxPerLane];
+    // all of the row's loads in flight together (clamped in-range indices)
+    float lv[NC];
 #pragma unroll
-    for (int c = 0; c < kTopkMaxPerLane; ++c) lv[c] = row[min(lane + kWave * c, E - 1)];
-    uint64_t keys[kTopkMaxPerLane];
+    for (int c = 0; c < NC; ++c) lv[c] = row[min(lane + kWave * c, E - 1)];
+    uint64_t keys[NC];
+    uint64_t lb = 0ull;
 #pragma unroll
-    for (int c = 0; c < kTopkMaxPerLane; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int e = lane + kWave * c;
         keys[c] = e < E ? ((uint64_t)logit_key(lv[c]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)
                         : 0ull;
+        lb = keys[c] > lb ? keys[c] : lb;
     }
-    uint64_t prev = ~0ull, mine = 0ull;
+    uint64_t mine = 0ull;
     for (int k = 0; k < K; ++k) {
-        uint64_t best = 0ull;
-#pragma unroll
-        for (int c = 0; c < kTopkMaxPerLane; ++c)
-            if (keys[c] < prev && keys[c] > best) best = keys[c];
-        best = wave_max_u64(best);
+        const uint32_t mh = wave_max_u32((uint32_t)(lb >> 32));
+        const uint32_t ml = wave_max_u32((uint32_t)(lb >> 32) == mh ? (uint32_t)lb : 0u);
+        const uint64_t best = ((uint64_t)mh << 32) | ml;
         if (lane == k) mine = best;
-        prev = best;
+        if (lb == best) {
+            uint64_t nb = 0ull;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (keys[c] < best && keys[c] > nb) nb = keys[c];
+            lb = nb;
+        }
     }
     const float v = key_logit((uint32_t)(mine >> 32));
     const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
@@ -325,11 +336,183 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, 
     }
 }
 
+__device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int K,
+                                          int32_t *ids_lds, float *w_out) {
+    const int nc = (E + kWave - 1) / kWave;
+    if (nc <= 1) wave_topk_nc<1>(row, E, K, ids_lds, w_out);
+    else if (nc <= 2) wave_topk_nc<2>(row, E, K, ids_lds, w_out);
+    else if (nc <= 4) wave_topk_nc<4>(row, E, K, ids_lds, w_out);
+    else if (nc <= 8) wave_topk_nc<8>(row, E, K, ids_lds, w_out);
+    else wave_topk_nc<16>(row, E, K, ids_lds, w_out);
+}
+
 // Register-resident admission.  p.order holds (slot, owner) pairs here, so
 // the owners of victim candidates arrive with the order itself.  Every
 // write to the persistent state is deferred to the final phase: a barrier
 // waits for a wave's outstanding memory operations, so stores issued
 // between barriers would each cost a memory round trip.
+constexpr int kNarrowWindow = 4 * kWave;
+
+// Orders LDS accesses of one wave: a compiler fence (a wave's LDS
+// instructions execute in issue order).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+struct lds_view {
+    int32_t *cnt, *resl, *dlist, *missl, *pslot, *pold, *pexp, *ids_l;
+    uint16_t *slot_e;
+    uint8_t *touched, *filled;
+    int32_t *misc;
+};
+
+// The whole admission step of at most 64 routes by wave 0 (lane i = route
+// i, then lane j = distinct expert j), with the same steps and results as
+// the wide path: histogram, ascending distinct list, the queries (hits
+// used, misses ascending, the j-th admitted miss takes the j-th unused
+// entry of the LRU order), and every write of the step except the order
+// itself.  The victims of a query are among the first
+//   (slots used so far this step) + (misses) <= 2 * 64 + 64
+// entries of the order, inside the 256-entry window the wave holds.
+__device__ __forceinline__ void narrow_step(const AdmitParams &p, lds_view v, const int (&wslot)[4],
+                                         const int (&wown)[4], uint32_t now) {
+    const int lane = threadIdx.x;
+    const int E = p.E, R = p.R;
+    const int64_t lbase = (int64_t)p.layer * E;
+
+    const int e_i = lane < R ? v.ids_l[lane] : -1;
+    const bool valid = lane < R && e_i >= 0 && e_i < E;
+    if (valid) atomicAdd(&v.cnt[e_i], 1);
+    const int ninvalid = __popcll(__ballot(lane < R && !valid));
+    wave_lds_fence();
+
+    // distinct valid experts, ascending: each lane scans a run of E
+    const int run = (E + kWave - 1) / kWave;
+    int c = 0;
+    for (int q = 0; q < run; ++q) {
+        const int e = lane * run + q;
+        c += (e < E && v.cnt[e] > 0);
+    }
+    const int incl = wave_inclusive_sum(c);
+    const int nD = __builtin_amdgcn_readlane(incl, kWave - 1);
+    {
+        int off = incl - c;
+        for (int q = 0; q < run; ++q) {
+            const int e = lane * run + q;
+            if (e < E && v.cnt[e] > 0) v.dlist[off++] = e;
+        }
+    }
+    wave_lds_fence();
+
+    int qwid, nq;
+    if (R <= p.one_call) {
+        qwid = nD > 0 ? nD : 1;
+        nq = nD > 0 ? 1 : 0;
+    } else {
+        qwid = p.query_width;
+        nq = (nD + qwid - 1) / qwid;
+    }
+    int fetched = 0, nplan = 0, nmissed = 0, noverflow = 0;
+    for (int q = 0; q < nq; ++q) {
+        const int qs = q * qwid;
+        const int qn = min(qs + qwid, nD) - qs;
+        // hits are used now; misses ranked in ascending expert order
+        const int e = lane < qn ? v.dlist[qs + lane] : -1;
+        const int s = e >= 0 ? v.resl[e] : -1;
+        if (e >= 0 && s >= 0) v.touched[s] = 1;
+        const bool miss = e >= 0 && s < 0;
+        const uint64_t mm = __ballot(miss);
+        const int nm = __popcll(mm);
+        if (miss)
+            v.missl[__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u))] = e;
+        nmissed += nm;
+        int allowed = nm;
+        if (p.max_fetch >= 0) allowed = min(nm, max(0, p.max_fetch - fetched));
+        wave_lds_fence();
+        if (allowed > 0) {
+            bool el[4];
+            int ce = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                el[i] = wslot[i] >= 0 && v.touched[wslot[i]] == 0;
+                ce += el[i];
+            }
+            const int incl2 = wave_inclusive_sum(ce);
+            const int elig = __builtin_amdgcn_readlane(incl2, kWave - 1);
+            int r = incl2 - ce;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (el[i]) {
+                    if (r < allowed) {
+                        const int j = nplan + r;
+                        const int em = v.missl[r];
+                        v.pslot[j] = wslot[i];
+                        v.pold[j] = wown[i];
+                        v.pexp[j] = em;
+                        v.resl[em] = wslot[i];
+                        v.filled[em] = 1;
+                        const int old = wown[i];
+                        // an expert of this layer losing its slot may belong to a
+                        // later query of this step: it becomes a miss there
+                        if (old >= lbase && old < lbase + E) v.resl[old - lbase] = -1;
+                    }
+                    ++r;
+                }
+            }
+            const int nv = min(allowed, elig);
+            wave_lds_fence();
+            for (int j = lane; j < nv; j += kWave) v.touched[v.pslot[nplan + j]] = 1;
+            wave_lds_fence();
+            noverflow += nm - nv;
+            nplan += nv;
+            fetched += nv;
+        } else {
+            noverflow += nm;
+        }
+    }
+
+    // expert -> plan entry, for the routes' plan indices
+    if (p.route_plan) {
+        for (int j = lane; j < nplan; j += kWave) v.missl[v.pexp[j]] = j;
+        wave_lds_fence();
+    }
+    if (lane < R) {
+        p.ids[lane] = valid ? v.resl[e_i] : -1;
+        if (p.route_plan) p.route_plan[lane] = (valid && v.filled[e_i]) ? v.missl[e_i] : -1;
+    }
+    for (int e = lane; e < E; e += kWave) p.res[lbase + e] = v.resl[e];
+    for (int j = lane; j < nplan; j += kWave) {
+        const int s = v.pslot[j], old = v.pold[j], em = v.pexp[j];
+        if (old >= 0 && !(old >= lbase && old < lbase + E)) p.res[old] = -1;
+        p.own[s] = (int32_t)(lbase + em);
+        p.plan_slot[j] = s;
+        p.plan_expert[j] = em;
+    }
+    for (int i = lane; i < nD; i += kWave) {
+        const int e = v.dlist[i];
+        const int s = v.resl[e];
+        if (s >= 0) {
+            p.stamp[s] = now;
+            v.slot_e[s] = (uint16_t)e;
+        }
+        atomicAdd(reinterpret_cast<unsigned long long *>(&p.freq[lbase + e]),
+                  (unsigned long long)v.cnt[e]);
+    }
+    if (lane == 0) {
+        unsigned long long *st =
+            reinterpret_cast<unsigned long long *>(p.stats + (int64_t)p.layer * MOE_NUM_STATS);
+        atomicAdd(&st[MOE_STAT_CALLS], 1ull);
+        atomicAdd(&st[MOE_STAT_MET], (unsigned long long)nD);
+        atomicAdd(&st[MOE_STAT_MISSED], (unsigned long long)nmissed);
+        atomicAdd(&st[MOE_STAT_OVERFLOW], (unsigned long long)noverflow);
+        atomicAdd(&st[MOE_STAT_INVALID], (unsigned long long)ninvalid);
+        p.clock[0] = now;
+        p.n_miss[0] = nplan;
+        v.misc[1] = nD;
+    }
+}
+
 template <int P>
 __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     extern __shared__ __align__(16) int32_t lds[];
@@ -376,6 +559,20 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
 #pragma unroll
     for (int q = 0; q < P; ++q)
         if (tid * P + q >= S) ord[q] = owner[q] = -1;
+    // A narrow step (at most one route per lane of wave 0) is admitted by
+    // wave 0 alone; its victims come from the head of the LRU order, of
+    // which the wave holds the first kNarrowWindow entries (four per lane).
+    const bool narrow = R <= kWave;
+    int wslot[4], wown[4];
+    if (narrow && wave == 0) {
+        const int4 *q4 = reinterpret_cast<const int4 *>(p.order) + tid * 2;
+        const int4 a = q4[0], b = q4[1];
+        wslot[0] = a.x; wown[0] = a.y; wslot[1] = a.z; wown[1] = a.w;
+        wslot[2] = b.x; wown[2] = b.y; wslot[3] = b.z; wown[3] = b.w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (tid * 4 + i >= S) wslot[i] = wown[i] = -1;
+    }
     // The layer's slot map row into LDS: loads of a batch issued together
     // (clamped in-range indices), stores after.
     for (int e0 = 0; e0 < E; e0 += 4 * kThreads) {
@@ -404,6 +601,14 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     }
     __syncthreads();
 
+    int nD;
+    if (narrow) {
+        if (wave == 0) narrow_step(p, lds_view{cnt, resl, dlist, missl, pslot, pold, pexp, ids_l, slot_e,
+                                                touched, filled, misc},
+                                   wslot, wown, now);
+        __syncthreads();
+        nD = misc[1];
+    } else {
     // Histogram of the valid routes; invalid routes counted.
     int my_invalid = 0;
     for (int i = tid; i < R; i += kThreads) {
@@ -418,7 +623,6 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
 
     // Distinct valid experts, ascending: each thread scans a run of E.
     const int erun = (E + kThreads - 1) / kThreads;
-    int nD;
     {
         int c = 0;
         for (int q = 0; q < erun; ++q) {
@@ -551,6 +755,8 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
         p.clock[0] = now;
         p.n_miss[0] = nplan;
     }
+
+    }  // wide step
 
     // LRU order: the unused entries keep their order; the used slots follow
     // in ascending slot order (they share this step's stamp), each owned by

@@ -109,6 +109,19 @@ __device__ __forceinline__ float group_total(float v) {
     return __uint_as_float(u);
 }
 
+// Maximum of a 32-bit unsigned value over the wave, returned to every lane:
+// a max-scan with the shift/broadcast pattern (lane 63 ends with the
+// maximum), then read back from lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_or_zero<kDppRowShr1>(v));
+    v = max(v, dpp_or_zero<kDppRowShr2>(v));
+    v = max(v, dpp_or_zero<kDppRowShr4>(v));
+    v = max(v, dpp_or_zero<kDppRowShr8>(v));
+    v = max(v, dpp_or_zero<kDppRowBcast15, 0xa>(v));
+    v = max(v, dpp_or_zero<kDppRowBcast31, 0xc>(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Maximum of a 64-bit value over the wave, returned to every lane: the same
 // shift/broadcast pattern as a max-scan (lane 63 ends with the maximum),
 // then read back from lane 63.  Values must be >= 0 (0 fills the gaps).

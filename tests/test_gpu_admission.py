@@ -162,3 +162,17 @@ def test_large_cache_uses_the_general_kernel():
     steps = [(int(g.integers(0, L)), g.integers(-1, E, int(g.integers(1, 700))), int(g.choice([-1, 5])))
              for _ in range(60)]
     _run(L, E, S, steps, check_every=10)
+
+
+@pytest.mark.parametrize("one,qw", [(256, 128), (20, 8), (1, 1)])
+def test_narrow_steps_with_caps_and_invalid_ids(one, qw):
+    """Steps of at most 64 routes (one route per lane of a wave), over a
+    cache larger than 256 slots, with fetch caps, ids outside [0, E) and
+    evictions across layers, at one-call and chunked widths."""
+    g = np.random.default_rng(14 + one)
+    L, E, S = 3, 200, 300
+    steps = []
+    for _ in range(300):
+        R = int(g.integers(0, 65))
+        steps.append((int(g.integers(0, L)), g.integers(-3, E + 3, R), int(g.choice([-1, -1, 0, 2, 9]))))
+    _run(L, E, S, steps, one=one, qw=qw)
