@@ -23,6 +23,12 @@ Also reported:
                  graph, 40 replays, microseconds per admission by routes.
   cpu_baseline   the oracle (plain C, one thread) on a bounded sample of
                  the same decode workload.
+
+Profile summaries: with --launch-log the run also writes which launches
+the timed and instrumented passes made (and this line); the summaries in
+profiles/ are made from a rocprofv3 trace (or counter run) of the same
+command by --summarize-trace / --summarize-pmc, over exactly the launches
+the line's figures average.
 """
 from __future__ import annotations
 
@@ -41,6 +47,9 @@ L, E, K, H, F, S = 40, 256, 8, 2048, 512, 3164
 ROW_BYTES = 6 * F * H            # one bf16 expert: w13 (4FH) + w2 (2FH) bytes
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 HOST_LINK_PEAK_GBS = 64.0        # PCIe 5.0 x16, one direction
+GEMV_PASSES = 4                  # routed-GEMV phase: passes over the 40 layers per graph
+GEMV_REPLAYS = 5                 # timed replays of that graph (after one untimed)
+GEMV_HEAD_START_CYCLES = 100_000_000  # spin before the timed calls (tens of ms of shader clock)
 
 
 def log(*a):
@@ -113,12 +122,21 @@ def make_trace(torch, W, n, seed=0):
     return (torch.from_numpy(lg).cuda(), torch.from_numpy(xs.view(np.int16)).cuda())
 
 
-def capture(torch, lay, x_st, lg_st, out):
+def capture(torch, lay, x_st, lg_st, out, ids=None, w=None, pairs=None):
+    """The 40-layer token graph; with `pairs` (two lists of L created
+    events), each layer step is preceded by an empty event pair (two
+    event-record nodes back to back)."""
+    import expert_slot_cache_moe_amd as m
+
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         for l in range(L):
-            lay.decode(l, x_st[l], lg_st[l], K, out[l])
+            if pairs is not None:
+                m.moe_record_event(pairs[0][l], stream)
+                m.moe_record_event(pairs[1][l], stream)
+            lay.decode(l, x_st[l], lg_st[l], K, out[l], ids_out=None if ids is None else ids[l],
+                       w_out=None if w is None else w[l])
     return graph
 
 
@@ -209,6 +227,194 @@ def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
                       f"single-threaded C oracle (double precision), {dt:.1f} s"}
 
 
+DECODE_KERNELS = ("admit_fast_kernel", "admit_kernel", "topk_kernel", "stage1_kernel", "stage2_kernel",
+                  "gather_kernel", "up_kernel", "down_d_kernel", "down_fused_kernel")
+
+
+def _short(name: str) -> str:
+    for k in DECODE_KERNELS:
+        if k in name:
+            return k
+    return ""
+
+
+def _read_dispatches(path, value_col=None):
+    import csv
+
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = _short(r["Kernel_Name"])
+            d = {"id": int(r["Dispatch_Id"]), "k": k, "name": r["Kernel_Name"]}
+            if "Start_Timestamp" in r and r["Start_Timestamp"]:
+                d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            if value_col:
+                if r.get("Counter_Name") != value_col:
+                    continue
+                d["v"] = float(r["Counter_Value"])
+            out.append(d)
+    out.sort(key=lambda d: d["id"])
+    return out
+
+
+def _split(log, moe):
+    """The moe dispatches of a bench run, in submission order, cut into
+    (timed layer steps, instrumented layer steps, routed-GEMV calls): a
+    staged layer step is admission, stage 1, stage 2; a routed-GEMV call is
+    stage 1, stage 2."""
+    L, W_, K_ = log["layers"], log["warmup"], log["steps"]
+    n_steps = (W_ + 2 * K_) * L
+    dec = moe[:3 * n_steps]
+    steps = [dec[i:i + 3] for i in range(0, len(dec), 3)]
+    ok = len(steps) == n_steps and all(
+        [d["k"] for d in st] == ["admit_fast_kernel", "stage1_kernel", "stage2_kernel"] for st in steps)
+    if not ok:
+        raise SystemExit("trace does not hold the staged decode launches the run made")
+    g = moe[3 * n_steps:3 * n_steps + 2 * log["gemv_calls"]]
+    calls = [g[i:i + 2] for i in range(0, len(g), 2)]
+    if len(calls) != log["gemv_calls"] or any([d["k"] for d in c] != ["stage1_kernel", "stage2_kernel"]
+                                              for c in calls):
+        raise SystemExit("trace does not hold the routed-GEMV launches the run made")
+    return steps[W_ * L:(W_ + K_) * L], steps[(W_ + K_) * L:], calls
+
+
+def stage1_expected_bytes(fetched):
+    """Bytes a fetching stage-1 launch must move: each fetched expert's row
+    read over the host link and written to its slot (its gate/up dots are
+    taken from the stream), the gate/up rows of the other routes and of
+    the shared expert read from HBM, and x."""
+    fetched = np.asarray(fetched, np.float64)
+    return 2 * fetched * ROW_BYTES + (K - fetched) * 4 * F * H + 4 * F * H + 2 * H
+
+
+def summarize_trace(csv_path, log_path):
+    log = json.load(open(log_path))
+    disp = _read_dispatches(csv_path)
+    timed, inst, calls = _split(log, [d for d in disp if d["k"]])
+    fetched = np.asarray(log["fetched"])
+    line = log.get("line", {})
+    out = []
+    p = out.append
+    p(f"# Kernel durations: {log['workload']}\n")
+    p("Command (repository root, MI355X):\n")
+    p(f"    {log['trace_command']}\n")
+    p("Summarised by `python3 bench.py --summarize-trace <kernel_trace.csv> --launch-log <log>`.")
+    p(f"The run made {log['warmup']} warm-up tokens, {log['steps']} timed tokens (graph replays, no "
+      f"events), an instrumented pass over the same {log['steps']} tokens from the same cache state "
+      f"(HIP events captured around each layer's launches), {log['layers']} layer steps per token, "
+      f"then the routed-GEMV phase ({log['gemv_calls']} moe_routed_decode calls over resident slots, "
+      f"the last {log['gemv_timed_calls']} timed) and the admission-only benchmark.\n")
+    stats = csv_path.replace("kernel_trace.csv", "kernel_stats.csv")
+    if stats != csv_path and os.path.exists(stats):
+        import csv
+
+        p("## All launches: rocprofv3 --stats (kernel_stats.csv)\n")
+        p("| kernel | calls | total ms | mean µs | min µs | max µs |")
+        p("|---|---|---|---|---|---|")
+        for r in csv.DictReader(open(stats)):
+            nm = _short(r["Name"]) or r["Name"].split("(")[0].replace("void ", "")[:60]
+            p(f"| {nm} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+              f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+              f"{float(r['MaxNs']) / 1e3:.2f} |")
+        p("")
+
+    def dur(steps, i):
+        return np.asarray([st[i]["us"] for st in steps])
+
+    hit, miss = fetched == 0, fetched > 0
+    rl, rg = line.get("roofline", {}), line.get("roofline_gemv", {})
+    tok = np.asarray([sum(d["us"] for st in timed[i:i + log["layers"]] for d in st)
+                      for i in range(0, len(timed), log["layers"])])
+    p("## The bench line's figures\n")
+    p("| figure | launches | rocprofv3 mean µs | bench (HIP events) µs |")
+    p("|---|---|---|---|")
+    p(f"| stage1_kernel in layer steps that fetched, instrumented pass (roofline) | {int(miss.sum())} | "
+      f"{dur(inst, 1)[miss].mean():.2f} | {rl.get('avg_launch_us')} |")
+    gc = np.asarray([c[0]["us"] + c[1]["us"] for c in calls])[-log["gemv_timed_calls"]:]
+    p(f"| stage1_kernel + stage2_kernel per moe_routed_decode call, routed-GEMV phase (roofline_gemv) | "
+      f"{len(gc)} | {gc.mean():.2f} | {rg.get('avg_launch_us')} |")
+    p(f"| decode kernels per timed token (ms) | {len(tok)} | {tok.mean() / 1000:.4f} | "
+      f"{line.get('ms_per_step')} (ms_per_step) |")
+    p("")
+    p("The roofline interval is read between event-record nodes captured around the launch in the "
+      f"graph ({rl.get('avg_launch_us_events')} µs); the nodes add their own processing to it, "
+      f"which an empty pair of nodes recorded before every layer step measures "
+      f"({rl.get('empty_event_pair_us')} µs) and the bench takes off.  The routed-GEMV "
+      "figure is one event pair inside the graph around its 160 calls, divided by the calls.  "
+      "ms_per_step is wall time over the timed replays (it also holds the per-token input "
+      "copies).\n")
+    p("## The timed tokens by kind of layer step (graph replays, no events; rocprofv3 only)\n")
+    p("The timed and instrumented passes replay the same tokens from the same cache state, so "
+      "each layer step has the same fetch count in both.\n")
+    p("| launch | launches | rocprofv3 mean µs |")
+    p("|---|---|---|")
+    p(f"| admit_fast_kernel (admission + fused top-k) | {len(timed)} | {dur(timed, 0).mean():.2f} |")
+    p(f"| stage1_kernel, layer steps that fetched | {int(miss.sum())} | {dur(timed, 1)[miss].mean():.2f} |")
+    p(f"| stage1_kernel, all-hit layer steps | {int(hit.sum())} | {dur(timed, 1)[hit].mean():.2f} |")
+    p(f"| stage2_kernel, all layer steps | {len(timed)} | {dur(timed, 2).mean():.2f} |")
+    p(f"| stage1 + stage2, all-hit layer steps (8 routed + shared expert) | {int(hit.sum())} | "
+      f"{(dur(timed, 1) + dur(timed, 2))[hit].mean():.2f} |")
+    p("")
+    if line:
+        p("## bench.py line of the same run\n")
+        p("    " + json.dumps(line))
+    print("\n".join(out))
+
+
+def summarize_pmc(fetch_csv, write_csv, log_path):
+    log = json.load(open(log_path))
+    fetched = np.asarray(log["fetched"])
+    res = {}
+    copy = {}
+    for cname, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        disp = _read_dispatches(path, cname)
+        copies = [d for d in disp if "copyBuffer" in d["name"]]
+        copy[cname] = copies[-1]["v"]            # the 256 MiB device copy ends the run
+        _, inst, calls = _split(log, [d for d in disp if d["k"]])
+        res[cname] = {"stage1_kernel": np.asarray([st[1]["v"] for st in inst]),
+                      "admit_fast_kernel": np.asarray([st[0]["v"] for st in inst]),
+                      "gemv": np.asarray([c[0]["v"] + c[1]["v"] for c in calls])[-log["gemv_timed_calls"]:]}
+    mib = 262144.0                                  # KiB moved each way by the calibration copy
+    fs, ws = mib / copy["FETCH_SIZE"], mib / copy["WRITE_SIZE"]
+    miss = fetched > 0
+    f1, w1 = res["FETCH_SIZE"]["stage1_kernel"], res["WRITE_SIZE"]["stage1_kernel"]
+    fg, wg = res["FETCH_SIZE"]["gemv"], res["WRITE_SIZE"]["gemv"]
+    gather_kib = fetched[miss].mean() * ROW_BYTES / 1024.0
+    stage1_kib = stage1_expected_bytes(fetched[miss]).mean() / 1024.0
+    gemv_kib = (K * ROW_BYTES + 2 * H * 2 + K * 8) / 1024.0
+    miss_traffic = (f1[miss] * fs + w1[miss] * ws).mean()
+    gemv_traffic = (fg * fs + wg * ws).mean()
+    print(f"""# HBM / host-link traffic of the decode-step kernels: {log['workload']}
+#
+# Commands (two passes, one counter each, from the repository root):
+#   {log['pmc_command'].replace('<C>', 'FETCH_SIZE')}
+#   {log['pmc_command'].replace('<C>', 'WRITE_SIZE')}
+# Summarised by: python3 bench.py --summarize-pmc <FETCH csv> <WRITE csv> --launch-log <log>
+#
+# Calibration: the run ends with a 256 MiB device-to-device copy
+# (262144 KiB read and 262144 KiB written); its counters read
+# FETCH_SIZE = {copy['FETCH_SIZE']:.1f} KiB and WRITE_SIZE = {copy['WRITE_SIZE']:.1f} KiB, so
+# fetch_scale = {fs:.3f} and write_scale = {ws:.3f}.
+#
+# Instrumented pass ({int(miss.sum())} layer steps that fetched) and routed-GEMV phase, mean KiB per launch:
+#   stage1_kernel, fetching steps:  FETCH {f1[miss].mean():10.1f}  WRITE {w1[miss].mean():10.1f}
+#       gathered bytes (algorithmic): {gather_kib:10.1f} KiB read over the host link, same written
+#       all bytes the launch must move: {stage1_kib:10.1f} KiB (gathered rows read and written, gate/up
+#       rows of the resident routes and of the shared expert read, x read)
+#   routed GEMV (moe_routed_decode, stage1 + stage2, {len(fg)} calls): FETCH {fg.mean():10.1f}  WRITE {wg.mean():10.1f}
+#       expert bytes (algorithmic): {gemv_kib:10.1f} KiB (8 routed experts' rows, x, out, ids, weights)
+#   admit_fast_kernel:              FETCH {res['FETCH_SIZE']['admit_fast_kernel'].mean():10.1f}  WRITE {res['WRITE_SIZE']['admit_fast_kernel'].mean():10.1f}
+#
+# Traffic / algorithmic ratios (scaled FETCH + WRITE over algorithmic bytes) used by bench.py:
+kernel_sources_sha256_16 = {kernel_sources_hash()}
+fetch_scale = {fs:.4f}
+write_scale = {ws:.4f}
+# fetching stage1 launches: measured over all the bytes the launch must move
+gather_traffic_ratio = {miss_traffic / stage1_kib:.4f}
+# routed GEMV call (stage1 + stage2)
+routed_traffic_ratio = {gemv_traffic / gemv_kib:.4f}""")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,7 +430,17 @@ def main():
                     help="workgroups of the miss-gather kernel (0: the library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--launch-log", default=None,
+                    help="write the timed/instrumented launch layout and the result line here")
+    ap.add_argument("--trace-command", default="", help="recorded in the launch log")
+    ap.add_argument("--pmc-command", default="", help="recorded in the launch log")
+    ap.add_argument("--summarize-trace", default=None, metavar="KERNEL_TRACE_CSV")
+    ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.launch_log)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, args.launch_log)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode step is data-parallel and this build runs "
               f"on a single MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
@@ -268,16 +484,25 @@ def main():
     log(f"[bench] timed {K_} tokens in {dt:.3f}s, {fetched / K_:.1f} misses/token")
 
     # Same tokens again from the same cache state, with HIP events captured
-    # around each layer's kernels, and each layer's fetch count read after
-    # every token, so that layer-steps with misses (host-link bound) and
-    # all-hit layer-steps (HBM bound) are timed apart.
+    # around each layer's launches (event-record nodes of the graph), and
+    # each layer's fetch count read after every token, so that layer-steps
+    # with misses (host-link bound) and all-hit layer-steps (HBM bound) are
+    # told apart.  The nodes add their own processing to an interval (a few
+    # microseconds): an empty pair before each layer step measures it, and
+    # it is taken off; this pass times only the long launches, the ones
+    # that fetch.
     m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"])
     m.moe_cache_set_timing(lay.cache, True)
-    tgraph = capture(torch, lay, x_st, lg_st, out)
+    ids_l = torch.empty((L, 1, K), dtype=torch.int32, device="cuda")
+    w_l = torch.empty((L, 1, K), dtype=torch.float32, device="cuda")
+    pairs = ([torch.cuda.Event(enable_timing=True) for _ in range(L)],
+             [torch.cuda.Event(enable_timing=True) for _ in range(L)])
+    for e in pairs[0] + pairs[1]:
+        e.record()                              # creates the events before capture
+    torch.cuda.synchronize()
+    tgraph = capture(torch, lay, x_st, lg_st, out, ids_l, w_l, pairs)
     staged = args.overlap == 2
-    adm_ms = 0.0
-    miss_rows, miss_ms, miss_n = 0, 0.0, 0      # layer-steps that fetched
-    hit_ms, hit_n = 0.0, 0                      # layer-steps that fetched nothing
+    k1_ms, pair_ms, fetch_l = [], [], []
     prev = m.moe_cache_read_state(lay.cache)["stats"]
     for t in range(W_, n_tok):
         x_st.copy_(x_all[t])
@@ -288,29 +513,61 @@ def main():
         cur = m.moe_cache_read_state(lay.cache)["stats"]
         d = cur - prev
         prev = cur
-        fetched_l = d[:, m.MOE_STAT_MISSED] - d[:, m.MOE_STAT_OVERFLOW]
-        adm_ms += ms[:, 0].sum()
-        fl = fetched_l > 0
-        miss_rows += int(fetched_l.sum())
-        miss_ms += ms[fl, 1].sum()
-        miss_n += int(fl.sum())
-        hit_n += int((~fl).sum())
-        # staged schedule: both stages carry routed work; otherwise only
-        # the routed slot does (the gather launch is empty on a hit)
-        hit_ms += (ms[~fl, 1] + ms[~fl, 2]).sum() if staged else ms[~fl, 2].sum()
+        fetch_l.append(d[:, m.MOE_STAT_MISSED] - d[:, m.MOE_STAT_OVERFLOW])
+        k1_ms.append(ms[:, 1])
+        pair_ms.append([pairs[0][l].elapsed_time(pairs[1][l]) for l in range(L)])
     m.moe_cache_set_timing(lay.cache, False)
-    launches = K_ * L
-    adm_us = adm_ms / launches * 1000.0
-    gat_us = miss_ms / max(miss_n, 1) * 1000.0
-    gather_bytes = miss_rows * ROW_BYTES / max(miss_n, 1)
+    fetch_l = np.concatenate(fetch_l)
+    k1_raw = np.concatenate(k1_ms)
+    pair_us = float(np.mean(pair_ms)) * 1000.0
+    fl = fetch_l > 0
+    miss_n = int(fl.sum())
+    gat_raw_us = k1_raw[fl].mean() * 1000.0 if miss_n else 0.0
+    gat_us = gat_raw_us - pair_us
+    gather_bytes = fetch_l[fl].mean() * ROW_BYTES if miss_n else 0.0
     gather_gbs = gather_bytes / (gat_us * 1e-6) / 1e9 if miss_n else 0.0
-    rout_us = hit_ms / max(hit_n, 1) * 1000.0
-    experts = K + 1 if staged else K                   # the shared expert rides in the stages
-    gemv_bytes = experts * ROW_BYTES + 2 * H * 2 + (E * 4 + H * 4 if staged else H * 4)
-    gemv_gbs = gemv_bytes / (rout_us * 1e-6) / 1e9 if hit_n else 0.0
+
+    # The routed GEMV alone (moe_routed_decode: the same two stage launches
+    # without a miss plan or a shared expert) over the last token's slots,
+    # one call per layer, GEMV_PASSES passes over the 40 layers in one graph
+    # with an event-record node before and after them: the calls between
+    # the two nodes run back to back, and a call's 8 experts were last read
+    # 39 calls (2 GB) earlier, so they come from HBM, not from the 256 MB
+    # last-level cache.
+    pool = m.moe_cache_pool(lay.cache)
+    ws = torch.empty(m.moe_routed_workspace_bytes(0, H, F, 1, K), dtype=torch.uint8, device="cuda")
+    gout = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    xg = x_all[n_tok - 1].clone()
+    gstream = torch.cuda.Stream()
+    ggraph = torch.cuda.CUDAGraph()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(gstream)
+    g1.record(gstream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(ggraph, stream=gstream):
+        # a few milliseconds of spin first: the host enqueues the graph's
+        # nodes one by one, and the routed calls (~15 us each) are shorter
+        # than that, so without a head start it would feed them with gaps
+        torch.cuda._sleep(GEMV_HEAD_START_CYCLES)
+        m.moe_record_event(g0, gstream)
+        for _ in range(GEMV_PASSES):
+            for l in range(L):
+                m.moe_routed_decode(pool, xg[l], ids_l[l], w_l[l], gout[l], ws, stream=gstream)
+        m.moe_record_event(g1, gstream)
+    per_call = []
+    for r in range(1 + GEMV_REPLAYS):
+        ggraph.replay()
+        torch.cuda.synchronize()
+        if r > 0:
+            per_call.append(g0.elapsed_time(g1) * 1000.0 / (GEMV_PASSES * L))
+    rout_us = float(np.mean(per_call))
+    assert (ids_l >= 0).all(), "the GEMV phase reads resident slots only"
+    gemv_bytes = K * ROW_BYTES + 2 * H * 2 + K * 8     # 8 experts' rows, x and out, ids and weights
+    gemv_gbs = gemv_bytes / (rout_us * 1e-6) / 1e9
 
     # host-link ceiling: a pinned hipMemcpyAsync of the same size
-    nbytes = max(int(round(miss_rows / max(miss_n, 1))), 1) * ROW_BYTES
+    nbytes = max(int(round(gather_bytes)), ROW_BYTES)
     src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     for _ in range(2):
@@ -324,6 +581,24 @@ def main():
     torch.cuda.synchronize()
     h2d_gbs = 5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
+
+    # HBM ceiling at the routed step's size: a device-to-device copy that
+    # reads and writes half of the expert bytes each
+    half = gemv_bytes // 2
+    a = torch.empty(half, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    rot = [torch.empty(256 << 20, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    best = float("inf")
+    for i in range(12):
+        rot[i % 2].zero_()                         # evicts the previous copy from the caches
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            best = min(best, e0.elapsed_time(e1))
+    d2d_gbs = 2 * half / (best * 1e-3) / 1e9
+    del a, b, rot
 
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -341,6 +616,10 @@ def main():
 
     ratios = traffic_ratios()
     value = L * K_ / dt
+    workload = ("shared-expert decode: 40 layers x 256 experts, top-8 + gated shared expert, hidden "
+                "2048, expert FFN 512, bf16 weights in pinned host memory, 3164-slot cache, batch 1, "
+                "Zipf(1.05) routing with temporal locality; one step = one token = 40 layer-steps in "
+                "one hipGraph")
     line = {
         "metric": "decode MoE layer-steps/s; admission µs/layer; routed GEMV HBM GB/s vs peak",
         "value": round(value, 1),
@@ -354,10 +633,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "shared-expert decode: 40 layers x 256 experts, top-8 + gated shared "
-                               "expert, hidden 2048, expert FFN 512, bf16 weights in pinned host "
-                               "memory, 3164-slot cache, batch 1, Zipf(1.05) routing with temporal "
-                               "locality; one step = one token = 40 layer-steps in one hipGraph",
+        "config": {"workload": workload,
                    "layers": L, "experts": E, "top_k": K, "hidden": H, "ffn": F, "slots": S,
                    "batch": 1, "misses_per_token": round(fetched / K_, 2)},
         "roofline": {"kernel": ("stage1_kernel (miss gather + gate/up), layer-steps with misses" if staged
@@ -365,23 +641,33 @@ def main():
                      "bound": "host-link", "achieved": round(gather_gbs, 2),
                      "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gather_gbs / HOST_LINK_PEAK_GBS, 4),
-                     "traffic": round(gather_bytes * ratios["gather_traffic_ratio"]) if ratios else None,
+                     "traffic": (round(stage1_expected_bytes(fetch_l[fl]).mean() * ratios["gather_traffic_ratio"])
+                                 if ratios and miss_n else None),
+                     "traffic_expected": round(stage1_expected_bytes(fetch_l[fl]).mean()) if miss_n else None,
                      "bytes_per_launch": round(gather_bytes), "avg_launch_us": round(gat_us, 2),
-                     "launches": miss_n, "memcpy_h2d_same_size_gbs": round(h2d_gbs, 2)},
-        "roofline_gemv": {"kernel": ("stage1_kernel + stage2_kernel, all-hit layer-steps (8 routed + "
-                                     "shared expert)" if staged
-                                     else "routed experts (up_kernel + down_fused_kernel), all-hit layer-steps"),
+                     "launches": miss_n, "memcpy_h2d_same_size_gbs": round(h2d_gbs, 2),
+                     "avg_launch_us_events": round(gat_raw_us, 2), "empty_event_pair_us": round(pair_us, 2)},
+        "roofline_gemv": {"kernel": "stage1_kernel + stage2_kernel as moe_routed_decode: 8 resident routed "
+                                    "experts of one token (gate/up, then down + combine)",
                           "bound": "hbm",
                           "achieved": round(gemv_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                           "traffic": round(gemv_bytes * ratios["routed_traffic_ratio"]) if ratios else None,
                           "bytes_per_launch": gemv_bytes, "avg_launch_us": round(rout_us, 2),
-                          "launches": hit_n},
-        "admission_us_decode": round(adm_us, 2),
+                          "launches": GEMV_REPLAYS * GEMV_PASSES * L,
+                          "d2d_copy_same_bytes_gbs": round(d2d_gbs, 1)},
         "admission_us": adm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.launch_log:
+        with open(args.launch_log, "w") as f:
+            json.dump({"workload": workload, "layers": L, "warmup": W_, "steps": K_,
+                       "overlap": args.overlap, "fetched": fetch_l.astype(int).tolist(),
+                       "gemv_calls": (1 + GEMV_REPLAYS) * GEMV_PASSES * L,
+                       "gemv_timed_calls": GEMV_REPLAYS * GEMV_PASSES * L,
+                       "trace_command": args.trace_command, "pmc_command": args.pmc_command,
+                       "line": line}, f)
 
 
 if __name__ == "__main__":

@@ -91,6 +91,7 @@ def lib():
             "moe_cache_read_plan": (st, [P, P, P, i32, P]),
             "moe_cache_set_timing": (st, [P, i32]),
             "moe_cache_timing": (st, [P, P, P]),
+            "moe_record_event": (st, [P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -353,3 +354,12 @@ def moe_cache_timing(cache: Cache) -> np.ndarray:
     n = np.zeros(1, np.int32)
     _check(lib().moe_cache_timing(cache.handle, _np_ptr(ms), _np_ptr(n)))
     return ms.reshape(cache.L, 3)
+
+
+def moe_record_event(event, stream=None) -> None:
+    """Records a torch.cuda.Event (already created: recorded once) on the
+    stream; under graph capture it becomes an event-record node."""
+    handle = event.cuda_event
+    if not handle:
+        raise ValueError("record the event once before capture so that it exists")
+    _check(lib().moe_record_event(C.c_void_p(handle), _stream(stream)))

@@ -295,13 +295,14 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 // value, then id among the lanes holding that value), and only the lane
 // that held it looks for its next best.
 template <int NC>
-__device__ __forceinline__ void wave_topk_nc(const float *__restrict__ row, int E, int K,
-                                             int32_t *ids_lds, float *w_out) {
+__device__ __forceinline__ void wave_topk_nc(const float *__restrict__ row, const float *pre, int E,
+                                             int K, int32_t *ids_lds, float *w_out) {
     const int lane = threadIdx.x & (kWave - 1);
-    // all of the row's loads in flight together (clamped in-range indices)
+    // the row's logits, loaded by the caller (pre) or here, all loads in
+    // flight together (clamped in-range indices)
     float lv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) lv[c] = row[min(lane + kWave * c, E - 1)];
+    for (int c = 0; c < NC; ++c) lv[c] = pre ? pre[c] : row[min(lane + kWave * c, E - 1)];
     uint64_t keys[NC];
     uint64_t lb = 0ull;
 #pragma unroll
@@ -336,14 +337,14 @@ __device__ __forceinline__ void wave_topk_nc(const float *__restrict__ row, int 
     }
 }
 
-__device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int K,
+__device__ __forceinline__ void wave_topk(const float *__restrict__ row, const float *pre, int E, int K,
                                           int32_t *ids_lds, float *w_out) {
     const int nc = (E + kWave - 1) / kWave;
-    if (nc <= 1) wave_topk_nc<1>(row, E, K, ids_lds, w_out);
-    else if (nc <= 2) wave_topk_nc<2>(row, E, K, ids_lds, w_out);
-    else if (nc <= 4) wave_topk_nc<4>(row, E, K, ids_lds, w_out);
-    else if (nc <= 8) wave_topk_nc<8>(row, E, K, ids_lds, w_out);
-    else wave_topk_nc<16>(row, E, K, ids_lds, w_out);
+    if (nc <= 1) wave_topk_nc<1>(row, pre, E, K, ids_lds, w_out);
+    else if (nc <= 2) wave_topk_nc<2>(row, pre, E, K, ids_lds, w_out);
+    else if (nc <= 4) wave_topk_nc<4>(row, pre, E, K, ids_lds, w_out);
+    else if (nc <= 8) wave_topk_nc<8>(row, pre, E, K, ids_lds, w_out);
+    else wave_topk_nc<16>(row, pre, E, K, ids_lds, w_out);
 }
 
 // Register-resident admission.  p.order holds (slot, owner) pairs here, so
@@ -361,6 +362,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 }
 
 struct lds_view {
+    int64_t *freq_l;
     int32_t *cnt, *resl, *dlist, *missl, *pslot, *pold, *pexp, *ids_l;
     uint16_t *slot_e;
     uint8_t *touched, *filled;
@@ -376,7 +378,7 @@ struct lds_view {
 //   (slots used so far this step) + (misses) <= 2 * 64 + 64
 // entries of the order, inside the 256-entry window the wave holds.
 __device__ __forceinline__ void narrow_step(const AdmitParams &p, lds_view v, const int (&wslot)[4],
-                                         const int (&wown)[4], uint32_t now) {
+                                         const int (&wown)[4], uint32_t now, const int64_t (&st0)[5]) {
     const int lane = threadIdx.x;
     const int E = p.E, R = p.R;
     const int64_t lbase = (int64_t)p.layer * E;
@@ -496,17 +498,15 @@ __device__ __forceinline__ void narrow_step(const AdmitParams &p, lds_view v, co
             p.stamp[s] = now;
             v.slot_e[s] = (uint16_t)e;
         }
-        atomicAdd(reinterpret_cast<unsigned long long *>(&p.freq[lbase + e]),
-                  (unsigned long long)v.cnt[e]);
+        p.freq[lbase + e] = v.freq_l[e] + v.cnt[e];
     }
     if (lane == 0) {
-        unsigned long long *st =
-            reinterpret_cast<unsigned long long *>(p.stats + (int64_t)p.layer * MOE_NUM_STATS);
-        atomicAdd(&st[MOE_STAT_CALLS], 1ull);
-        atomicAdd(&st[MOE_STAT_MET], (unsigned long long)nD);
-        atomicAdd(&st[MOE_STAT_MISSED], (unsigned long long)nmissed);
-        atomicAdd(&st[MOE_STAT_OVERFLOW], (unsigned long long)noverflow);
-        atomicAdd(&st[MOE_STAT_INVALID], (unsigned long long)ninvalid);
+        int64_t *st = p.stats + (int64_t)p.layer * MOE_NUM_STATS;
+        st[MOE_STAT_CALLS] = st0[MOE_STAT_CALLS] + 1;
+        st[MOE_STAT_MET] = st0[MOE_STAT_MET] + nD;
+        st[MOE_STAT_MISSED] = st0[MOE_STAT_MISSED] + nmissed;
+        st[MOE_STAT_OVERFLOW] = st0[MOE_STAT_OVERFLOW] + noverflow;
+        st[MOE_STAT_INVALID] = st0[MOE_STAT_INVALID] + ninvalid;
         p.clock[0] = now;
         p.n_miss[0] = nplan;
         v.misc[1] = nD;
@@ -519,7 +519,8 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     const int E = p.E, S = p.S, R = p.R;
     int32_t *wsum = lds;            // [32]
     int32_t *misc = lds + 32;       // [16]: 0 invalid routes
-    int32_t *cnt = misc + 16;       // [E] routes per expert
+    int64_t *freq_l = reinterpret_cast<int64_t *>(misc + 16);  // [E] the layer's histogram row
+    int32_t *cnt = misc + 16 + 2 * E;  // [E] routes per expert
     int32_t *resl = cnt + E;        // [E] the layer's slot map row, kept current
     int32_t *dlist = resl + E;      // [E] distinct valid experts, ascending
     int32_t *missl = dlist + E;     // [E] misses of the current query
@@ -533,6 +534,27 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int64_t lbase = (int64_t)p.layer * E;
+
+    // Every load of the prologue is issued before any result is used: the
+    // first logits row of each wave (fused top-k), the LRU order, the slot
+    // map and histogram rows, the statistics and the clock.  This kernel is
+    // the only writer of the layer's statistics and histogram during the
+    // step, so they are updated with plain stores of the values read here.
+    float lgv[kTopkMaxPerLane];
+    const bool pre_row = p.logits != nullptr && wave < p.T;
+    if (pre_row) {
+        const float *row = p.logits + (int64_t)wave * E;
+        const int lane = tid & (kWave - 1);
+#pragma unroll
+        for (int c = 0; c < kTopkMaxPerLane; ++c)
+            if (c * kWave < E) lgv[c] = row[min(lane + kWave * c, E - 1)];
+    }
+    int64_t st0[5];
+    if (tid == 0) {
+        const int64_t *st = p.stats + (int64_t)p.layer * MOE_NUM_STATS;
+#pragma unroll
+        for (int k = 0; k < 5; ++k) st0[k] = st[k];
+    }
 
     // This thread's run of the LRU order: (slot, owner) pairs.  The order
     // buffer holds kThreads * P pairs (admit_order_bytes), so the loads are
@@ -577,13 +599,19 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     // (clamped in-range indices), stores after.
     for (int e0 = 0; e0 < E; e0 += 4 * kThreads) {
         int32_t v[4];
+        int64_t fv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = p.res[lbase + min(e0 + tid + j * kThreads, E - 1)];
+        for (int j = 0; j < 4; ++j) {
+            const int64_t e = lbase + min(e0 + tid + j * kThreads, E - 1);
+            v[j] = p.res[e];
+            fv[j] = p.freq[e];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = e0 + tid + j * kThreads;
             if (e < E) {
                 resl[e] = v[j];
+                freq_l[e] = fv[j];
                 cnt[e] = 0;
                 filled[e] = 0;
             }
@@ -595,7 +623,8 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
 
     if (p.logits != nullptr) {
         for (int t = wave; t < p.T; t += kWaves)
-            wave_topk(p.logits + (int64_t)t * E, E, p.K, ids_l + t * p.K, p.w_out + (int64_t)t * p.K);
+            wave_topk(p.logits + (int64_t)t * E, t == wave ? lgv : nullptr, E, p.K, ids_l + t * p.K,
+                      p.w_out + (int64_t)t * p.K);
     } else {
         for (int i = tid; i < R; i += kThreads) ids_l[i] = p.ids[i];
     }
@@ -603,9 +632,9 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
 
     int nD;
     if (narrow) {
-        if (wave == 0) narrow_step(p, lds_view{cnt, resl, dlist, missl, pslot, pold, pexp, ids_l, slot_e,
-                                                touched, filled, misc},
-                                   wslot, wown, now);
+        if (wave == 0) narrow_step(p, lds_view{freq_l, cnt, resl, dlist, missl, pslot, pold, pexp, ids_l,
+                                                slot_e, touched, filled, misc},
+                                   wslot, wown, now, st0);
         __syncthreads();
         nD = misc[1];
     } else {
@@ -741,17 +770,15 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
             p.stamp[s] = now;
             slot_e[s] = (uint16_t)e;
         }
-        atomicAdd(reinterpret_cast<unsigned long long *>(&p.freq[lbase + e]),
-                  (unsigned long long)cnt[e]);
+        p.freq[lbase + e] = freq_l[e] + cnt[e];
     }
     if (tid == 0) {
-        unsigned long long *st =
-            reinterpret_cast<unsigned long long *>(p.stats + (int64_t)p.layer * MOE_NUM_STATS);
-        atomicAdd(&st[MOE_STAT_CALLS], 1ull);
-        atomicAdd(&st[MOE_STAT_MET], (unsigned long long)nD);
-        atomicAdd(&st[MOE_STAT_MISSED], (unsigned long long)nmissed);
-        atomicAdd(&st[MOE_STAT_OVERFLOW], (unsigned long long)noverflow);
-        atomicAdd(&st[MOE_STAT_INVALID], (unsigned long long)misc[0]);
+        int64_t *st = p.stats + (int64_t)p.layer * MOE_NUM_STATS;
+        st[MOE_STAT_CALLS] = st0[MOE_STAT_CALLS] + 1;
+        st[MOE_STAT_MET] = st0[MOE_STAT_MET] + nD;
+        st[MOE_STAT_MISSED] = st0[MOE_STAT_MISSED] + nmissed;
+        st[MOE_STAT_OVERFLOW] = st0[MOE_STAT_OVERFLOW] + noverflow;
+        st[MOE_STAT_INVALID] = st0[MOE_STAT_INVALID] + misc[0];
         p.clock[0] = now;
         p.n_miss[0] = nplan;
     }
@@ -809,7 +836,7 @@ size_t admit_lds_bytes(int E, int S, int max_routes) {
     // the larger of the two kernels' layouts
     const size_t general = (32 + 8 + 5 * (size_t)E + (size_t)max_routes) * 4 + (size_t)S + (size_t)E;
     const size_t fast =
-        (32 + 16 + 8 * (size_t)E + (size_t)max_routes) * 4 + 3 * (size_t)S + (size_t)E;
+        (32 + 16 + 10 * (size_t)E + (size_t)max_routes) * 4 + 3 * (size_t)S + (size_t)E;
     return (std::max(general, fast) + 15) & ~(size_t)15;
 }
 

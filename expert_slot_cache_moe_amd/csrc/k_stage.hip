@@ -17,6 +17,10 @@
 // routed experts, fetched ones from their gate/up dots -- and the combine
 // in ascending k, then + the gated shared term, exactly as the serial path.
 //
+// Without a miss plan and a shared expert the same two launches are the
+// single-token routed GEMV over slot ids (resident routes' gate/up, then
+// down + combine + an optional fp32 addend).
+//
 // Bit-exactness with the serial path: resident routes and the shared expert
 // run the same device code; a fetched expert's gate/up dot products are
 // built from the same 8-element chunk partials combined by the same trees
@@ -59,6 +63,7 @@ struct Stage2Params {
     int has_shared;
     const uint16_t *hs;
     const float *gamma;
+    const float *addend;       // [H] fp32 added to the routed sum, or NULL
     uint16_t *out;
 };
 
@@ -168,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
     const int k = b / p.a_tiles;
     const int tile = b - k * p.a_tiles;
     const int s = p.idx[k];
-    const int plan = p.route_plan[k];
+    const int plan = p.route_plan ? p.route_plan[k] : -1;
     if ((s < 0) | (s >= p.slots.num_rows) | (plan >= 0)) return;
     up_rows<LPRH, NCHH>(p.slots, s, tile * JT + wave * (kWave / LPRH) + sub, li, p.x,
                         p.h + (int64_t)k * F);
@@ -219,7 +224,7 @@ __device__ __forceinline__ void stage2_batch(const Stage2Params &p, int k0, int 
     for (int q = 0; q < kDownBatch; ++q) {
         const int kk = min(k0 + q, p.K - 1);
         sl[q] = p.idx[kk];
-        pe[q] = p.route_plan[kk];
+        pe[q] = p.route_plan ? p.route_plan[kk] : -1;
     }
     __builtin_amdgcn_sched_barrier(0);
     WSeg<MOE_FMT_BF16, NCHF> w2[kDownBatch];
@@ -266,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
     for (int k0 = kDownBatch; k0 < p.K; k0 += kDownBatch)
         stage2_batch<LPRF, NCHF, false>(p, k0, ii, li, acc, vs);
     float res = acc;
+    if (p.addend) res = acc + p.addend[ii];
     if (p.has_shared) {
         // gamma * vs is rounded on its own (the library builds without fp
         // contraction), as the serial path rounds it when storing it
@@ -321,8 +327,8 @@ bool stage_supported(int fmt, int H, int F) {
 hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, const PoolView &slots,
                          const int32_t *idx, const float *w, const int32_t *route_plan, int K,
                          const uint16_t *x, uint16_t *h, const PoolView *shared, uint16_t *hs,
-                         const uint16_t *gate_vec, float *gamma, uint16_t *out, int which,
-                         hipStream_t s) {
+                         const uint16_t *gate_vec, float *gamma, const float *addend, uint16_t *out,
+                         int which, hipStream_t s) {
     using namespace stage_detail;
     Stage1Params a{};
     a.g = g;
@@ -360,6 +366,7 @@ hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, co
         b.shared = slots;
         b.hs = h;
     }
+    b.addend = addend;
     b.out = out;
     const int ch = slots.H / 8, cf = slots.F / 8;
 #define MOE_STAGE_CALL(CH, LH, NH, CF, LF, NF) \

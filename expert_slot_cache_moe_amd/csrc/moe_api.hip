@@ -214,6 +214,12 @@ hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t 
     const RoutedWs L = routed_ws(pv.H, pv.F, T, K);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     const int n = T * K;
+    if (T == 1 && stage_supported(pv.fmt, pv.H, pv.F)) {
+        // the decode schedule's two stage launches, with no gather and no
+        // shared expert (identical arithmetic to the kernels below)
+        return launch_stages(GatherParams{}, 0, nullptr, pv, idx, w, nullptr, K, x, h, nullptr, nullptr,
+                             nullptr, nullptr, addend, out, 3, s);
+    }
     if (T == 1) {
         Items it{};
         it.mode = ITEM_ROUTE;
@@ -756,7 +762,7 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
                                   shared ? &spv : nullptr, hs,
                                   shared ? static_cast<const uint16_t *>(shared->gate_dev)
                                          : nullptr,
-                                  gamma, static_cast<uint16_t *>(out), which, s),
+                                  gamma, nullptr, static_cast<uint16_t *>(out), which, s),
                     "stage launch");
             if (timing) HIP_TRY(record_timing(tev[2 * which + 1], s), "timing");
         }
@@ -895,6 +901,13 @@ moe_status_t moe_cache_read_plan(moe_cache_t *c, int32_t *ps, int32_t *pe, int32
         HIP_TRY(hipMemcpy(ps, c->plan_slot, (size_t)k * 4, hipMemcpyDeviceToHost), "copy plan");
         HIP_TRY(hipMemcpy(pe, c->plan_expert, (size_t)k * 4, hipMemcpyDeviceToHost), "copy plan");
     }
+    return MOE_OK;
+}
+
+moe_status_t moe_record_event(void *event, void *stream) {
+    if (!event) return fail(MOE_INVALID_ARG, "NULL event");
+    HIP_TRY(record_timing(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream)),
+            "event record");
     return MOE_OK;
 }
 

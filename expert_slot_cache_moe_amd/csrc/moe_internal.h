@@ -259,8 +259,10 @@ bool stage_supported(int fmt, int H, int F);
 hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, const PoolView &slots,
                          const int32_t *idx, const float *w, const int32_t *route_plan, int K,
                          const uint16_t *x, uint16_t *h, const PoolView *shared, uint16_t *hs,
-                         const uint16_t *gate_vec, float *gamma, uint16_t *out, int which,
-                         hipStream_t s);   // which: 1 stage 1, 2 stage 2, 3 both
+                         const uint16_t *gate_vec, float *gamma, const float *addend, uint16_t *out,
+                         int which, hipStream_t s);   // which: 1 stage 1, 2 stage 2, 3 both
+// (route_plan NULL: no route was fetched in this step; gather_blocks 0: no
+// gather; shared NULL: no shared expert; addend NULL: nothing added)
 
 // Shape support of the expert kernels for one matrix width.
 bool expert_shape_supported(int fmt, int H, int F);

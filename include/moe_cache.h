@@ -309,6 +309,14 @@ moe_status_t moe_cache_read_plan(moe_cache_t *cache, int32_t *plan_slot_host,
 moe_status_t moe_cache_set_timing(moe_cache_t *cache, int32_t enable);
 moe_status_t moe_cache_timing(moe_cache_t *cache, float *ms_host, int32_t *layers_read);
 
+/* Records the HIP event `event` (a hipEvent_t, created by the caller) on
+ * `stream`.  While the stream is being captured into a graph the record
+ * becomes an event-record node of that graph, so every replay records it
+ * again (a plain hipEventRecord under capture would not be replayed);
+ * otherwise it is hipEventRecord.  A measurement aid: events around a
+ * sequence of launches inside one graph time them with nothing between. */
+moe_status_t moe_record_event(void *event, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -317,11 +317,12 @@ def test_graph_replay_matches_eager_over_changing_routes(overlap):
         eager_l.close()
 
 
-def test_kernel_timing_events_eager_and_captured():
+@pytest.mark.parametrize("overlap", [1, 2])
+def test_kernel_timing_events_eager_and_captured(overlap):
     """The optional timing events work in eager mode and as event-record
     nodes of a captured graph."""
     L = 2
-    lay, _, _ = _tiny_layers(1, True, seed=5, L=L, E=16, S=10)
+    lay, _, _ = _tiny_layers(overlap, True, seed=5, L=L, E=16, S=10)
     try:
         m.moe_cache_set_timing(lay.cache, True)
         g = W.rng(5, "timing")
@@ -345,6 +346,34 @@ def test_kernel_timing_events_eager_and_captured():
         m.moe_cache_set_timing(lay.cache, False)
     finally:
         lay.close()
+
+
+def test_timed_staged_steps_match_untimed_ones():
+    """Timing the staged schedule eagerly (events attached to the launches)
+    changes neither the output bytes nor the cache state, misses included."""
+    L, E, S, H = 2, 32, 6, 64
+    lays = [_tiny_layers(2, True, seed=21, L=L, E=E, S=S)[0] for _ in range(2)]
+    g = W.rng(21, "timing-eager")
+    outs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in lays]
+    try:
+        m.moe_cache_set_timing(lays[1].cache, True)
+        for t in range(12):
+            for l in range(L):
+                x = _dev_u16(W.normal_bf16(g, (1, H)))
+                lg = torch.from_numpy(W.zipf_logits(g, 1, E, 0.5)).cuda()
+                for lay, o in zip(lays, outs):
+                    lay.decode(l, x, lg, 2, o)
+                torch.cuda.synchronize()
+                assert torch.equal(outs[0], outs[1]), (t, l)
+            ms = m.moe_cache_timing(lays[1].cache)
+            assert (ms > 0).all() and (ms < 1000).all()
+        a, b = (m.moe_cache_read_state(lay.cache) for lay in lays)
+        for k in ("res", "own", "stamp", "stats", "freq"):
+            np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+        assert m.moe_cache_stats(lays[0].cache)[2] > 10      # the trace does miss
+    finally:
+        for lay in lays:
+            lay.close()
 
 
 def test_all_schedules_are_bit_identical():
