@@ -140,6 +140,78 @@ def capture(torch, lay, x_st, lg_st, out, ids=None, w=None, pairs=None):
     return graph
 
 
+# Wide steps (their routed GEMV alone, moe_routed_decode over a pool):
+# (name, format, H, F, token rows, top-k, experts, pool copies rotated over)
+WIDE = (
+    ("wide decode bf16: 150 rows x top-2 over 160 experts, H 1024, F 256", 0, 1024, 256, 150, 2, 160, 8),
+    ("wide decode e2m1 (E4M3 per-16 scales): 600 rows x top-2 over 160 experts, H 1024, F 256",
+     1, 1024, 256, 600, 2, 160, 8),
+    ("prefill chunk bf16: 42 rows x top-6 over 256 experts, H 4096, F 1024", 0, 4096, 1024, 42, 6, 256, 1),
+    ("prefill chunk bf16: 50 rows x top-6 over 640 experts, H 4096, F 1024", 0, 4096, 1024, 50, 6, 640, 1),
+)
+WIDE_SETS = 8            # routing sets per graph (one call each)
+WIDE_REPLAYS = 3         # timed replays (after one untimed)
+
+
+def wide_gemv_benchmark(torch, m, seed=0):
+    """Routed GEMV of the wide-step shapes: one graph per shape holding a
+    head-start spin, an event node, WIDE_SETS calls over different routings
+    (each over its own copy of the pool where the shape allows, so that no
+    call finds its rows in the last-level cache) and an event node."""
+    res = []
+    for name, fmt, Hw, Fw, T, Kw, Ew, copies in WIDE:
+        rb = m.moe_bank_row_bytes(fmt, Hw, Fw)
+        rows = Ew * copies
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+        if fmt == 0:
+            banks = [torch.randn((rows, r // 2), device="cuda", generator=gen).mul_(0.02)
+                     .to(torch.bfloat16).view(torch.uint8) for r in rb]
+        else:
+            banks = [torch.randint(0, 256, (rows, r), dtype=torch.uint8, device="cuda", generator=gen)
+                     for r in rb]
+            for b in (1, 4):
+                banks[b].fill_(0x30)                       # E4M3 scale 0.125
+            for b in (2, 5):
+                banks[b].view(torch.float32).fill_(1.0)    # global scales
+        pool = m.make_pool(fmt, Hw, Fw, rows, banks)
+        g = np.random.default_rng(seed)
+        sets = [np.stack([g.choice(Ew, Kw, replace=False) for _ in range(T)]) + (i % copies) * Ew
+                for i in range(WIDE_SETS)]
+        distinct = float(np.mean([len(np.unique(x)) for x in sets]))
+        idx = [torch.from_numpy(x.astype(np.int32)).cuda() for x in sets]
+        x = torch.randn((T, Hw), device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
+        w = torch.rand((T, Kw), device="cuda", generator=gen)
+        out = torch.empty((T, Hw), dtype=torch.int16, device="cuda")
+        ws = torch.empty(m.moe_routed_workspace_bytes(fmt, Hw, Fw, T, Kw), dtype=torch.uint8, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        st = torch.cuda.Stream()
+        for e in ev:
+            e.record(st)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=st):
+            torch.cuda._sleep(GEMV_HEAD_START_CYCLES)
+            m.moe_record_event(ev[0], st)
+            for i in range(WIDE_SETS):
+                m.moe_routed_decode(pool, x, idx[i], w, out, ws, stream=st)
+            m.moe_record_event(ev[1], st)
+        per = []
+        for r in range(1 + WIDE_REPLAYS):
+            graph.replay()
+            torch.cuda.synchronize()
+            if r:
+                per.append(ev[0].elapsed_time(ev[1]) * 1000.0 / WIDE_SETS)
+        us = float(np.mean(per))
+        nbytes = distinct * sum(rb) + 2 * T * Hw * 2 + T * Kw * 8
+        res.append({"workload": name, "us_per_call": round(us, 2), "distinct_experts": round(distinct, 1),
+                    "bytes_per_call": round(nbytes), "achieved_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+        del banks, pool, ws, graph
+        torch.cuda.empty_cache()
+    return res
+
+
 def admission_benchmark(torch, m, W, replays=40, layers=48):
     res = {}
     caches = [m.moe_cache_create(num_layers=1, num_experts=512, num_slots=2100, max_routes=1280)
@@ -228,7 +300,8 @@ def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
 
 
 DECODE_KERNELS = ("admit_fast_kernel", "admit_kernel", "topk_kernel", "stage1_kernel", "stage2_kernel",
-                  "gather_kernel", "up_kernel", "down_d_kernel", "down_fused_kernel")
+                  "gather_kernel", "up_kernel", "down_d_kernel", "down_fused_kernel",
+                  "group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "combine_kernel")
 
 
 def _short(name: str) -> str:
@@ -276,6 +349,23 @@ def _split(log, moe):
                                               for c in calls):
         raise SystemExit("trace does not hold the routed-GEMV launches the run made")
     return steps[W_ * L:(W_ + K_) * L], steps[(W_ + K_) * L:], calls
+
+
+def _wide_calls(log, moe):
+    """Per wide shape, its timed calls' dispatches (grouping, gate/up, down,
+    combine), following the decode and routed-GEMV phases."""
+    L, W_, K_ = log["layers"], log["warmup"], log["steps"]
+    pos = 3 * (W_ + 2 * K_) * L + 2 * log["gemv_calls"]
+    out = []
+    kinds = ["group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "combine_kernel"]
+    for wcfg in log.get("wide") or []:
+        seq = moe[pos:pos + 4 * wcfg["calls"]]
+        pos += 4 * wcfg["calls"]
+        calls = [seq[i:i + 4] for i in range(0, len(seq), 4)]
+        if len(calls) != wcfg["calls"] or any([d["k"] for d in c] != kinds for c in calls):
+            raise SystemExit("trace does not hold the wide-step launches the run made")
+        out.append((wcfg["workload"], calls[-wcfg["timed_calls"]:]))
+    return out
 
 
 def stage1_expected_bytes(fetched):
@@ -335,6 +425,12 @@ def summarize_trace(csv_path, log_path):
       f"{len(gc)} | {gc.mean():.2f} | {rg.get('avg_launch_us')} |")
     p(f"| decode kernels per timed token (ms) | {len(tok)} | {tok.mean() / 1000:.4f} | "
       f"{line.get('ms_per_step')} (ms_per_step) |")
+    wl = {r["workload"]: r for r in (line.get("routed_gemv_wide") or [])}
+    for name, wc in _wide_calls(log, [d for d in disp if d["k"]]):
+        tot = np.asarray([sum(d["us"] for d in c) for c in wc])
+        parts = " + ".join(f"{np.mean([c[i]['us'] for c in wc]):.2f}" for i in range(4))
+        p(f"| routed GEMV, {name}: group_count + up_mfma + down_mfma + combine ({parts}) | {len(wc)} | "
+          f"{tot.mean():.2f} | {wl.get(name, {}).get('us_per_call')} |")
     p("")
     p("The roofline interval is read between event-record nodes captured around the launch in the "
       f"graph ({rl.get('avg_launch_us_events')} µs); the nodes add their own processing to it, "
@@ -422,6 +518,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-admission", action="store_true")
+    ap.add_argument("--no-wide", action="store_true", help="skip the wide-step routed GEMV shapes")
     ap.add_argument("--cpu-sample-tokens", type=int, default=6)
     ap.add_argument("--overlap", type=int, default=2,
                     help="layer-step schedule passed to the cache (0 serial, 1 side-stream "
@@ -607,6 +704,7 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    wide = None if args.no_wide else wide_gemv_benchmark(torch, m)
     adm = None if args.no_admission else admission_benchmark(torch, m, W)
     lay.close()
     del lay
@@ -657,6 +755,7 @@ def main():
                           "launches": GEMV_REPLAYS * GEMV_PASSES * L,
                           "d2d_copy_same_bytes_gbs": round(d2d_gbs, 1)},
         "admission_us": adm,
+        "routed_gemv_wide": wide,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -666,6 +765,9 @@ def main():
                        "overlap": args.overlap, "fetched": fetch_l.astype(int).tolist(),
                        "gemv_calls": (1 + GEMV_REPLAYS) * GEMV_PASSES * L,
                        "gemv_timed_calls": GEMV_REPLAYS * GEMV_PASSES * L,
+                       "wide": None if wide is None else [
+                           {"workload": r["workload"], "calls": (1 + WIDE_REPLAYS) * WIDE_SETS,
+                            "timed_calls": WIDE_REPLAYS * WIDE_SETS} for r in wide],
                        "trace_command": args.trace_command, "pmc_command": args.pmc_command,
                        "line": line}, f)
 
