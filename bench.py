@@ -465,13 +465,15 @@ def summarize_pmc(fetch_csv, write_csv, log_path):
     for cname, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         disp = _read_dispatches(path, cname)
         copies = [d for d in disp if "copyBuffer" in d["name"]]
-        copy[cname] = copies[-1]["v"]            # the 256 MiB device copy ends the run
+        copy[cname] = max(d["v"] for d in copies)    # the 256 MiB device copy is the run's largest
         _, inst, calls = _split(log, [d for d in disp if d["k"]])
         res[cname] = {"stage1_kernel": np.asarray([st[1]["v"] for st in inst]),
                       "admit_fast_kernel": np.asarray([st[0]["v"] for st in inst]),
                       "gemv": np.asarray([c[0]["v"] + c[1]["v"] for c in calls])[-log["gemv_timed_calls"]:]}
     mib = 262144.0                                  # KiB moved each way by the calibration copy
     fs, ws = mib / copy["FETCH_SIZE"], mib / copy["WRITE_SIZE"]
+    if not (0.5 <= fs <= 4.0 and 0.5 <= ws <= 4.0):
+        raise SystemExit(f"calibration copy not found (scales {fs:.3g}, {ws:.3g})")
     miss = fetched > 0
     f1, w1 = res["FETCH_SIZE"]["stage1_kernel"], res["WRITE_SIZE"]["stage1_kernel"]
     fg, wg = res["FETCH_SIZE"]["gemv"], res["WRITE_SIZE"]["gemv"]
@@ -487,7 +489,7 @@ def summarize_pmc(fetch_csv, write_csv, log_path):
 #   {log['pmc_command'].replace('<C>', 'WRITE_SIZE')}
 # Summarised by: python3 bench.py --summarize-pmc <FETCH csv> <WRITE csv> --launch-log <log>
 #
-# Calibration: the run ends with a 256 MiB device-to-device copy
+# Calibration: the run makes one 256 MiB device-to-device copy, its largest
 # (262144 KiB read and 262144 KiB written); its counters read
 # FETCH_SIZE = {copy['FETCH_SIZE']:.1f} KiB and WRITE_SIZE = {copy['WRITE_SIZE']:.1f} KiB, so
 # fetch_scale = {fs:.3f} and write_scale = {ws:.3f}.
