@@ -22,6 +22,8 @@
 // PR #491 section 5) are expanded to bf16 in registers: the product of an
 // E2M1 value and an E4M3 scale has at most six significant bits, so it is
 // exact in bf16, and the MFMA sees exactly the dequantized weights.
+#include <algorithm>
+
 #include "k_expert.inc"
 
 namespace moe {
@@ -37,7 +39,6 @@ constexpr int kTile = 16;                       // rows and tokens of one MFMA t
 constexpr int kSlab = 128;                      // contraction elements per sweep step
 constexpr int kMWaves = 4;
 constexpr int kMThreads = kMWaves * kWave;
-constexpr int kTT = 2;                          // token tiles per pass over the weights
 constexpr int kRowsPerBlock = kMWaves * kTile;  // output rows of one workgroup
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
@@ -110,21 +111,6 @@ __device__ __forceinline__ float matrix_glob(const PoolView &p, int64_t prow, in
     }
 }
 
-// Group g of the step: its pool row, route count and route list, read with
-// three independent loads (slots past the last group hold row -1).
-__device__ __forceinline__ bool group_of(const Items &items, int g, int num_rows, ItemRef &r) {
-    const int row = items.grp_row[g];
-    const int count = items.grp_count[g];
-    const int start = items.grp_start[g];
-    r.row = row;
-    r.count = count;
-    r.first = 0;
-    r.list = items.grp_routes + start;
-    r.K = items.K;
-    // one branch on all three values, so the three loads issue together
-    return !((row < 0) | (row >= num_rows) | (count <= 0) | (start < 0));
-}
-
 // 32 bf16 activations of one token row for one slab.
 __device__ __forceinline__ void load_b(const uint16_t *row, int e0, u32x4 (&b)[4]) {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(row + e0);
@@ -132,96 +118,107 @@ __device__ __forceinline__ void load_b(const uint16_t *row, int e0, u32x4 (&b)[4
     for (int i = 0; i < 4; ++i) b[i] = src[i];
 }
 
-// Slabs whose loads are issued together before any of them is used: deep
-// enough that a wave keeps 8-16 KB in flight, shallow enough for the
-// register file (4-bit rows are a quarter of the bytes of bf16 rows).
-template <int FMT> struct Depth { static constexpr int v = FMT == MOE_FMT_BF16 ? 2 : 4; };
+// Slabs a wave keeps in flight: a bf16 slab carries 8 KB of a wave's gate
+// and up rows, a 4-bit one 2.3 KB, so 4-bit waves run four slabs ahead and
+// bf16 waves two.  Slab s lives in buffer s % NB; once it is consumed, the
+// buffer is refilled with slab s + NB, so loads stay in flight while the
+// matrix cores work.
+template <int FMT> struct Ahead { static constexpr int v = FMT == MOE_FMT_BF16 ? 2 : 4; };
 
-// gate/up + SwiGLU for one group and 64 rows j per workgroup:
-// h[route][j] = bf16(silu(g) * u) for every route of the group.  The first
-// weights are requested as soon as the group's row is known, before the
-// route list and token rows (two more dependent loads) are read.
+// The group table entry gi (row -1 past the last group).
+struct GroupEntry {
+    int row = -1, count = 0, start = -1;
+    __device__ __forceinline__ void load(const Items &items, int gi, int gmax) {
+        if (gi < gmax) {
+            row = items.grp_row[gi];
+            count = items.grp_count[gi];
+            start = items.grp_start[gi];
+        } else {
+            row = -1;
+        }
+    }
+    __device__ __forceinline__ bool valid(int num_rows) const {
+        return (row >= 0) & (row < num_rows) & (count > 0) & (start >= 0);
+    }
+};
+
+// gate/up + SwiGLU, 64 rows j per workgroup, for the groups blockIdx.y,
+// blockIdx.y + gridDim.y, ...: h[route][j] = bf16(silu(g) * u) for every
+// route of a group.  The grid holds about as many workgroups as the device
+// keeps resident; the group table is a prefix of valid groups followed by
+// row -1, so the first invalid entry ends the loop.  The next group's
+// table entry is read while the current one is computed; a group's weights
+// are requested before its route list and token rows (two dependent
+// loads) are read.  Tokens go through the matrix cores 16 at a time; a
+// group of more than 16 routes streams its rows once per 16.
 template <int FMT>
 __global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, Items items,
                                                                const uint16_t *__restrict__ x,
                                                                uint16_t *__restrict__ h) {
-    constexpr int D = Depth<FMT>::v;
-    ItemRef it;
-    if (!group_of(items, blockIdx.y, pool.num_rows, it)) return;
-    const int H = pool.H, F = pool.F;
+    constexpr int NB = Ahead<FMT>::v;
+    const int H = pool.H, F = pool.F, K = items.K;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int c = lane & (kTile - 1), q = lane / kTile;
     const int j0 = blockIdx.x * kRowsPerBlock + wave * kTile;
     if (j0 >= F) return;
-
-    // the weights of D slabs at once (slabs past H repeat the last one, in range)
-    ASlab<FMT> wg[D], wu[D];
-    auto load_chunk = [&](int k0) {
+    const int gmax = min(items.n, pool.num_rows);
+    const int nslab = H / kSlab;
+    GroupEntry cur;
+    cur.load(items, blockIdx.y, gmax);
+    for (int gi = blockIdx.y; gi < gmax && cur.valid(pool.num_rows); gi += gridDim.y) {
+        GroupEntry nxt;
+        nxt.load(items, gi + gridDim.y, gmax);
+        const int64_t row = cur.row;
+        const int32_t *list = items.grp_routes + cur.start;
+        for (int base = 0; base < cur.count; base += kTile) {
+            ASlab<FMT> wg[NB], wu[NB];
+            u32x4 xb[NB][4];
+            auto load_w = [&](int s, int bfr) {
+                const int e0 = s * kSlab + 32 * q;
+                wg[bfr].load(pool, row, 0, j0 + c, e0);
+                wu[bfr].load(pool, row, 0, F + j0 + c, e0);
+            };
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int e0 = min(k0 + d * kSlab, H - kSlab) + 32 * q;
-            wg[d].load(pool, it.row, 0, j0 + c, e0);
-            wu[d].load(pool, it.row, 0, F + j0 + c, e0);
-        }
-    };
-    load_chunk(0);
-    const float glob = matrix_glob<FMT>(pool, it.row, 0);
-
-    for (int base = 0; base < it.count; base += kTile * kTT) {
-        if (base > 0) load_chunk(0);
-        const int ntile = min(kTT, (it.count - base + kTile - 1) / kTile);
-        const uint16_t *xr[kTT];
+            for (int bfr = 0; bfr < NB; ++bfr)
+                if (bfr < nslab) load_w(bfr, bfr);
+            const float glob = matrix_glob<FMT>(pool, row, 0);
+            const int n = min(base + c, cur.count - 1);
+            const uint16_t *xr = x + (int64_t)(list[n] / K) * H;
 #pragma unroll
-        for (int t = 0; t < kTT; ++t) {
-            const int n = min(base + t * kTile + c, it.count - 1);
-            xr[t] = x + (int64_t)it.token(n) * H;
-        }
-        f32x4 ag[kTT], au[kTT];
+            for (int bfr = 0; bfr < NB; ++bfr)
+                if (bfr < nslab) load_b(xr, bfr * kSlab + 32 * q, xb[bfr]);
+            f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
+            for (int s0 = 0; s0 < nslab; s0 += NB) {
 #pragma unroll
-        for (int t = 0; t < kTT; ++t) ag[t] = au[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < H; k0 += D * kSlab) {
-            if (k0 > 0) load_chunk(k0);
-            // the activations one slab ahead of their use
-            u32x4 xb[2][kTT][4];
-#pragma unroll
-            for (int t = 0; t < kTT; ++t)
-                if (t < ntile) load_b(xr[t], k0 + 32 * q, xb[0][t]);
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                if (k0 + d * kSlab >= H) break;
-                if (d + 1 < D && k0 + (d + 1) * kSlab < H) {
-#pragma unroll
-                    for (int t = 0; t < kTT; ++t)
-                        if (t < ntile) load_b(xr[t], k0 + (d + 1) * kSlab + 32 * q, xb[(d + 1) & 1][t]);
-                }
-                u32x4 ga[4], ua[4];
-                wg[d].expand(ga);
-                wu[d].expand(ua);
-#pragma unroll
-                for (int t = 0; t < kTT; ++t) {
-                    if (t < ntile) {
+                for (int bfr = 0; bfr < NB; ++bfr) {
+                    const int s = s0 + bfr;
+                    if (s < nslab) {
+                        u32x4 ga[4], ua[4];
+                        wg[bfr].expand(ga);
+                        wu[bfr].expand(ua);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            ag[t] = mfma(ga[i], xb[d & 1][t][i], ag[t]);
-                            au[t] = mfma(ua[i], xb[d & 1][t][i], au[t]);
+                            ag = mfma(ga[i], xb[bfr][i], ag);
+                            au = mfma(ua[i], xb[bfr][i], au);
+                        }
+                        if (s + NB < nslab) {
+                            load_w(s + NB, bfr);
+                            load_b(xr, (s + NB) * kSlab + 32 * q, xb[bfr]);
                         }
                     }
                 }
             }
-        }
-        // lane holds rows j0 + 4q + i (i < 4) of token column c
-#pragma unroll
-        for (int t = 0; t < kTT; ++t) {
-            const int n = base + t * kTile + c;
-            if (t < ntile && n < it.count) {
-                const int64_t r = it.route(n);
+            // lane holds rows j0 + 4q + i (i < 4) of token column c
+            if (base + c < cur.count) {
+                const int64_t r = list[base + c];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float g = ag[t][i] * glob, u = au[t][i] * glob;
+                    const float g = ag[i] * glob, u = au[i] * glob;
                     h[r * F + j0 + 4 * q + i] = f32_to_bf16(silu_mul(g, u));
                 }
             }
         }
+        cur = nxt;
     }
 }
 
@@ -233,94 +230,86 @@ template <int FMT> struct DownTiles { static constexpr int v = FMT == MOE_FMT_BF
 template <int FMT>
 constexpr int down_rows_per_block() { return kMWaves * kTile * DownTiles<FMT>::v; }
 
-// down projection for one group and 16 * RT rows i per wave:
-// d[route][i] = (W2 h[route])_i, fp32.
+// down projection, 16 * RT rows i per wave, for the groups blockIdx.y,
+// blockIdx.y + gridDim.y, ... (as in up_mfma_kernel):
+// d[route][i] = (W2 h[route])_i, fp32.  Two slabs in flight.
 template <int FMT>
 __global__ __launch_bounds__(kMThreads, 2) void down_mfma_kernel(PoolView pool, Items items,
                                                               const uint16_t *__restrict__ h,
                                                               float *__restrict__ d) {
-    constexpr int D = 2;
+    constexpr int NB = 2;
     constexpr int RT = DownTiles<FMT>::v;
-    ItemRef it;
-    if (!group_of(items, blockIdx.y, pool.num_rows, it)) return;
     const int H = pool.H, F = pool.F;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int c = lane & (kTile - 1), q = lane / kTile;
     const int i0 = (blockIdx.x * kMWaves + wave) * RT * kTile;
     if (i0 >= H) return;
-    ASlab<FMT> w2[D][RT];
-    auto load_chunk = [&](int k0) {
+    const int gmax = min(items.n, pool.num_rows);
+    const int nslab = F / kSlab;
+    GroupEntry cur;
+    cur.load(items, blockIdx.y, gmax);
+    for (int gi = blockIdx.y; gi < gmax && cur.valid(pool.num_rows); gi += gridDim.y) {
+        GroupEntry nxt;
+        nxt.load(items, gi + gridDim.y, gmax);
+        const int64_t row = cur.row;
+        const int32_t *list = items.grp_routes + cur.start;
+        for (int base = 0; base < cur.count; base += kTile) {
+            ASlab<FMT> w2[NB][RT];
+            u32x4 hb[NB][4];
+            auto load_w = [&](int s, int bfr) {
+                const int e0 = s * kSlab + 32 * q;
 #pragma unroll
-        for (int dd = 0; dd < D; ++dd) {
-            const int e0 = min(k0 + dd * kSlab, F - kSlab) + 32 * q;
+                for (int rt = 0; rt < RT; ++rt)
+                    w2[bfr][rt].load(pool, row, 1, min(i0 + rt * kTile, H - kTile) + c, e0);
+            };
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                w2[dd][rt].load(pool, it.row, 1, min(i0 + rt * kTile, H - kTile) + c, e0);
-        }
-    };
-    load_chunk(0);
-    const float glob = matrix_glob<FMT>(pool, it.row, 1);
-
-    for (int base = 0; base < it.count; base += kTile * kTT) {
-        if (base > 0) load_chunk(0);
-        const int ntile = min(kTT, (it.count - base + kTile - 1) / kTile);
-        const uint16_t *hr[kTT];
+            for (int bfr = 0; bfr < NB; ++bfr)
+                if (bfr < nslab) load_w(bfr, bfr);
+            const float glob = matrix_glob<FMT>(pool, row, 1);
+            const int n = min(base + c, cur.count - 1);
+            const uint16_t *hr = h + (int64_t)list[n] * F;
 #pragma unroll
-        for (int t = 0; t < kTT; ++t) {
-            const int n = min(base + t * kTile + c, it.count - 1);
-            hr[t] = h + (int64_t)it.route(n) * F;
-        }
-        f32x4 acc[RT][kTT];
+            for (int bfr = 0; bfr < NB; ++bfr)
+                if (bfr < nslab) load_b(hr, bfr * kSlab + 32 * q, hb[bfr]);
+            f32x4 acc[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+            for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < nslab; s0 += NB) {
 #pragma unroll
-            for (int t = 0; t < kTT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < F; k0 += D * kSlab) {
-            if (k0 > 0) load_chunk(k0);
-            u32x4 hb[D][kTT][4];
+                for (int bfr = 0; bfr < NB; ++bfr) {
+                    const int s = s0 + bfr;
+                    if (s < nslab) {
 #pragma unroll
-            for (int dd = 0; dd < D; ++dd) {
-                const int e0 = min(k0 + dd * kSlab, F - kSlab) + 32 * q;
+                        for (int rt = 0; rt < RT; ++rt) {
+                            u32x4 wa[4];
+                            w2[bfr][rt].expand(wa);
 #pragma unroll
-                for (int t = 0; t < kTT; ++t)
-                    if (t < ntile) load_b(hr[t], e0, hb[dd][t]);
-            }
-#pragma unroll
-            for (int dd = 0; dd < D; ++dd) {
-                if (k0 + dd * kSlab >= F) break;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    u32x4 wa[4];
-                    w2[dd][rt].expand(wa);
-#pragma unroll
-                    for (int t = 0; t < kTT; ++t) {
-                        if (t < ntile) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) acc[rt][t] = mfma(wa[i], hb[dd][t][i], acc[rt][t]);
+                            for (int i = 0; i < 4; ++i) acc[rt] = mfma(wa[i], hb[bfr][i], acc[rt]);
+                        }
+                        if (s + NB < nslab) {
+                            load_w(s + NB, bfr);
+                            load_b(hr, (s + NB) * kSlab + 32 * q, hb[bfr]);
                         }
                     }
                 }
             }
-        }
-#pragma unroll
-        for (int t = 0; t < kTT; ++t) {
-            const int n = base + t * kTile + c;
-            if (t < ntile && n < it.count) {
-                const int64_t r = it.route(n);
+            if (base + c < cur.count) {
+                const int64_t r = list[base + c];
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const int ib = i0 + rt * kTile;
                     if (ib < H) {
                         float4 v;
-                        v.x = acc[rt][t][0] * glob;
-                        v.y = acc[rt][t][1] * glob;
-                        v.z = acc[rt][t][2] * glob;
-                        v.w = acc[rt][t][3] * glob;
+                        v.x = acc[rt][0] * glob;
+                        v.y = acc[rt][1] * glob;
+                        v.z = acc[rt][2] * glob;
+                        v.w = acc[rt][3] * glob;
                         *reinterpret_cast<float4 *>(d + r * H + ib + 4 * q) = v;
                     }
                 }
             }
         }
+        cur = nxt;
     }
 }
 
@@ -419,15 +408,45 @@ bool group_mfma_supported(int fmt, int H, int F) {
            F % mfma_detail::kSlab == 0;
 }
 
+namespace {
+// Workgroups of `kern` the device keeps resident at once (computed once per
+// kernel and device; 0 if the runtime cannot tell).
+template <typename KERN>
+int resident(KERN kern, int *cache) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+    if (cache[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, mfma_detail::kMThreads, 0) !=
+                hipSuccess)
+            return 0;
+        cache[dev] = std::max(1, cus * per_cu);
+    }
+    return cache[dev];
+}
+
+// Group rows of the grid: every group gets a workgroup row when the device
+// holds them all at once, else as many rows as it holds.
+int group_rows(int max_items, int cols, int resident_wgs) {
+    if (resident_wgs <= 0) return max_items;
+    return std::max(1, std::min(max_items, resident_wgs / std::max(cols, 1)));
+}
+}  // namespace
+
 hipError_t launch_up_mfma(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
                           uint16_t *h, hipStream_t s) {
     using namespace mfma_detail;
     if (max_items <= 0) return hipSuccess;
-    const dim3 grid((pool.F + kRowsPerBlock - 1) / kRowsPerBlock, max_items);
-    if (pool.fmt == MOE_FMT_BF16)
+    static int res_bf16[16], res_e2m1[16];
+    const int cols = (pool.F + kRowsPerBlock - 1) / kRowsPerBlock;
+    if (pool.fmt == MOE_FMT_BF16) {
+        const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<MOE_FMT_BF16>, res_bf16)));
         hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_BF16>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
-    else
+    } else {
+        const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<MOE_FMT_E2M1>, res_e2m1)));
         hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_E2M1>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
+    }
     return hipGetLastError();
 }
 
@@ -435,13 +454,16 @@ hipError_t launch_down_mfma(const PoolView &pool, const Items &items, int max_it
                             float *d, hipStream_t s) {
     using namespace mfma_detail;
     if (max_items <= 0) return hipSuccess;
+    static int res_bf16[16], res_e2m1[16];
     if (pool.fmt == MOE_FMT_BF16) {
         constexpr int rows = down_rows_per_block<MOE_FMT_BF16>();
-        const dim3 grid((pool.H + rows - 1) / rows, max_items);
+        const int cols = (pool.H + rows - 1) / rows;
+        const dim3 grid(cols, group_rows(max_items, cols, resident(down_mfma_kernel<MOE_FMT_BF16>, res_bf16)));
         hipLaunchKernelGGL(down_mfma_kernel<MOE_FMT_BF16>, grid, dim3(kMThreads), 0, s, pool, items, h, d);
     } else {
         constexpr int rows = down_rows_per_block<MOE_FMT_E2M1>();
-        const dim3 grid((pool.H + rows - 1) / rows, max_items);
+        const int cols = (pool.H + rows - 1) / rows;
+        const dim3 grid(cols, group_rows(max_items, cols, resident(down_mfma_kernel<MOE_FMT_E2M1>, res_e2m1)));
         hipLaunchKernelGGL(down_mfma_kernel<MOE_FMT_E2M1>, grid, dim3(kMThreads), 0, s, pool, items, h, d);
     }
     return hipGetLastError();
