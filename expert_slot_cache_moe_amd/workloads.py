@@ -2,7 +2,7 @@
 
 This module only draws numbers and lays them out in the storage formats
 the library and the oracle read (bf16 bit patterns, 4-bit codes with e4m3
-scales); it holds none of the decode step's arithmetic and imports neither
+or e8m0 scales); it holds none of the decode step's arithmetic and imports neither
 the oracle nor the HIP binding, so both can be fed from it.
 
 Recipes (numpy PCG64; each purpose gets its own stream spawned from the
@@ -10,7 +10,8 @@ seed):
   - expert weights: N(0, 0.02), stored as bf16 (round to nearest even via
     torch), or quantized per 16 consecutive elements of a row: scale =
     e4m3(amax / 6) (torch's float8_e4m3fn conversion), code = the nearest
-    E2M1 value of w / scale, global scale 1.0;
+    E2M1 value of w / scale, global scale 1.0; or MXFP4 (per 32 elements,
+    a power-of-two e8m0 scale, the OCP MX recipe);
   - hidden states: N(0, 1) as bf16;
   - router logits: N(0, 1) plus a Zipf rank bias -s * ln(rank + 1) over a
     seeded expert permutation, so the softmax favours experts with
@@ -81,8 +82,44 @@ def e2m1_expert_rows(g: np.random.Generator, rows: int, H: int, F: int, std=0.02
     return [np.stack(b) for b in banks]
 
 
+def _quantize_mxfp4(w: np.ndarray):
+    """w [n, cols] float32 -> (codes [n, cols/2] u8, e8m0 scales [n, cols/32] u8):
+    the OCP MX recipe, shared scale 2^(floor(log2(amax)) - 2) per 32
+    consecutive elements (2 = the largest E2M1 exponent), codes the nearest
+    E2M1 value of w / scale, saturating at 6."""
+    n, cols = w.shape
+    blk = w.reshape(n, cols // 32, 32).astype(np.float64)
+    amax = np.abs(blk).max(axis=2)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    code8 = np.clip(e + 127, 0, 254).astype(np.uint8)
+    scale = np.ldexp(1.0, code8.astype(np.int64) - 127)
+    mag = np.abs(blk) / scale[:, :, None]
+    mids = (E2M1_VALUES[1:] + E2M1_VALUES[:-1]) / 2
+    code = np.searchsorted(mids, mag).astype(np.uint8)
+    code |= (blk < 0).astype(np.uint8) << 3
+    code = code.reshape(n, cols)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, code8
+
+
+def mxfp4_expert_rows(g: np.random.Generator, rows: int, H: int, F: int, std=0.02):
+    """Four banks [rows, bytes]: w13 codes/e8m0 scales, w2 codes/e8m0 scales."""
+    banks = [[], [], [], []]
+    for _ in range(rows):
+        for m, (nr, nc) in enumerate(((2 * F, H), (H, F))):
+            w = g.standard_normal((nr, nc), dtype=np.float32) * np.float32(std)
+            codes, scales = _quantize_mxfp4(w)
+            banks[2 * m].append(codes.reshape(-1))
+            banks[2 * m + 1].append(scales.reshape(-1))
+    return [np.stack(b) for b in banks]
+
+
 def expert_rows(fmt: int, g, rows, H, F, std=0.02):
-    return bf16_expert_rows(g, rows, H, F, std) if fmt == 0 else e2m1_expert_rows(g, rows, H, F, std)
+    if fmt == 0:
+        return bf16_expert_rows(g, rows, H, F, std)
+    if fmt == 1:
+        return e2m1_expert_rows(g, rows, H, F, std)
+    return mxfp4_expert_rows(g, rows, H, F, std)
 
 
 # ---------------------------------------------------------------- routing

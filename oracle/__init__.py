@@ -12,6 +12,7 @@ from .ref import (  # noqa: F401
     bf16_to_f64,
     e4m3_to_f64,
     e2m1_to_f64,
+    e8m0_to_f64,
     query_widths,
     OracleCache,
     topk,

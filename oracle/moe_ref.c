@@ -83,6 +83,16 @@ double ref_e2m1_to_double(uint8_t nib)
     return sign ? -mag : mag;
 }
 
+/* OCP MX E8M0 scale (the MX formats' shared block scale): an unsigned
+ * biased exponent, value 2^(v - 127); v = 255 is NaN; no sign, no
+ * mantissa, no zero. */
+double ref_e8m0_to_double(uint8_t v)
+{
+    if (v == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)v - 127);
+}
+
 /* ------------------------------------------------------------------ */
 /* Expert weight access.                                               */
 /*                                                                     */
@@ -99,10 +109,16 @@ double ref_e2m1_to_double(uint8_t nib)
 /*   bank3: w2 codes   [H][F/2]                                        */
 /*   bank4: w2 scales  [H][F/16]                                       */
 /*   bank5: w2 global  fp32                                            */
+/* Format 2 (MXFP4: e2m1 with one e8m0 scale per 32 consecutive        */
+/* elements of a row, the OCP MX block), four banks:                   */
+/*   bank0: w13 codes  [2F][H/2]   element c in byte c/2, even c low   */
+/*   bank1: w13 scales [2F][H/32]  e8m0, one per 32 consecutive c      */
+/*   bank2: w2 codes   [H][F/2]                                        */
+/*   bank3: w2 scales  [H][F/32]                                       */
 /* ------------------------------------------------------------------ */
 
 typedef struct {
-    int fmt;                 /* 0 = bf16, 1 = e2m1/e4m3/fp32 */
+    int fmt;                 /* 0 = bf16, 1 = e2m1/e4m3/fp32, 2 = mxfp4 */
     int H, F;
     const uint8_t *bank[6];
     int64_t rb[6];           /* bytes per row in each bank */
@@ -125,6 +141,14 @@ static double ref_weight(const ref_pool *p, int64_t row, int m, int64_t r, int64
         uint16_t b;
         memcpy(&b, base + 2 * (r * ncol + c), 2);
         return ref_bf16_to_double(b);
+    } else if (p->fmt == 2) {
+        int b0 = 2 * m;
+        const uint8_t *codes = p->bank[b0] + row * p->rb[b0];
+        const uint8_t *scales = p->bank[b0 + 1] + row * p->rb[b0 + 1];
+        uint8_t byte = codes[r * (ncol / 2) + c / 2];
+        uint8_t nib = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+        uint8_t sc = scales[r * (ncol / 32) + c / 32];
+        return ref_e2m1_to_double(nib) * ref_e8m0_to_double(sc);
     } else {
         int b0 = 3 * m;
         const uint8_t *codes = p->bank[b0] + row * p->rb[b0];
@@ -168,7 +192,7 @@ static void ref_expert(const ref_pool *p, int64_t row, const uint16_t *x, double
 static void ref_pool_init(ref_pool *p, int fmt, int H, int F, const uint8_t *const *banks,
                           const int64_t *rb)
 {
-    int nb = fmt == 0 ? 2 : 6;
+    int nb = fmt == 0 ? 2 : (fmt == 2 ? 4 : 6);
     memset(p, 0, sizeof *p);
     p->fmt = fmt;
     p->H = H;

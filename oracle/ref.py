@@ -44,6 +44,8 @@ def lib():
         L.ref_e4m3_to_double.restype = C.c_double
         L.ref_e2m1_to_double.argtypes = [u8]
         L.ref_e2m1_to_double.restype = C.c_double
+        L.ref_e8m0_to_double.argtypes = [u8]
+        L.ref_e8m0_to_double.restype = C.c_double
         L.ref_query_widths.argtypes = [i32, i32, i32, i32, P]
         L.ref_query_widths.restype = i32
         L.ref_admit.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i32, P, i32, i32, P, P, P]
@@ -77,6 +79,10 @@ def e4m3_to_f64(v: int) -> float:
 
 def e2m1_to_f64(v: int) -> float:
     return lib().ref_e2m1_to_double(int(v))
+
+
+def e8m0_to_f64(v: int) -> float:
+    return lib().ref_e8m0_to_double(int(v))
 
 
 def query_widths(R: int, E: int, one_call: int = 256, qw: int = 128) -> list:
@@ -144,7 +150,7 @@ class Pool:
     def __init__(self, fmt: int, H: int, F: int, banks):
         self.fmt, self.H, self.F = fmt, H, F
         self.banks = [np.ascontiguousarray(b, np.uint8) for b in banks]
-        nb = 2 if fmt == 0 else 6
+        nb = {0: 2, 1: 6, 2: 4}[fmt]
         assert len(self.banks) == nb
         self._ptrs = (C.c_void_p * 6)(*([b.ctypes.data for b in self.banks] + [0] * (6 - nb)))
         self._rb = (C.c_int64 * 6)(*([b.shape[1] for b in self.banks] + [0] * (6 - nb)))

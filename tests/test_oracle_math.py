@@ -11,6 +11,7 @@ import scipy.special as sps
 import torch
 
 import oracle
+from expert_slot_cache_moe_amd import workloads as W
 
 # OCP Microscaling Formats spec, FP4 E2M1 value table (codes 0..7; the
 # sign bit gives codes 8..15).
@@ -33,6 +34,15 @@ def test_e4m3_decode_matches_torch_for_every_code():
     nan = np.isnan(ref)
     assert nan.sum() == 2 and (np.isnan(got) == nan).all()
     np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+def test_e8m0_decode_matches_torch_for_every_code():
+    """The OCP MX shared scale: 2^(v - 127), 255 = NaN (torch float8_e8m0fnu)."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([oracle.e8m0_to_f64(v) for v in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255]) and not np.isnan(got[:255]).any()
+    np.testing.assert_array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
 
 
 def test_e2m1_decode_matches_the_ocp_table():
@@ -151,6 +161,68 @@ def test_e2m1_expert_matches_numpy_dequant_swiglu(g13, g2):
         W2 = _numpy_dequant(c2[r], s2[r], g2)
         ref = _numpy_swiglu(W13, W2, _bf16_value(x))
         np.testing.assert_allclose(oracle.expert_ffn(pool, r, x), ref, rtol=1e-9, atol=1e-12)
+
+
+def _mxfp4_pool(rng, rows, H, F):
+    def mat(nr, nc):
+        codes = rng.integers(0, 256, (rows, nr, nc // 2), dtype=np.uint8)
+        scales = rng.integers(110, 140, (rows, nr, nc // 32), dtype=np.uint8)
+        return codes, scales
+
+    c13, s13 = mat(2 * F, H)
+    c2, s2 = mat(H, F)
+    banks = [c13.reshape(rows, -1), s13.reshape(rows, -1), c2.reshape(rows, -1), s2.reshape(rows, -1)]
+    return (c13, s13, c2, s2), oracle.Pool(2, H, F, banks)
+
+
+def _numpy_dequant_mx(codes, scales):
+    """codes [nr, nc/2] (element 2i low nibble), scales [nr, nc/32] e8m0 via torch."""
+    table = np.array(E2M1_TABLE + [-v for v in E2M1_TABLE])
+    lo, hi = codes & 0xF, codes >> 4
+    q = np.stack([table[lo], table[hi]], axis=-1).reshape(codes.shape[0], -1)
+    s = torch.from_numpy(scales.copy()).view(torch.float8_e8m0fnu).double().numpy()
+    return q * np.repeat(s, 32, axis=1)
+
+
+def test_mxfp4_expert_matches_numpy_dequant_swiglu():
+    """MXFP4 (OCP MX: E2M1 elements, one E8M0 scale per 32) against an
+    independent dequantisation and numpy matmuls."""
+    rng = np.random.default_rng(18)
+    H, F, rows = 64, 64, 3
+    (c13, s13, c2, s2), pool = _mxfp4_pool(rng, rows, H, F)
+    x = _bf16(rng.standard_normal(H) * 0.05)
+    for r in range(rows):
+        ref = _numpy_swiglu(_numpy_dequant_mx(c13[r], s13[r]), _numpy_dequant_mx(c2[r], s2[r]),
+                            _bf16_value(x))
+        np.testing.assert_allclose(oracle.expert_ffn(pool, r, x), ref, rtol=1e-9, atol=1e-12)
+
+
+def test_mxfp4_quantized_rows_round_trip_within_half_a_step():
+    """The generator's MXFP4 rows decode (oracle) to within half an E2M1
+    step of the drawn weights, |w - q| <= scale * 1 (the widest gap, 4 -> 6,
+    halved), except that magnitudes past 6 * scale (the OCP MX scale
+    2^(floor(log2 amax) - 2) leaves amax / scale in [4, 8)) saturate to
+    6 * scale; signs are kept."""
+    g = W.rng(3, "mx-roundtrip")
+    H, F = 64, 32
+    banks = W.mxfp4_expert_rows(g, 1, H, F)
+    pool = oracle.Pool(2, H, F, banks)
+    g = W.rng(3, "mx-roundtrip")
+    w13 = g.standard_normal((2 * F, H), dtype=np.float32) * np.float32(0.02)
+    q = _numpy_dequant_mx(banks[0][0].reshape(2 * F, H // 2), banks[1][0].reshape(2 * F, H // 32))
+    scale = np.repeat(torch.from_numpy(banks[1][0].reshape(2 * F, H // 32).copy())
+                      .view(torch.float8_e8m0fnu).double().numpy(), 32, axis=1)
+    sat = np.abs(w13) > 6 * scale
+    assert (np.abs(w13 - q)[~sat] <= scale[~sat] * 1.0 + 1e-12).all()
+    np.testing.assert_array_equal(np.abs(q[sat]), 6 * scale[sat])
+    assert sat.any() and (~sat).any()
+    assert ((np.sign(q) == np.sign(w13)) | (q == 0)).all()
+    # the oracle reads the same rows: one unit activation picks column 0
+    x = np.zeros(H, np.uint16)
+    x[0] = 0x3F80                                    # bf16 1.0
+    ref = _numpy_swiglu(q, _numpy_dequant_mx(banks[2][0].reshape(H, F // 2), banks[3][0].reshape(H, F // 32)),
+                        _bf16_value(x))
+    np.testing.assert_allclose(oracle.expert_ffn(pool, 0, x), ref, rtol=1e-9, atol=1e-15)
 
 
 def test_routed_sums_weighted_experts_and_skips_minus_one():
