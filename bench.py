@@ -146,6 +146,8 @@ WIDE = (
     ("wide decode bf16: 150 rows x top-2 over 160 experts, H 1024, F 256", 0, 1024, 256, 150, 2, 160, 8),
     ("wide decode e2m1 (E4M3 per-16 scales): 600 rows x top-2 over 160 experts, H 1024, F 256",
      1, 1024, 256, 600, 2, 160, 8),
+    ("wide decode mxfp4 (E8M0 per-32 scales): 600 rows x top-2 over 160 experts, H 1024, F 256",
+     2, 1024, 256, 600, 2, 160, 8),
     ("prefill chunk bf16: 42 rows x top-6 over 256 experts, H 4096, F 1024", 0, 4096, 1024, 42, 6, 256, 1),
     ("prefill chunk bf16: 50 rows x top-6 over 640 experts, H 4096, F 1024", 0, 4096, 1024, 50, 6, 640, 1),
 )
@@ -170,10 +172,14 @@ def wide_gemv_benchmark(torch, m, seed=0):
         else:
             banks = [torch.randint(0, 256, (rows, r), dtype=torch.uint8, device="cuda", generator=gen)
                      for r in rb]
-            for b in (1, 4):
-                banks[b].fill_(0x30)                       # E4M3 scale 0.125
-            for b in (2, 5):
-                banks[b].view(torch.float32).fill_(1.0)    # global scales
+            if fmt == 1:
+                for b in (1, 4):
+                    banks[b].fill_(0x30)                       # E4M3 scale 0.125
+                for b in (2, 5):
+                    banks[b].view(torch.float32).fill_(1.0)    # global scales
+            else:
+                for b in (1, 3):
+                    banks[b].fill_(120)                        # E8M0 scale 2^-7
         pool = m.make_pool(fmt, Hw, Fw, rows, banks)
         g = np.random.default_rng(seed)
         sets = [np.stack([g.choice(Ew, Kw, replace=False) for _ in range(T)]) + (i % copies) * Ew

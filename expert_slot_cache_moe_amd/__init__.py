@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_cache.so")
 
 MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR, MOE_OUT_OF_MEMORY = range(5)
-MOE_FMT_BF16, MOE_FMT_E2M1 = 0, 1
+MOE_FMT_BF16, MOE_FMT_E2M1, MOE_FMT_MXFP4 = 0, 1, 2
 MOE_MAX_BANKS = 6
 MOE_NUM_STATS = 5
 STAT_NAMES = ("calls", "met", "missed", "overflow", "invalid")

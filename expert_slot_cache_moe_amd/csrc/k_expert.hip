@@ -29,7 +29,7 @@
 
 namespace moe {
 
-// Instantiated in k_expert_bf16.hip and k_expert_e2m1.hip.
+// Instantiated in k_expert_bf16.hip, k_expert_e2m1.hip and k_expert_mxfp4.hip.
 namespace expert_detail {
 #define MOE_EXTERN_FMT(FMT)                                                                        \
     extern template hipError_t launch_up_fmt<FMT>(const PoolView &, const Items &, int,            \
@@ -45,6 +45,7 @@ namespace expert_detail {
                                                           uint16_t *, hipStream_t);
 MOE_EXTERN_FMT(MOE_FMT_BF16)
 MOE_EXTERN_FMT(MOE_FMT_E2M1)
+MOE_EXTERN_FMT(MOE_FMT_MXFP4)
 #undef MOE_EXTERN_FMT
 }  // namespace expert_detail
 
@@ -161,13 +162,13 @@ bool chunks_ok(int chunks, int max_chunks) {
 int epc(int fmt) { return fmt == MOE_FMT_BF16 ? 8 : 32; }
 int max_chunks(int fmt) {
     return fmt == MOE_FMT_BF16 ? expert_detail::MaxChunks<MOE_FMT_BF16>::v
-                               : expert_detail::MaxChunks<MOE_FMT_E2M1>::v;
+                               : expert_detail::MaxChunks<MOE_FMT_E2M1>::v;  // = the MXFP4 limit
 }
 
 }  // namespace
 
 bool expert_shape_supported(int fmt, int H, int F) {
-    if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_E2M1) return false;
+    if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_E2M1 && fmt != MOE_FMT_MXFP4) return false;
     if (H <= 0 || F <= 0 || H % epc(fmt) || F % epc(fmt)) return false;
     // the shared gate reads H in 8-element chunks
     if (H % 8) return false;
@@ -194,6 +195,8 @@ hipError_t launch_up(const PoolView &pool, const Items &items, int max_items, co
                      uint16_t *h, const uint16_t *gate_vec, float *gamma, hipStream_t s) {
     if (max_items <= 0) return hipSuccess;
     using namespace expert_detail;
+    if (pool.fmt == MOE_FMT_MXFP4)
+        return launch_up_fmt<MOE_FMT_MXFP4>(pool, items, max_items, x, h, gate_vec, gamma, s);
     return pool.fmt == MOE_FMT_BF16
                ? launch_up_fmt<MOE_FMT_BF16>(pool, items, max_items, x, h, gate_vec, gamma, s)
                : launch_up_fmt<MOE_FMT_E2M1>(pool, items, max_items, x, h, gate_vec, gamma, s);
@@ -203,6 +206,8 @@ hipError_t launch_down_to_d(const PoolView &pool, const Items &items, int max_it
                             const uint16_t *h, float *d, const float *gamma, hipStream_t s) {
     if (max_items <= 0) return hipSuccess;
     using namespace expert_detail;
+    if (pool.fmt == MOE_FMT_MXFP4)
+        return launch_down_to_d_fmt<MOE_FMT_MXFP4>(pool, items, max_items, h, d, gamma, s);
     return pool.fmt == MOE_FMT_BF16
                ? launch_down_to_d_fmt<MOE_FMT_BF16>(pool, items, max_items, h, d, gamma, s)
                : launch_down_to_d_fmt<MOE_FMT_E2M1>(pool, items, max_items, h, d, gamma, s);
@@ -213,6 +218,8 @@ hipError_t launch_down_fused(const PoolView &pool, const int32_t *idx, const flo
                              const int32_t *route_plan, uint16_t *out, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     using namespace expert_detail;
+    if (pool.fmt == MOE_FMT_MXFP4)
+        return launch_down_fused_fmt<MOE_FMT_MXFP4>(pool, idx, w, T, K, h, addend, d, route_plan, out, s);
     return pool.fmt == MOE_FMT_BF16
                ? launch_down_fused_fmt<MOE_FMT_BF16>(pool, idx, w, T, K, h, addend, d, route_plan, out, s)
                : launch_down_fused_fmt<MOE_FMT_E2M1>(pool, idx, w, T, K, h, addend, d, route_plan, out,

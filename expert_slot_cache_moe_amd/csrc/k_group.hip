@@ -101,6 +101,37 @@ template <> struct ASlab<MOE_FMT_E2M1> {
     }
 };
 
+// MXFP4: a lane's 32 elements of a slab are exactly one E8M0 scale block;
+// gfx950 converts two codes to bf16 with the block's power-of-two scale in
+// one instruction, exactly (E2M1 times a power of two fits bf16).
+template <> struct ASlab<MOE_FMT_MXFP4> {
+    u32x4 codes;
+    uint32_t sc;
+    __device__ __forceinline__ void load(const PoolView &p, int64_t prow, int m, int r, int e0) {
+        const int ncols = m == 0 ? p.H : p.F;
+        const int b = 2 * m;
+        codes = *reinterpret_cast<const u32x4 *>(p.bank[b] + prow * p.rb[b] +
+                                                 (int64_t)r * (ncols / 2) + e0 / 2);
+        sc = p.bank[b + 1][prow * p.rb[b + 1] + (int64_t)r * (ncols / 32) + e0 / 32];
+    }
+    __device__ __forceinline__ void expand(u32x4 (&a)[4]) const {
+        const float s = e8m0_f(sc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t word = codes[i];
+            u32x4 o;
+#define MOE_MX_BYTE(B) \
+    o[B] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, B));
+            MOE_MX_BYTE(0)
+            MOE_MX_BYTE(1)
+            MOE_MX_BYTE(2)
+            MOE_MX_BYTE(3)
+#undef MOE_MX_BYTE
+            a[i] = o;
+        }
+    }
+};
+
 template <int FMT>
 __device__ __forceinline__ float matrix_glob(const PoolView &p, int64_t prow, int m) {
     if constexpr (FMT == MOE_FMT_E2M1) {
@@ -438,9 +469,12 @@ hipError_t launch_up_mfma(const PoolView &pool, const Items &items, int max_item
                           uint16_t *h, hipStream_t s) {
     using namespace mfma_detail;
     if (max_items <= 0) return hipSuccess;
-    static int res_bf16[16], res_e2m1[16];
+    static int res_bf16[16], res_e2m1[16], res_mx[16];
     const int cols = (pool.F + kRowsPerBlock - 1) / kRowsPerBlock;
-    if (pool.fmt == MOE_FMT_BF16) {
+    if (pool.fmt == MOE_FMT_MXFP4) {
+        const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<MOE_FMT_MXFP4>, res_mx)));
+        hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_MXFP4>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
+    } else if (pool.fmt == MOE_FMT_BF16) {
         const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<MOE_FMT_BF16>, res_bf16)));
         hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_BF16>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
     } else {
@@ -454,8 +488,13 @@ hipError_t launch_down_mfma(const PoolView &pool, const Items &items, int max_it
                             float *d, hipStream_t s) {
     using namespace mfma_detail;
     if (max_items <= 0) return hipSuccess;
-    static int res_bf16[16], res_e2m1[16];
-    if (pool.fmt == MOE_FMT_BF16) {
+    static int res_bf16[16], res_e2m1[16], res_mx[16];
+    if (pool.fmt == MOE_FMT_MXFP4) {
+        constexpr int rows = down_rows_per_block<MOE_FMT_MXFP4>();
+        const int cols = (pool.H + rows - 1) / rows;
+        const dim3 grid(cols, group_rows(max_items, cols, resident(down_mfma_kernel<MOE_FMT_MXFP4>, res_mx)));
+        hipLaunchKernelGGL(down_mfma_kernel<MOE_FMT_MXFP4>, grid, dim3(kMThreads), 0, s, pool, items, h, d);
+    } else if (pool.fmt == MOE_FMT_BF16) {
         constexpr int rows = down_rows_per_block<MOE_FMT_BF16>();
         const int cols = (pool.H + rows - 1) / rows;
         const dim3 grid(cols, group_rows(max_items, cols, resident(down_mfma_kernel<MOE_FMT_BF16>, res_bf16)));

@@ -52,6 +52,12 @@ void row_bytes_of(int fmt, int H, int F, int64_t rb[MOE_MAX_BANKS], int *nb) {
         rb[0] = (int64_t)2 * F * H * 2;
         rb[1] = (int64_t)H * F * 2;
         *nb = 2;
+    } else if (fmt == MOE_FMT_MXFP4) {
+        rb[0] = (int64_t)2 * F * H / 2;
+        rb[1] = (int64_t)2 * F * H / 32;
+        rb[2] = (int64_t)H * F / 2;
+        rb[3] = (int64_t)H * F / 32;
+        *nb = 4;
     } else {
         rb[0] = (int64_t)2 * F * H / 2;
         rb[1] = (int64_t)2 * F * H / 16;
@@ -184,7 +190,8 @@ PoolView slot_pool_view(const moe_cache *c) {
 
 moe_status_t pool_view_of(const moe_pool_t *pool, PoolView &pv) {
     if (!pool) return fail(MOE_INVALID_ARG, "pool is NULL");
-    if (pool->weight_format != MOE_FMT_BF16 && pool->weight_format != MOE_FMT_E2M1)
+    if (pool->weight_format != MOE_FMT_BF16 && pool->weight_format != MOE_FMT_E2M1 &&
+        pool->weight_format != MOE_FMT_MXFP4)
         return fail(MOE_INVALID_ARG, "unknown weight format %d", pool->weight_format);
     if (pool->num_rows < 1) return fail(MOE_INVALID_ARG, "pool has %d rows", pool->num_rows);
     if (!expert_shape_supported(pool->weight_format, pool->hidden, pool->ffn))
@@ -382,11 +389,14 @@ const char *moe_last_error(void) { return g_last_error.c_str(); }
 moe_status_t moe_bank_row_bytes(int32_t weight_format, int32_t hidden, int32_t ffn,
                                 int64_t row_bytes_out[MOE_MAX_BANKS], int32_t *num_banks_out) {
     if (!row_bytes_out || !num_banks_out) return fail(MOE_INVALID_ARG, "NULL output");
-    if (weight_format != MOE_FMT_BF16 && weight_format != MOE_FMT_E2M1)
+    if (weight_format != MOE_FMT_BF16 && weight_format != MOE_FMT_E2M1 &&
+        weight_format != MOE_FMT_MXFP4)
         return fail(MOE_INVALID_ARG, "unknown weight format %d", weight_format);
     if (hidden < 1 || ffn < 1) return fail(MOE_INVALID_ARG, "hidden/ffn must be >= 1");
     if (weight_format == MOE_FMT_E2M1 && (hidden % 16 || ffn % 16))
         return fail(MOE_INVALID_ARG, "4-bit rows need hidden and ffn multiples of 16");
+    if (weight_format == MOE_FMT_MXFP4 && (hidden % 32 || ffn % 32))
+        return fail(MOE_INVALID_ARG, "mxfp4 rows need hidden and ffn multiples of 32");
     int nb;
     row_bytes_of(weight_format, hidden, ffn, row_bytes_out, &nb);
     *num_banks_out = nb;
@@ -442,7 +452,8 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
 
     // Weights.
     if (d->num_banks != 0) {
-        if (d->weight_format != MOE_FMT_BF16 && d->weight_format != MOE_FMT_E2M1) {
+        if (d->weight_format != MOE_FMT_BF16 && d->weight_format != MOE_FMT_E2M1 &&
+            d->weight_format != MOE_FMT_MXFP4) {
             moe_status_t s = fail(MOE_INVALID_ARG, "unknown weight format %d", d->weight_format);
             return bail(s);
         }

@@ -45,6 +45,13 @@ __device__ __forceinline__ float e4m3_f(uint32_t v) {
     return __uint_as_float(__float_as_uint(mag) | s);
 }
 
+// OCP MX E8M0 block scale: 2^(v - 127), v = 255 NaN (v = 0 is the
+// subnormal float 2^-127).
+__device__ __forceinline__ float e8m0_f(uint32_t v) {
+    if (v == 0xFFu) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float(v ? (v << 23) : 0x00400000u);
+}
+
 // OCP E2M1: bias 1, exponent 0 subnormal (0 or 0.5).
 __device__ __forceinline__ float e2m1_f(uint32_t n) {
     uint32_t e = (n >> 1) & 3u;

@@ -70,8 +70,14 @@ typedef enum {
  *   bank 0: w13 codes  [2F][H/2]    bank 3: w2 codes  [H][F/2]
  *   bank 1: w13 scales [2F][H/16]   bank 4: w2 scales [H][F/16]
  *   bank 2: w13 global fp32         bank 5: w2 global fp32
- * A weight is code * scale * global. */
-enum { MOE_FMT_BF16 = 0, MOE_FMT_E2M1 = 1 };
+ * A weight is code * scale * global.
+ * MOE_FMT_MXFP4, four banks per expert row (OCP MX FP4: E2M1 values with
+ * one E8M0 scale, 2^(s - 127), per 32 consecutive elements of a row; code
+ * layout as above):
+ *   bank 0: w13 codes  [2F][H/2]    bank 2: w2 codes  [H][F/2]
+ *   bank 1: w13 scales [2F][H/32]   bank 3: w2 scales [H][F/32]
+ * A weight is code * 2^(s - 127). */
+enum { MOE_FMT_BF16 = 0, MOE_FMT_E2M1 = 1, MOE_FMT_MXFP4 = 2 };
 #define MOE_MAX_BANKS 6
 
 /* Statistics slots, per layer (int64 each) [P3 Solution]. */

@@ -89,6 +89,10 @@ def _routed_gpu(pool, x, idx, w, H, addend=None):
     (1, 1024, 256, 40, 33, 2),      # e2m1, grouped path
     (0, 4096, 1024, 10, 7, 6),      # prefill-chunk shape
     (1, 64, 64, 6, 3, 3),           # e2m1, smallest rows
+    (2, 1024, 256, 40, 1, 2),       # mxfp4, decode path
+    (2, 2048, 512, 12, 1, 8),       # mxfp4, shared-expert decode shape
+    (2, 1024, 256, 40, 33, 2),      # mxfp4, grouped path (matrix cores)
+    (2, 64, 64, 6, 3, 3),           # mxfp4, smallest rows (vector path)
 ])
 def test_routed_matches_oracle(fmt, H, F, rows, T, K):
     g = W.rng(4, "routed", fmt, H, T)
@@ -103,7 +107,7 @@ def test_routed_matches_oracle(fmt, H, F, rows, T, K):
     _close(_bf16_to_f64(out), ref, f"fmt{fmt} H{H} T{T}")
 
 
-@pytest.mark.parametrize("fmt,rows", [(0, 6), (1, 6), (0, 2), (1, 2)])
+@pytest.mark.parametrize("fmt,rows", [(0, 6), (1, 6), (2, 6), (0, 2), (1, 2), (2, 2)])
 def test_grouped_routes_do_not_depend_on_their_place_in_the_group(fmt, rows):
     """Wide steps put a group's routes in arrival order; a token's output
     must not depend on it.  Permuting the tokens permutes the output bit
@@ -194,6 +198,36 @@ def _oracle_layer(oc, host, sh, layer, x, lg, K, fmt, H, F, max_fetch=-1):
     return ref, slots, w
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_tiny_layer_decode_4bit_formats(fmt):
+    """The layer step with 4-bit experts (E4M3-scaled E2M1 and MXFP4): slot
+    ids exact, outputs within tolerance of the oracle, gathered slots hold
+    their experts' bytes."""
+    lay, host, sh = _tiny_layers(2, True, seed=31, fmt=fmt, E=16, S=6, H=64, F=128, K=2)
+    oc = oracle.OracleCache(1, 16, 6)
+    g = W.rng(31, "tiny-4bit", fmt)
+    out = torch.empty((1, 64), dtype=torch.int16, device="cuda")
+    ids = torch.empty((1, 2), dtype=torch.int32, device="cuda")
+    try:
+        for t in range(16):
+            x = W.normal_bf16(g, (1, 64))
+            lg = W.zipf_logits(g, 1, 16, 0.8)
+            lay.decode(0, _dev_u16(x), torch.from_numpy(lg).cuda(), 2, out, ids_out=ids)
+            torch.cuda.synchronize()
+            ref, slots, _ = _oracle_layer(oc, host, sh, 0, x, lg, 2, fmt, 64, 128)
+            np.testing.assert_array_equal(ids.cpu().numpy(), slots, err_msg=f"step {t}")
+            _close(_bf16_to_f64(out), ref, f"fmt {fmt} step {t}")
+        for b in range(len(lay.slot_banks)):
+            sb = lay.slot_banks[b].cpu().numpy()
+            for s_ in range(6):
+                e = oc.own[s_]
+                if e >= 0:
+                    np.testing.assert_array_equal(sb[s_], host[0][b][e])
+        assert m.moe_cache_stats(lay.cache)[2] > 5
+    finally:
+        lay.close()
+
+
 @pytest.mark.parametrize("overlap", [0, 1, 2])
 @pytest.mark.parametrize("shared", [False, True])
 def test_tiny_layer_decode_32_steps(overlap, shared):
@@ -234,6 +268,7 @@ def _replicated_rows(fmt, g, E, H, F, distinct):
     (0, 1024, 256, 160, 160, 150, 2, 256, 128, 160, 150),   # wide bf16 step
     (1, 1024, 256, 160, 1100, 600, 2, 256, 128, 40, 64),    # wide e2m1 step over 1100 slots
     (1, 1024, 256, 160, 160, 600, 2, 3, 3, 40, 64),         # ... one layer's experts, 3 per query
+    (2, 1024, 256, 160, 1100, 600, 2, 256, 128, 40, 64),    # the wide 4-bit step as MXFP4
     (0, 4096, 1024, 256, 256, 42, 6, 3, 3, 8, 6),           # prefill chunk, 3 per query
     (0, 4096, 1024, 640, 640, 50, 6, 256, 128, 8, 4),       # prefill chunk over 640 experts
 ])
