@@ -1,0 +1,77 @@
+"""The shared-expert decode workload at full size, in the launch
+configuration bench.py times: 40 layers x 256 experts, top-8 + gated
+shared expert, H 2048, F 512, 3164 slots, bf16 experts in a 64.4 GB
+pinned host store, the staged schedule captured as one hipGraph per token.
+After 64 warm-up tokens, the next 3 tokens' slot ids (all 40 layers) must
+equal the oracle's admission bit for bit, their router weights match, and
+their outputs match the oracle within the tolerance, the oracle reading
+each routed expert's own host rows (so the gathered slot bytes are checked
+too)."""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import expert_slot_cache_moe_amd as m
+from expert_slot_cache_moe_amd import workloads as W
+import oracle
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def test_full_size_decode_matches_oracle():
+    L, E, K, H, F, S = bench.L, bench.E, bench.K, bench.H, bench.F, bench.S
+    warm, check, distinct = 64, 3, 64
+    lay = bench.build_stack(torch, m, W, overlap=2)
+    try:
+        lg_all, x_all = bench.make_trace(torch, W, warm + check)
+        x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+        lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
+        out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+        ids = torch.empty((L, 1, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((L, 1, K), dtype=torch.float32, device="cuda")
+        graph = bench.capture(torch, lay, x_st, lg_st, out, ids, w)
+        for t in range(warm):
+            x_st.copy_(x_all[t])
+            lg_st.copy_(lg_all[t])
+            graph.replay()
+        torch.cuda.synchronize()
+
+        lg_np = lg_all.cpu().numpy()
+        x_np = x_all.cpu().numpy().view(np.uint16)
+        oc = oracle.OracleCache(L, E, S)
+        for t in range(warm):
+            for l in range(L):
+                e_ids, _ = oracle.topk(lg_np[t, l], K)
+                oc.admit(l, e_ids.reshape(-1))
+        g = W.rng(0, "bench", "experts")
+        pool = oracle.Pool(0, H, F, W.bf16_expert_rows(g, distinct, H, F))
+        gs = W.rng(0, "bench", "shared")
+        shared = [(W.normal_bf16(gs, 2 * F * H, 0.02), W.normal_bf16(gs, H * F, 0.02),
+                   W.normal_bf16(gs, H, 0.02)) for _ in range(L)]
+
+        misses = 0
+        for t in range(warm, warm + check):
+            x_st.copy_(x_all[t])
+            lg_st.copy_(lg_all[t])
+            graph.replay()
+            torch.cuda.synchronize()
+            got_ids = ids.cpu().numpy()
+            got_w = w.cpu().numpy()
+            got = out.view(torch.bfloat16).double().cpu().numpy()
+            for l in range(L):
+                e_ids, wts = oracle.topk(lg_np[t, l], K)
+                slots = oc.admit(l, e_ids.reshape(-1)).reshape(1, K)
+                misses += len(oc.plan_slot)
+                np.testing.assert_array_equal(got_ids[l], slots, err_msg=f"token {t} layer {l}")
+                np.testing.assert_allclose(got_w[l], wts, rtol=1e-5)
+                rows = ((l * E + e_ids) * 7919) % distinct          # the host row each expert holds
+                idx = np.where(slots >= 0, rows, -1).astype(np.int32)
+                _, add = oracle.shared(H, F, *shared[l], x_np[t, l])
+                ref = oracle.routed(pool, idx, wts, x_np[t, l], addend=add)
+                err = np.abs(got[l] - ref).max()
+                assert err <= TOL * np.abs(ref).max(), f"token {t} layer {l}: max err {err:.3e}"
+        assert misses > 0                    # the checked tokens do fetch
+    finally:
+        lay.close()
