@@ -22,8 +22,9 @@
  *        one-call width, sorted fixed-length distinct list in query-width
  *        chunks, statistics counted once per step, histogram per route.
  *   [P4] llama.cpp fork PR #126, "cuda : MoE look-ahead expert prefetch
- *        ...": section Consumer -- expert ids outside [0, n_experts) are
- *        ignored.
+ *        ...": sections Consumer and Eviction guard -- expert ids outside
+ *        [0, n_experts) are ignored; speculative fills through the LRU
+ *        victim order, pinned slots never chosen, and the LFRU guard.
  *
  * Precision: every floating-point result is computed in double.  Inputs
  * are the stored formats (bf16, e2m1 nibbles, e4m3 scales, fp32 logits
@@ -332,8 +333,11 @@ void ref_topk(int T, int E, int K, const float *logits, int32_t *ids, double *w)
 /*   own[S]     l*E + e held by the slot, or -1                        */
 /*   stamp[S]   clock value of the slot's last use (0 = never)         */
 /*   clock[1]   step counter, one tick per admission step              */
-/*   stats[L*5] per layer: calls, met, missed, overflow, invalid       */
-/*   freq[L*E]  per layer, per expert: routes seen                     */
+/*   stats[L*8] per layer: calls, met, missed, overflow, invalid,      */
+/*              prefetch calls, prefetch fills, prefetch drops         */
+/*   freq[L*E]  per layer, per expert: routes seen (demand only)       */
+/*   dlast[L*E] clock value of the expert's last demand step (0 never) */
+/*   last_demand[1] clock value of the latest demand step (0 none)     */
 /*                                                                     */
 /* One step admits the routes of one layer ([P3] Solution):            */
 /*  - a step of at most one_call routes is one query over its routes;  */
@@ -356,7 +360,10 @@ void ref_topk(int T, int E, int K, const float *logits, int32_t *ids, double *w)
 /* within a query; the gather copies exactly these rows.               */
 /* ------------------------------------------------------------------ */
 
-enum { REF_CALLS = 0, REF_MET = 1, REF_MISSED = 2, REF_OVERFLOW = 3, REF_INVALID = 4 };
+enum {
+    REF_CALLS = 0, REF_MET = 1, REF_MISSED = 2, REF_OVERFLOW = 3, REF_INVALID = 4,
+    REF_PF_CALLS = 5, REF_PF_FILLED = 6, REF_PF_DROPPED = 7, REF_NSTATS = 8
+};
 
 /* The widths of the queries a step of R routes over E experts is
  * admitted in.  Returns the number of queries written to out. */
@@ -390,23 +397,27 @@ static int ref_victim_cmp(const void *a, const void *b)
 
 /* Returns 0 on success, -1 on a bad argument. */
 int ref_admit(int L, int E, int S, int one_call, int qw, int32_t *res, int32_t *own,
-              uint32_t *stamp, uint32_t *clock, int64_t *stats, int64_t *freq, int layer,
-              int32_t *ids, int R, int max_fetch, int32_t *plan_slot, int32_t *plan_expert,
-              int32_t *n_miss)
+              uint32_t *stamp, uint32_t *clock, int64_t *stats, int64_t *freq, uint32_t *dlast,
+              uint32_t *last_demand, int layer, int32_t *ids, int R, int max_fetch,
+              int32_t *plan_slot, int32_t *plan_expert, int32_t *n_miss)
 {
     if (layer < 0 || layer >= L || R < 0 || E < 1 || S < 1 || one_call < 1 || qw < 1)
         return -1;
     int32_t *resl = res + (int64_t)layer * E;
-    int64_t *st = stats + (int64_t)layer * 5;
+    int64_t *st = stats + (int64_t)layer * REF_NSTATS;
     uint32_t now = ++(*clock);
 
-    /* Histogram over every valid route; invalid routes counted. */
+    /* Histogram over every valid route; invalid routes counted.  The
+     * step is a demand access of each of its valid experts. */
     for (int i = 0; i < R; i++) {
-        if (ids[i] >= 0 && ids[i] < E)
+        if (ids[i] >= 0 && ids[i] < E) {
             freq[(int64_t)layer * E + ids[i]] += 1;
-        else
+            dlast[(int64_t)layer * E + ids[i]] = now;
+        } else {
             st[REF_INVALID] += 1;
+        }
     }
+    *last_demand = now;
 
     /* The queries, as lists of candidate ids (sentinel E = padding). */
     int nlist;
@@ -510,6 +521,118 @@ int ref_admit(int L, int E, int S, int one_call, int qw, int32_t *res, int32_t *
     free(inq);
     free(dq);
     free(miss);
+    free(vict);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Look-ahead prefetch with the LFRU eviction guard ([P4] Consumer,    */
+/* Eviction guard).  One call fills a layer's predicted experts ahead  */
+/* of its demand step, through the same LRU victim order:              */
+/*  - ids outside [0, E) are ignored; the rest are taken once each,    */
+/*    ascending;                                                       */
+/*  - a predicted expert already resident is used now (its slot's      */
+/*    stamp takes this call's clock value), so no fill of the same     */
+/*    call evicts it;                                                  */
+/*  - victims are the slots not used in this call and not pinned,      */
+/*    least recently used first, lower slot id first among equals.  A  */
+/*    slot is pinned when it was used at or after the latest demand    */
+/*    step (its readers may still run, and fills made since then are   */
+/*    still being copied);                                             */
+/*  - each missing prediction, ascending, looks at the next victim.    */
+/*    The victim's owner is protected when it has at least 2 demand    */
+/*    accesses and its score exceeds 1.25 x the prediction's score + 4 */
+/*    (score = demand frequency x 256 + recency byte, the byte being   */
+/*    255 - min(255, clock - last demand), 0 if never demanded).  A    */
+/*    protected owner stays and the prediction is dropped (the next    */
+/*    prediction looks at the same victim); otherwise the prediction   */
+/*    takes the slot;                                                  */
+/*  - heat (freq, dlast) counts demand accesses only: prefetch reads   */
+/*    it and never writes it.                                          */
+/* The fill plan lists (slot, expert) in ascending expert order.       */
+/* ------------------------------------------------------------------ */
+
+static int64_t ref_lfru_score(const int64_t *freq, const uint32_t *dlast, int64_t x, uint32_t now)
+{
+    int64_t rec = 0;
+    if (dlast[x] != 0) {
+        uint32_t age = now - dlast[x];
+        rec = 255 - (age < 255 ? (int64_t)age : 255);
+    }
+    return freq[x] * 256 + rec;
+}
+
+/* Returns 0 on success, -1 on a bad argument. */
+int ref_prefetch(int L, int E, int S, int32_t *res, int32_t *own, uint32_t *stamp,
+                 uint32_t *clock, const uint32_t *last_demand, int64_t *stats,
+                 const int64_t *freq, const uint32_t *dlast, int layer, const int32_t *ids, int n,
+                 int32_t *plan_slot, int32_t *plan_expert, int32_t *n_fill)
+{
+    if (layer < 0 || layer >= L || n < 0 || E < 1 || S < 1)
+        return -1;
+    *n_fill = 0;
+    if (n == 0)   /* width 0: nothing happens, not even a call */
+        return 0;
+    int64_t lbase = (int64_t)layer * E;
+    int64_t *st = stats + (int64_t)layer * REF_NSTATS;
+    uint32_t now = ++(*clock);
+    uint32_t ld = *last_demand;
+
+    char *want = (char *)calloc((size_t)E, 1);
+    for (int i = 0; i < n; i++)
+        if (ids[i] >= 0 && ids[i] < E)
+            want[ids[i]] = 1;
+
+    /* Predicted experts already resident are used now. */
+    for (int e = 0; e < E; e++)
+        if (want[e] && res[lbase + e] >= 0)
+            stamp[res[lbase + e]] = now;
+
+    ref_victim *vict = (ref_victim *)malloc(sizeof(ref_victim) * (size_t)S);
+    int nv = 0;
+    for (int s = 0; s < S; s++) {
+        int pinned = stamp[s] != 0 && stamp[s] >= ld;
+        if (stamp[s] < now && !pinned) {
+            vict[nv].stamp = stamp[s];
+            vict[nv].slot = s;
+            nv++;
+        }
+    }
+    qsort(vict, (size_t)nv, sizeof(ref_victim), ref_victim_cmp);
+
+    int cursor = 0, nfill = 0;
+    for (int e = 0; e < E; e++) {
+        if (!want[e] || res[lbase + e] >= 0)
+            continue;
+        if (cursor >= nv) {
+            st[REF_PF_DROPPED] += 1;
+            continue;
+        }
+        int32_t s = vict[cursor].slot;
+        int32_t o = own[s];
+        if (o >= 0 && freq[o] >= 2) {
+            int64_t so = ref_lfru_score(freq, dlast, o, now);
+            int64_t sp = ref_lfru_score(freq, dlast, lbase + e, now);
+            if (4 * so > 5 * sp + 16) {   /* so > 1.25 sp + 4 */
+                st[REF_PF_DROPPED] += 1;
+                continue;
+            }
+        }
+        if (o >= 0)
+            res[o] = -1;
+        own[s] = (int32_t)(lbase + e);
+        res[lbase + e] = s;
+        stamp[s] = now;
+        plan_slot[nfill] = s;
+        plan_expert[nfill] = e;
+        nfill++;
+        cursor++;
+    }
+    st[REF_PF_FILLED] += nfill;
+    st[REF_PF_CALLS] += 1;
+    *n_fill = nfill;
+
+    free(want);
     free(vict);
     return 0;
 }

@@ -48,8 +48,10 @@ def lib():
         L.ref_e8m0_to_double.restype = C.c_double
         L.ref_query_widths.argtypes = [i32, i32, i32, i32, P]
         L.ref_query_widths.restype = i32
-        L.ref_admit.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i32, P, i32, i32, P, P, P]
+        L.ref_admit.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, i32, P, i32, i32, P, P, P]
         L.ref_admit.restype = i32
+        L.ref_prefetch.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, i32, P, i32, P, P, P]
+        L.ref_prefetch.restype = i32
         L.ref_topk.argtypes = [i32, i32, i32, P, P, P]
         L.ref_topk.restype = None
         L.ref_expert_ffn.argtypes = [i32, i32, i32, P, P, i64, P, P]
@@ -101,10 +103,14 @@ class OracleCache:
         self.own = np.full(S, -1, np.int32)
         self.stamp = np.zeros(S, np.uint32)
         self.clock = np.zeros(1, np.uint32)
-        self.stats = np.zeros((L, 5), np.int64)
+        self.stats = np.zeros((L, 8), np.int64)
         self.freq = np.zeros(L * E, np.int64)
+        self.dlast = np.zeros(L * E, np.uint32)
+        self.last_demand = np.zeros(1, np.uint32)
         self.plan_slot = np.zeros(0, np.int32)
         self.plan_expert = np.zeros(0, np.int32)
+        self.fill_slot = np.zeros(0, np.int32)
+        self.fill_expert = np.zeros(0, np.int32)
 
     def admit(self, layer: int, ids, max_fetch: int = -1) -> np.ndarray:
         """One admission step; returns the rewritten ids (slot or -1)."""
@@ -117,8 +123,8 @@ class OracleCache:
         rc = lib().ref_admit(
             self.L, self.E, self.S, self.one_call, self.query_width,
             _p(self.res), _p(self.own), _p(self.stamp), _p(self.clock),
-            _p(self.stats), _p(self.freq), layer, _p(ids), R, max_fetch,
-            _p(ps), _p(pe), _p(nm),
+            _p(self.stats), _p(self.freq), _p(self.dlast), _p(self.last_demand),
+            layer, _p(ids), R, max_fetch, _p(ps), _p(pe), _p(nm),
         )
         if rc != 0:
             raise ValueError("oracle admission rejected its arguments")
@@ -126,10 +132,29 @@ class OracleCache:
         self.plan_expert = pe[: nm[0]].copy()
         return ids
 
+    def prefetch(self, layer: int, ids):
+        """One look-ahead prefetch of a layer's predicted experts; the fill
+        plan lands in fill_slot / fill_expert."""
+        ids = np.ascontiguousarray(np.asarray(ids, np.int32).copy())
+        cap = max(self.E, 1)
+        ps = np.zeros(cap, np.int32)
+        pe = np.zeros(cap, np.int32)
+        nf = np.zeros(1, np.int32)
+        rc = lib().ref_prefetch(
+            self.L, self.E, self.S, _p(self.res), _p(self.own), _p(self.stamp), _p(self.clock),
+            _p(self.last_demand), _p(self.stats), _p(self.freq), _p(self.dlast),
+            layer, _p(ids), ids.size, _p(ps), _p(pe), _p(nf),
+        )
+        if rc != 0:
+            raise ValueError("oracle prefetch rejected its arguments")
+        self.fill_slot = ps[: nf[0]].copy()
+        self.fill_expert = pe[: nf[0]].copy()
+
     def state(self) -> dict:
         return dict(
             res=self.res.copy(), own=self.own.copy(), stamp=self.stamp.copy(),
             clock=int(self.clock[0]), stats=self.stats.copy(), freq=self.freq.copy(),
+            dlast=self.dlast.copy(), last_demand=int(self.last_demand[0]),
         )
 
 

@@ -7,7 +7,14 @@ form: the cache is an explicit recency list of slots (least recently used
 first), instead of per-slot clock stamps sorted on demand.  Slots used in
 the same step are appended in ascending slot order, which is the tie rule
 the oracle expresses as "(stamp, slot) ascending".
+
+The look-ahead prefetch (llama.cpp fork PR #126, sections Consumer and
+Eviction guard) is modelled the same way: candidates are read off the
+recency list, skipping slots used since the latest demand step, and the
+guard compares demand heat kept as per-expert counters and last-demand
+ticks.
 """
+from fractions import Fraction
 
 
 class SpecCache:
@@ -26,6 +33,12 @@ class SpecCache:
         self.invalid = [0] * L
         self.hist = [[0] * E for _ in range(L)]
         self.plan = []
+        self.last_seen = {}                  # (layer, expert) -> tick of its last demand
+        self.demand_tick = 0
+        self.pf_calls = [0] * L
+        self.pf_filled = [0] * L
+        self.pf_dropped = [0] * L
+        self.fills = []
 
     def step(self, layer, ids, max_fetch=-1):
         E = self.E
@@ -34,6 +47,8 @@ class SpecCache:
         self.invalid[layer] += len(ids) - len(valid)
         for e in valid:
             self.hist[layer][e] += 1
+            self.last_seen[(layer, e)] = self.tick
+        self.demand_tick = self.tick
 
         if len(ids) <= self.one_call:
             queries = [sorted(set(valid))] if ids else []
@@ -78,6 +93,59 @@ class SpecCache:
         self.recency = [s for s in self.recency if s not in used] + sorted(set(used))
         return [self.where.get((layer, e), -1) if 0 <= e < E else -1 for e in ids]
 
+    def heat(self, key):
+        """Demand frequency and a recency byte that is 255 right after a
+        demand access and falls by one per tick, to 0 (0 if never)."""
+        f = self.hist[key[0]][key[1]]
+        if key not in self.last_seen:
+            return f, 0
+        return f, max(0, 255 - (self.tick - self.last_seen[key]))
+
+    def warm_against(self, resident, predicted):
+        f_r, r_r = self.heat(resident)
+        f_p, r_p = self.heat(predicted)
+        if f_r < 2:
+            return False
+        score_r = Fraction(f_r * 256 + r_r)
+        score_p = Fraction(f_p * 256 + r_p)
+        return score_r > score_p * Fraction(5, 4) + 4
+
+    def prefetch(self, layer, ids):
+        E = self.E
+        self.fills = []
+        if not ids:
+            return
+        self.tick += 1
+        self.pf_calls[layer] += 1
+        want = sorted({e for e in ids if 0 <= e < E})
+        used = [self.where[(layer, e)] for e in want if (layer, e) in self.where]
+        recent = {s for s in range(self.S)
+                  if self.last_tick[s] != 0 and self.last_tick[s] >= self.demand_tick}
+        candidates = [s for s in self.recency if s not in used and s not in recent]
+        self.fills = []
+        k = 0
+        for e in want:
+            if (layer, e) in self.where:
+                continue
+            if k == len(candidates):
+                self.pf_dropped[layer] += 1
+                continue
+            s = candidates[k]
+            if self.holder[s] is not None and self.warm_against(self.holder[s], (layer, e)):
+                self.pf_dropped[layer] += 1
+                continue
+            if self.holder[s] is not None:
+                del self.where[self.holder[s]]
+            self.holder[s] = (layer, e)
+            self.where[(layer, e)] = s
+            used.append(s)
+            self.fills.append((s, e))
+            k += 1
+        self.pf_filled[layer] += len(self.fills)
+        for s in used:
+            self.last_tick[s] = self.tick
+        self.recency = [s for s in self.recency if s not in used] + sorted(set(used))
+
     # The same state in the oracle's array form.
     def arrays(self):
         import numpy as np
@@ -88,8 +156,13 @@ class SpecCache:
             res[l * self.E + e] = s
             own[s] = l * self.E + e
         stats = np.array(
-            [[self.calls[l], self.met[l], self.missed[l], self.overflow[l], self.invalid[l]]
+            [[self.calls[l], self.met[l], self.missed[l], self.overflow[l], self.invalid[l],
+              self.pf_calls[l], self.pf_filled[l], self.pf_dropped[l]]
              for l in range(self.L)], np.int64)
         freq = np.array([c for row in self.hist for c in row], np.int64)
+        dlast = np.zeros(self.L * self.E, np.uint32)
+        for (l, e), t in self.last_seen.items():
+            dlast[l * self.E + e] = t
         return dict(res=res, own=own, stamp=np.array(self.last_tick, np.uint32),
-                    clock=self.tick, stats=stats, freq=freq)
+                    clock=self.tick, stats=stats, freq=freq, dlast=dlast,
+                    last_demand=self.demand_tick)
