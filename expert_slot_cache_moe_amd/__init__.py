@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe_cache.so")
 MOE_OK, MOE_INVALID_ARG, MOE_UNSUPPORTED, MOE_HIP_ERROR, MOE_OUT_OF_MEMORY = range(5)
 MOE_FMT_BF16, MOE_FMT_E2M1, MOE_FMT_MXFP4 = 0, 1, 2
 MOE_MAX_BANKS = 6
-MOE_NUM_STATS = 5
-STAT_NAMES = ("calls", "met", "missed", "overflow", "invalid")
-MOE_STAT_CALLS, MOE_STAT_MET, MOE_STAT_MISSED, MOE_STAT_OVERFLOW, MOE_STAT_INVALID = range(5)
+MOE_NUM_STATS = 8
+STAT_NAMES = ("calls", "met", "missed", "overflow", "invalid", "pf_calls", "pf_filled",
+              "pf_dropped")
+(MOE_STAT_CALLS, MOE_STAT_MET, MOE_STAT_MISSED, MOE_STAT_OVERFLOW, MOE_STAT_INVALID,
+ MOE_STAT_PF_CALLS, MOE_STAT_PF_FILLED, MOE_STAT_PF_DROPPED) = range(8)
 
 
 class MoeError(RuntimeError):
@@ -86,9 +88,12 @@ def lib():
             "moe_shared_expert": (st, [P, i32, P, i32, P, P, i64, P]),
             "moe_layer_decode": (st, [P, i32, P, P, i32, i32, P, i32, P, P, P, P]),
             "moe_cache_stats": (st, [P, i32, P, P]),
-            "moe_cache_read_state": (st, [P, P, P, P, P, P, P, P]),
-            "moe_cache_write_state": (st, [P, P, P, P, C.c_uint32]),
+            "moe_prefetch": (st, [P, i32, P, i32, P]),
+            "moe_prefetch_join": (st, [P, P]),
+            "moe_cache_read_state": (st, [P, P, P, P, P, P, P, P, P, P]),
+            "moe_cache_write_state": (st, [P, P, P, P, C.c_uint32, P, P, P]),
             "moe_cache_read_plan": (st, [P, P, P, i32, P]),
+            "moe_cache_read_fills": (st, [P, P, P, i32, P]),
             "moe_cache_set_timing": (st, [P, i32]),
             "moe_cache_timing": (st, [P, P, P]),
             "moe_record_event": (st, [P, P]),
@@ -139,7 +144,7 @@ def _stream(stream):
 
 
 def _np_ptr(a):
-    return a.ctypes.data_as(C.c_void_p)
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
 
 
 # ---------------------------------------------------------------- helpers
@@ -302,6 +307,15 @@ def moe_layer_decode(cache: Cache, layer: int, x, logits, K: int, out, shared=No
         _dev_ptr(ids_out), _dev_ptr(w_out), _stream(stream)))
 
 
+def moe_prefetch(cache: Cache, layer: int, ids, n=None, stream=None) -> None:
+    n = ids.numel() if n is None else n
+    _check(lib().moe_prefetch(cache.handle, layer, _dev_ptr(ids), n, _stream(stream)))
+
+
+def moe_prefetch_join(cache: Cache, stream=None) -> None:
+    _check(lib().moe_prefetch_join(cache.handle, _stream(stream)))
+
+
 # ---------------------------------------------------------------- inspection
 
 def moe_cache_stats(cache: Cache, layer: int = -1, stream=None) -> np.ndarray:
@@ -319,18 +333,25 @@ def moe_cache_read_state(cache: Cache) -> dict:
     stats = np.zeros((L, MOE_NUM_STATS), np.int64)
     freq = np.zeros(L * E, np.int64)
     order = np.zeros(S, np.int32)
+    dlast = np.zeros(L * E, np.uint32)
+    last_demand = np.zeros(1, np.uint32)
     _check(lib().moe_cache_read_state(cache.handle, _np_ptr(res), _np_ptr(own), _np_ptr(stamp),
-                                      _np_ptr(clock), _np_ptr(stats), _np_ptr(freq), _np_ptr(order)))
+                                      _np_ptr(clock), _np_ptr(stats), _np_ptr(freq), _np_ptr(order),
+                                      _np_ptr(dlast), _np_ptr(last_demand)))
     return dict(res=res, own=own, stamp=stamp, clock=int(clock[0]), stats=stats, freq=freq,
-                order=order)
+                order=order, dlast=dlast, last_demand=int(last_demand[0]))
 
 
-def moe_cache_write_state(cache: Cache, res, own, stamp, clock: int) -> None:
+def moe_cache_write_state(cache: Cache, res, own, stamp, clock: int, freq=None, dlast=None,
+                          last_demand=None) -> None:
     res = np.ascontiguousarray(res, np.int32)
     own = np.ascontiguousarray(own, np.int32)
     stamp = np.ascontiguousarray(stamp, np.uint32)
+    fq = None if freq is None else np.ascontiguousarray(freq, np.int64)
+    dl = None if dlast is None else np.ascontiguousarray(dlast, np.uint32)
+    ld = None if last_demand is None else np.array([last_demand], np.uint32)
     _check(lib().moe_cache_write_state(cache.handle, _np_ptr(res), _np_ptr(own), _np_ptr(stamp),
-                                       clock))
+                                       clock, _np_ptr(fq), _np_ptr(dl), _np_ptr(ld)))
 
 
 def moe_cache_read_plan(cache: Cache):
@@ -339,6 +360,17 @@ def moe_cache_read_plan(cache: Cache):
     pe = np.zeros(cap, np.int32)
     n = np.zeros(1, np.int32)
     _check(lib().moe_cache_read_plan(cache.handle, _np_ptr(ps), _np_ptr(pe), cap, _np_ptr(n)))
+    k = min(int(n[0]), cap)
+    return ps[:k].copy(), pe[:k].copy()
+
+
+def moe_cache_read_fills(cache: Cache):
+    """The fill plan of the last prefetch: (slots, experts)."""
+    cap = cache.E
+    ps = np.zeros(cap, np.int32)
+    pe = np.zeros(cap, np.int32)
+    n = np.zeros(1, np.int32)
+    _check(lib().moe_cache_read_fills(cache.handle, _np_ptr(ps), _np_ptr(pe), cap, _np_ptr(n)))
     k = min(int(n[0]), cap)
     return ps[:k].copy(), pe[:k].copy()
 

@@ -146,8 +146,9 @@ struct moe_cache {
     void *state = nullptr;
     int32_t *res = nullptr, *own = nullptr, *order = nullptr;
     int32_t *plan_slot = nullptr, *plan_expert = nullptr, *n_miss = nullptr;
-    uint32_t *stamp = nullptr, *clock = nullptr;
+    uint32_t *stamp = nullptr, *clock = nullptr, *dlast = nullptr;
     int64_t *stats = nullptr, *freq = nullptr;
+    int32_t *fill_slot = nullptr, *fill_expert = nullptr, *n_fill = nullptr;
     int plan_cap = 0;
     size_t admit_lds = 0;
     // layer workspace
@@ -165,6 +166,11 @@ struct moe_cache {
     // ordering
     hipStream_t side = nullptr;
     hipEvent_t ready = nullptr, done = nullptr;
+    // look-ahead prefetch: its copy stream, fork/join events, and whether a
+    // copy is still to be waited for
+    hipStream_t pf_side = nullptr;
+    hipEvent_t pf_ready = nullptr, pf_done = nullptr;
+    int pf_pending = 0;
     int last_layer = -1;
     int gather_wg = 64;
     // timing
@@ -308,10 +314,22 @@ moe_status_t check_shared(const moe_shared_t *sh, int H, int F, int *Fs) {
 
 // With logits set, the admission computes the top-k of T rows itself
 // (R = T * K) and writes the weights to w.
+// Orders `s` after the copy of a pending prefetch.
+moe_status_t join_prefetch(moe_cache *c, hipStream_t s) {
+    if (!c->pf_pending) return MOE_OK;
+    HIP_TRY(hipStreamWaitEvent(s, c->pf_done, 0), "wait for the prefetch copy");
+    c->pf_pending = 0;
+    return MOE_OK;
+}
+
 moe_status_t launch_admit_checked(moe_cache *c, int layer, int32_t *ids, int R, int max_fetch,
                                   hipStream_t s, int32_t *route_plan = nullptr,
                                   const float *logits = nullptr, int T = 0, int K = 0,
                                   float *w = nullptr) {
+    {
+        moe_status_t js = join_prefetch(c, s);
+        if (js != MOE_OK) return js;
+    }
     AdmitParams p{};
     p.route_plan = route_plan;
     p.logits = logits;
@@ -333,6 +351,7 @@ moe_status_t launch_admit_checked(moe_cache *c, int layer, int32_t *ids, int R, 
     p.clock = c->clock;
     p.stats = c->stats;
     p.freq = c->freq;
+    p.dlast = c->dlast;
     p.plan_slot = c->plan_slot;
     p.plan_expert = c->plan_expert;
     p.n_miss = c->n_miss;
@@ -341,24 +360,31 @@ moe_status_t launch_admit_checked(moe_cache *c, int layer, int32_t *ids, int R, 
     return MOE_OK;
 }
 
-GatherParams gather_params(const moe_cache *c) {
+// The gather of a plan of (slot, expert) rows of one layer.
+GatherParams gather_params(const moe_cache *c, int layer, const int32_t *n, const int32_t *ps,
+                           const int32_t *pe) {
     GatherParams g{};
-    g.n_miss = c->n_miss;
-    g.plan_slot = c->plan_slot;
-    g.plan_expert = c->plan_expert;
+    g.n_miss = n;
+    g.plan_slot = ps;
+    g.plan_expert = pe;
     g.nb = c->nb;
     const int unit = gather_unit_bytes();
     int units = 0;
     for (int b = 0; b < c->nb; ++b) {
         g.unit_start[b] = units;
         units += (int)((c->rb[b] + unit - 1) / unit);
-        g.host[b] = c->host_dev[(size_t)c->last_layer * c->nb + b];
+        g.host[b] = c->host_dev[(size_t)layer * c->nb + b];
         g.slot[b] = static_cast<uint8_t *>(c->d.slot_banks_dev[b]);
         g.rb[b] = c->rb[b];
     }
     g.unit_start[c->nb] = units;
     g.units_per_entry = units;
     return g;
+}
+
+// The miss gather of the last demand admission.
+GatherParams gather_params(const moe_cache *c) {
+    return gather_params(c, c->last_layer, c->n_miss, c->plan_slot, c->plan_expert);
 }
 
 moe_status_t launch_gather_checked(moe_cache *c, hipStream_t s) {
@@ -506,9 +532,13 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     const size_t o_own = off; off += align_up(S * 4);
     const size_t o_stamp = off; off += align_up(S * 4);
     const size_t o_order = off; off += align_up(admit_order_bytes((int)S));
-    const size_t o_clock = off; off += align_up(4);
+    const size_t o_clock = off; off += align_up(8);
     const size_t o_stats = off; off += align_up(L * MOE_NUM_STATS * 8);
     const size_t o_freq = off; off += align_up(L * E * 8);
+    const size_t o_dlast = off; off += align_up(L * E * 4);
+    const size_t o_fs = off; off += align_up(E * 4);
+    const size_t o_fe = off; off += align_up(E * 4);
+    const size_t o_nf = off; off += align_up(4);
     const size_t o_ps = off; off += align_up((size_t)c->plan_cap * 4);
     const size_t o_pe = off; off += align_up((size_t)c->plan_cap * 4);
     const size_t o_nm = off; off += align_up(4);
@@ -527,6 +557,10 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     c->clock = reinterpret_cast<uint32_t *>(base + o_clock);
     c->stats = reinterpret_cast<int64_t *>(base + o_stats);
     c->freq = reinterpret_cast<int64_t *>(base + o_freq);
+    c->dlast = reinterpret_cast<uint32_t *>(base + o_dlast);
+    c->fill_slot = reinterpret_cast<int32_t *>(base + o_fs);
+    c->fill_expert = reinterpret_cast<int32_t *>(base + o_fe);
+    c->n_fill = reinterpret_cast<int32_t *>(base + o_nf);
     c->plan_slot = reinterpret_cast<int32_t *>(base + o_ps);
     c->plan_expert = reinterpret_cast<int32_t *>(base + o_pe);
     c->n_miss = reinterpret_cast<int32_t *>(base + o_nm);
@@ -588,6 +622,13 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     HIP_TRY(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking), "side stream");
     HIP_TRY(hipEventCreateWithFlags(&c->ready, hipEventDisableTiming), "ready event");
     HIP_TRY(hipEventCreateWithFlags(&c->done, hipEventDisableTiming), "done event");
+    HIP_TRY(hipStreamCreateWithFlags(&c->pf_side, hipStreamNonBlocking), "prefetch stream");
+    HIP_TRY(hipEventCreateWithFlags(&c->pf_ready, hipEventDisableTiming), "prefetch event");
+    HIP_TRY(hipEventCreateWithFlags(&c->pf_done, hipEventDisableTiming), "prefetch event");
+    if (prefetch_lds_bytes(d->num_experts, d->num_slots) > (size_t)max_lds)
+        return bail(fail(MOE_UNSUPPORTED, "prefetch needs %zu B of LDS (E=%d, S=%d); device has %d",
+                         prefetch_lds_bytes(d->num_experts, d->num_slots), d->num_experts,
+                         d->num_slots, max_lds));
     c->tev.assign((size_t)d->num_layers * 6, nullptr);
     c->trecorded.assign(d->num_layers, 0);
     HIP_TRY(hipDeviceSynchronize(), "create sync");
@@ -603,6 +644,9 @@ void moe_cache_destroy(moe_cache_t *c) {
     if (c->ready) (void)hipEventDestroy(c->ready);
     if (c->done) (void)hipEventDestroy(c->done);
     if (c->side) (void)hipStreamDestroy(c->side);
+    if (c->pf_ready) (void)hipEventDestroy(c->pf_ready);
+    if (c->pf_done) (void)hipEventDestroy(c->pf_done);
+    if (c->pf_side) (void)hipStreamDestroy(c->pf_side);
     if (c->ws) (void)hipFree(c->ws);
     if (c->state) (void)hipFree(c->state);
     delete c;
@@ -843,6 +887,56 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
     return MOE_OK;
 }
 
+moe_status_t moe_prefetch(moe_cache_t *c, int32_t layer, const int32_t *ids, int32_t n,
+                          void *stream) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    if (layer < 0 || layer >= c->d.num_layers)
+        return fail(MOE_INVALID_ARG, "layer %d outside [0, %d)", layer, c->d.num_layers);
+    if (n < 0 || n > c->d.max_routes)
+        return fail(MOE_INVALID_ARG, "n=%d outside [0, max_routes=%d]", n, c->d.max_routes);
+    if (n == 0) return MOE_OK;   // width 0 leaves everything as it is
+    if (!ids) return fail(MOE_INVALID_ARG, "NULL ids");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the kernel rewrites the fill plan the pending copy reads
+    moe_status_t js = join_prefetch(c, s);
+    if (js != MOE_OK) return js;
+    PrefetchParams p{};
+    p.ids = ids;
+    p.n = n;
+    p.layer = layer;
+    p.E = c->d.num_experts;
+    p.S = c->d.num_slots;
+    p.pairs = admit_order_pairs(p.S) ? 1 : 0;
+    p.res = c->res;
+    p.own = c->own;
+    p.stamp = c->stamp;
+    p.order = c->order;
+    p.clock = c->clock;
+    p.stats = c->stats;
+    p.freq = c->freq;
+    p.dlast = c->dlast;
+    p.fill_slot = c->fill_slot;
+    p.fill_expert = c->fill_expert;
+    p.n_fill = c->n_fill;
+    HIP_TRY(launch_prefetch(p, s), "prefetch launch");
+    if (c->nb == 0) return MOE_OK;
+    // The copy forks off `s`: nothing on `s` waits for it until the next
+    // demand admission or prefetch.
+    HIP_TRY(hipEventRecord(c->pf_ready, s), "record prefetch fork");
+    HIP_TRY(hipStreamWaitEvent(c->pf_side, c->pf_ready, 0), "prefetch stream waits");
+    HIP_TRY(launch_gather(gather_params(c, layer, c->n_fill, c->fill_slot, c->fill_expert),
+                          c->gather_wg, c->pf_side),
+            "prefetch copy launch");
+    HIP_TRY(hipEventRecord(c->pf_done, c->pf_side), "record prefetch done");
+    c->pf_pending = 1;
+    return MOE_OK;
+}
+
+moe_status_t moe_prefetch_join(moe_cache_t *c, void *stream) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    return join_prefetch(c, static_cast<hipStream_t>(stream));
+}
+
 moe_status_t moe_cache_stats(moe_cache_t *c, int32_t layer, int64_t *out, void *stream) {
     if (!c || !out) return fail(MOE_INVALID_ARG, "NULL cache or output");
     if (layer < -1 || layer >= c->d.num_layers) return fail(MOE_INVALID_ARG, "layer %d", layer);
@@ -859,7 +953,8 @@ moe_status_t moe_cache_stats(moe_cache_t *c, int32_t layer, int64_t *out, void *
 }
 
 moe_status_t moe_cache_read_state(moe_cache_t *c, int32_t *res, int32_t *own, uint32_t *stamp,
-                                  uint32_t *clock, int64_t *stats, int64_t *freq, int32_t *order) {
+                                  uint32_t *clock, int64_t *stats, int64_t *freq, int32_t *order,
+                                  uint32_t *dlast, uint32_t *last_demand) {
     if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
     const size_t L = c->d.num_layers, E = c->d.num_experts, S = c->d.num_slots;
     HIP_TRY(hipDeviceSynchronize(), "sync");
@@ -869,6 +964,9 @@ moe_status_t moe_cache_read_state(moe_cache_t *c, int32_t *res, int32_t *own, ui
     if (clock) HIP_TRY(hipMemcpy(clock, c->clock, 4, hipMemcpyDeviceToHost), "copy clock");
     if (stats) HIP_TRY(hipMemcpy(stats, c->stats, L * MOE_NUM_STATS * 8, hipMemcpyDeviceToHost), "copy stats");
     if (freq) HIP_TRY(hipMemcpy(freq, c->freq, L * E * 8, hipMemcpyDeviceToHost), "copy freq");
+    if (dlast) HIP_TRY(hipMemcpy(dlast, c->dlast, L * E * 4, hipMemcpyDeviceToHost), "copy dlast");
+    if (last_demand)
+        HIP_TRY(hipMemcpy(last_demand, c->clock + 1, 4, hipMemcpyDeviceToHost), "copy last demand");
     if (order) {
         std::vector<int32_t> img(admit_order_pairs((int)S) ? 2 * S : S);
         HIP_TRY(hipMemcpy(img.data(), c->order, img.size() * 4, hipMemcpyDeviceToHost), "copy order");
@@ -879,7 +977,8 @@ moe_status_t moe_cache_read_state(moe_cache_t *c, int32_t *res, int32_t *own, ui
 }
 
 moe_status_t moe_cache_write_state(moe_cache_t *c, const int32_t *res, const int32_t *own,
-                                   const uint32_t *stamp, uint32_t clock) {
+                                   const uint32_t *stamp, uint32_t clock, const int64_t *freq,
+                                   const uint32_t *dlast, const uint32_t *last_demand) {
     if (!c || !res || !own || !stamp) return fail(MOE_INVALID_ARG, "NULL state");
     const size_t L = c->d.num_layers, E = c->d.num_experts, S = c->d.num_slots;
     for (size_t s = 0; s < S; ++s) {
@@ -890,13 +989,20 @@ moe_status_t moe_cache_write_state(moe_cache_t *c, const int32_t *res, const int
     for (size_t i = 0; i < L * E; ++i) {
         if (res[i] < -1 || res[i] >= (int32_t)S) return fail(MOE_INVALID_ARG, "res[%zu] out of range", i);
         if (res[i] >= 0 && own[res[i]] != (int32_t)i) return fail(MOE_INVALID_ARG, "res/own disagree at %zu", i);
+        if (dlast && dlast[i] > clock) return fail(MOE_INVALID_ARG, "dlast[%zu] > clock", i);
+        if (freq && freq[i] < 0) return fail(MOE_INVALID_ARG, "freq[%zu] < 0", i);
     }
+    if (last_demand && *last_demand > clock) return fail(MOE_INVALID_ARG, "last_demand > clock");
     const std::vector<int32_t> order = order_image((int)S, stamp, own);
     HIP_TRY(hipDeviceSynchronize(), "sync");
     HIP_TRY(hipMemcpy(c->res, res, L * E * 4, hipMemcpyHostToDevice), "write res");
     HIP_TRY(hipMemcpy(c->own, own, S * 4, hipMemcpyHostToDevice), "write own");
     HIP_TRY(hipMemcpy(c->stamp, stamp, S * 4, hipMemcpyHostToDevice), "write stamp");
     HIP_TRY(hipMemcpy(c->clock, &clock, 4, hipMemcpyHostToDevice), "write clock");
+    if (freq) HIP_TRY(hipMemcpy(c->freq, freq, L * E * 8, hipMemcpyHostToDevice), "write freq");
+    if (dlast) HIP_TRY(hipMemcpy(c->dlast, dlast, L * E * 4, hipMemcpyHostToDevice), "write dlast");
+    if (last_demand)
+        HIP_TRY(hipMemcpy(c->clock + 1, last_demand, 4, hipMemcpyHostToDevice), "write last demand");
     HIP_TRY(hipMemcpy(c->order, order.data(), order.size() * 4, hipMemcpyHostToDevice), "write order");
     return MOE_OK;
 }
@@ -911,6 +1017,20 @@ moe_status_t moe_cache_read_plan(moe_cache_t *c, int32_t *ps, int32_t *pe, int32
     if (k > 0) {
         HIP_TRY(hipMemcpy(ps, c->plan_slot, (size_t)k * 4, hipMemcpyDeviceToHost), "copy plan");
         HIP_TRY(hipMemcpy(pe, c->plan_expert, (size_t)k * 4, hipMemcpyDeviceToHost), "copy plan");
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_cache_read_fills(moe_cache_t *c, int32_t *ps, int32_t *pe, int32_t cap, int32_t *n) {
+    if (!c || !n || (cap > 0 && (!ps || !pe))) return fail(MOE_INVALID_ARG, "NULL fill plan output");
+    HIP_TRY(hipDeviceSynchronize(), "sync");
+    int32_t nf = 0;
+    HIP_TRY(hipMemcpy(&nf, c->n_fill, 4, hipMemcpyDeviceToHost), "copy n_fill");
+    *n = nf;
+    const int k = std::min(std::max(cap, 0), nf);
+    if (k > 0) {
+        HIP_TRY(hipMemcpy(ps, c->fill_slot, (size_t)k * 4, hipMemcpyDeviceToHost), "copy fills");
+        HIP_TRY(hipMemcpy(pe, c->fill_expert, (size_t)k * 4, hipMemcpyDeviceToHost), "copy fills");
     }
     return MOE_OK;
 }

@@ -168,9 +168,10 @@ struct AdmitParams {
     uint32_t *stamp;       // [S]
     int32_t *order;        // LRU order, least recently used first: [S] slots, or, when
                            // admit_order_pairs(S), [S] (slot, owner) pairs
-    uint32_t *clock;       // [1]
-    int64_t *stats;        // [L*5]
+    uint32_t *clock;       // [2]: the clock, the clock value of the latest demand step
+    int64_t *stats;        // [L*MOE_NUM_STATS]
     int64_t *freq;         // [L*E]
+    uint32_t *dlast;       // [L*E] clock value of each expert's last demand step
     int32_t *plan_slot;    // [min(max_routes, E)]
     int32_t *plan_expert;
     int32_t *n_miss;       // [1]
@@ -182,6 +183,26 @@ struct AdmitParams {
     const float *logits;
     int32_t T, K;
     float *w_out;
+};
+
+// One look-ahead prefetch: predicted ids of one layer, the admission state,
+// and the fill plan it writes.
+struct PrefetchParams {
+    const int32_t *ids;    // [n]
+    int32_t n;
+    int32_t layer;
+    int32_t E, S;
+    int32_t pairs;         // order holds (slot, owner) pairs
+    int32_t *res, *own;
+    uint32_t *stamp;
+    int32_t *order;
+    uint32_t *clock;       // [2]
+    int64_t *stats;
+    const int64_t *freq;
+    const uint32_t *dlast;
+    int32_t *fill_slot;    // [E]
+    int32_t *fill_expert;  // [E]
+    int32_t *n_fill;       // [1]
 };
 
 struct GatherParams {
@@ -238,6 +259,8 @@ bool admit_fused_topk_supported(int E, int S, int K);
 // Bytes of the LRU order buffer for S slots (padded for whole-vector loads).
 size_t admit_order_bytes(int S);
 bool admit_order_pairs(int S);
+size_t prefetch_lds_bytes(int E, int S);
+hipError_t launch_prefetch(const PrefetchParams &p, hipStream_t s);
 hipError_t launch_gather(const GatherParams &p, int workgroups, hipStream_t s);
 int gather_unit_bytes();
 

@@ -68,4 +68,10 @@ class SlotCacheLayers:
         return make_pool(self.fmt, self.H, self.F, self.E, banks)
 
     def close(self):
-        moe_cache_destroy(self.cache)
+        if self.cache is not None:
+            moe_cache_destroy(self.cache)
+        self.cache = None
+        # drop the pinned host store and the slot banks with the cache
+        self.host = []
+        self.slot_banks = []
+        self.shared = None

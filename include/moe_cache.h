@@ -25,8 +25,12 @@
  *        returns slot ids; one-call width 256; wider steps admitted as
  *        a sorted fixed-length distinct-expert list in 128-wide queries,
  *        no host sync; statistics once per step, histogram per route.
- *   [P4] llama.cpp fork PR #126, "cuda : MoE look-ahead expert prefetch",
- *        section Consumer: expert ids outside [0, n_experts) are ignored.
+ *   [P4] llama.cpp fork PR #126, "cuda : MoE look-ahead expert prefetch
+ *        (PR-A consumer) + LFRU eviction guard", sections Consumer and
+ *        Eviction guard: expert ids outside [0, n_experts) are ignored;
+ *        predicted experts are filled ahead of their layer through the
+ *        same victim order, never into a pinned slot, without a compute
+ *        stream wait; a warm resident is protected by the LFRU guard.
  *
  * Conventions for every entry point:
  *   - Pointers named *_dev are device pointers (hipMalloc / torch cuda
@@ -87,7 +91,10 @@ enum {
     MOE_STAT_MISSED = 2,   /* distinct experts a query found non-resident      */
     MOE_STAT_OVERFLOW = 3, /* misses left without a slot (cap or no victim)    */
     MOE_STAT_INVALID = 4,  /* routes whose id is outside [0, E)                */
-    MOE_NUM_STATS = 5
+    MOE_STAT_PF_CALLS = 5,   /* prefetch calls of width > 0 [P4]               */
+    MOE_STAT_PF_FILLED = 6,  /* predicted experts filled by a prefetch         */
+    MOE_STAT_PF_DROPPED = 7, /* predictions dropped (guard, or no victim)      */
+    MOE_NUM_STATS = 8
 };
 
 typedef struct moe_cache moe_cache_t;
@@ -276,6 +283,41 @@ moe_status_t moe_layer_decode(moe_cache_t *cache, int32_t layer, const void *x_d
                               const moe_shared_t *shared, int32_t max_fetch, void *out_dev,
                               int32_t *ids_out_dev, float *w_out_dev, void *stream);
 
+/* Look-ahead prefetch of a layer's predicted experts [P4 Consumer,
+ * Eviction guard].  ids_dev: int32 [n] predicted expert ids of `layer`;
+ * ids outside [0, E) are ignored, the rest taken once each, ascending.
+ * One clock tick per call of n > 0; n = 0 does nothing at all.
+ *  - A predicted expert already resident is used now (stamped), so no
+ *    fill of the same call evicts it.
+ *  - Victims are the least recently used slots (ties: lower slot id)
+ *    that are not pinned: a slot used at or after the latest demand
+ *    admission (its readers may still run; fills since then may still be
+ *    in flight) is never chosen.
+ *  - Each missing prediction, ascending, looks at the next victim.  Its
+ *    owner is protected when it has at least 2 demand accesses and
+ *    score(owner) > 1.25 score(prediction) + 4, score = demand routes x
+ *    256 + (255 - min(255, clock - last demand step), 0 if never); then
+ *    the prediction is dropped and the next one looks at the same
+ *    victim.  Otherwise the prediction takes the slot.
+ *  - Heat (histogram, last demand step) counts demand admissions only.
+ * On `stream` (the stream of the demand admissions: one writer of the
+ * slot map) one kernel updates the state and writes the fill plan; the
+ * fills' rows are then copied from pinned host memory on the cache's own
+ * prefetch stream, forked from `stream` by an event, so the copy overlaps
+ * whatever `stream` runs next.  The next demand admission of any layer
+ * (moe_admit, moe_layer_decode) first waits for that copy, on the device;
+ * so does the next prefetch, whose kernel reuses the fill plan.  Under
+ * graph capture, call moe_prefetch_join before ending a capture with a
+ * prefetch still pending.  A cache without banks updates the state only.
+ * Errors: MOE_INVALID_ARG (layer outside [0, L), n < 0 or n > max_routes,
+ * null ids with n > 0). */
+moe_status_t moe_prefetch(moe_cache_t *cache, int32_t layer, const int32_t *ids_dev, int32_t n,
+                          void *stream);
+
+/* Makes `stream` wait, on the device, for the copy of the last prefetch,
+ * if one is pending (no-op otherwise). */
+moe_status_t moe_prefetch_join(moe_cache_t *cache, void *stream);
+
 /* ---------------------------------------------------------------- inspection */
 
 /* Copies the layer's statistics (layer = -1: sums over layers) into
@@ -283,25 +325,36 @@ moe_status_t moe_layer_decode(moe_cache_t *cache, int32_t layer, const void *x_d
 moe_status_t moe_cache_stats(moe_cache_t *cache, int32_t layer, int64_t *stats_host, void *stream);
 
 /* Debug snapshot of the admission state into host arrays (any may be
- * NULL): res [L*E], own [S], stamp [S], clock [1], stats [L*5],
- * freq [L*E], order [S] (slots from least to most recently used).
- * Synchronises the device. */
+ * NULL): res [L*E], own [S], stamp [S], clock [1], stats
+ * [L*MOE_NUM_STATS], freq [L*E] (demand routes), order [S] (slots from
+ * least to most recently used), dlast [L*E] (clock of each expert's last
+ * demand step, 0 = never), last_demand [1] (clock of the latest demand
+ * step, 0 = none).  Synchronises the device. */
 moe_status_t moe_cache_read_state(moe_cache_t *cache, int32_t *res_host, int32_t *own_host,
                                   uint32_t *stamp_host, uint32_t *clock_host, int64_t *stats_host,
-                                  int64_t *freq_host, int32_t *order_host);
+                                  int64_t *freq_host, int32_t *order_host, uint32_t *dlast_host,
+                                  uint32_t *last_demand_host);
 
-/* Debug restore of res/own/stamp/clock (stats and histogram are left as
- * they are).  own must be the inverse of res; the LRU order is rebuilt
- * from the stamps.  Synchronises the device.  Errors: MOE_INVALID_ARG if
- * res and own disagree. */
+/* Debug restore of res/own/stamp/clock, and of freq/dlast/last_demand when
+ * given (NULL leaves them, and the statistics, as they are).  own must be
+ * the inverse of res, and no stamp, dlast or last_demand may exceed
+ * clock; the LRU order is rebuilt from the stamps.  Synchronises the
+ * device.  Errors: MOE_INVALID_ARG if these do not hold. */
 moe_status_t moe_cache_write_state(moe_cache_t *cache, const int32_t *res_host,
                                    const int32_t *own_host, const uint32_t *stamp_host,
-                                   uint32_t clock);
+                                   uint32_t clock, const int64_t *freq_host,
+                                   const uint32_t *dlast_host, const uint32_t *last_demand_host);
 
 /* The miss plan of the last admission: up to cap (slot, expert) pairs and
  * its length.  Synchronises the device. */
 moe_status_t moe_cache_read_plan(moe_cache_t *cache, int32_t *plan_slot_host,
                                  int32_t *plan_expert_host, int32_t cap, int32_t *n_miss_host);
+
+/* The fill plan of the last moe_prefetch of width > 0: up to cap (slot,
+ * expert) pairs, ascending expert, and its length.  Synchronises the
+ * device. */
+moe_status_t moe_cache_read_fills(moe_cache_t *cache, int32_t *fill_slot_host,
+                                  int32_t *fill_expert_host, int32_t cap, int32_t *n_fill_host);
 
 /* Optional timing of the layer step's kernels with HIP events recorded on
  * the stream each kernel runs on (as external event nodes when the step is

@@ -15,9 +15,9 @@ pytestmark = pytest.mark.gpu
 def _same(gc, oc, check_plan=True):
     st = m.moe_cache_read_state(gc)
     o = oc.state()
-    for k in ("res", "own", "stamp", "stats", "freq"):
+    for k in ("res", "own", "stamp", "stats", "freq", "dlast"):
         np.testing.assert_array_equal(st[k].reshape(o[k].shape), o[k], err_msg=k)
-    assert st["clock"] == o["clock"]
+    assert st["clock"] == o["clock"] and st["last_demand"] == o["last_demand"]
     # the LRU order array is the slots sorted by (stamp, slot)
     expect_order = np.lexsort((np.arange(oc.S), o["stamp"]))
     np.testing.assert_array_equal(st["order"], expect_order, err_msg="order")
@@ -81,7 +81,7 @@ def test_wide_step_counts_printed_on_the_pages():
         t = torch.from_numpy(routes.astype(np.int32)).cuda()
         m.moe_admit(gc, 0, t)
         d = m.moe_cache_stats(gc, 0) - before
-        assert d.tolist() == [1, 160, 153, 0, 0]
+        assert d.tolist() == [1, 160, 153, 0, 0, 0, 0, 0]
         st = m.moe_cache_read_state(gc)
         np.testing.assert_array_equal(st["own"][t.cpu().numpy()], routes)
         assert int(st["freq"].sum()) == 7 + 300

@@ -7,6 +7,8 @@ equal the oracle's admission bit for bit, their router weights match, and
 their outputs match the oracle within the tolerance, the oracle reading
 each routed expert's own host rows (so the gathered slot bytes are checked
 too)."""
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -75,3 +77,9 @@ def test_full_size_decode_matches_oracle():
         assert misses > 0                    # the checked tokens do fetch
     finally:
         lay.close()
+        # hand the 60 GB of pinned host memory back, so later tests can pin
+        del lay
+        gc.collect()
+        torch.cuda.synchronize()
+        if hasattr(torch._C, "_host_emptyCache"):
+            torch._C._host_emptyCache()
