@@ -255,6 +255,61 @@ def admission_benchmark(torch, m, W, replays=40, layers=48):
     return res
 
 
+# Look-ahead prefetch: accuracies of the synthetic next-layer predictor.
+LOOKAHEAD_ACCURACY = (1.0, 0.5)
+
+
+def lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok, seed=0):
+    """The timed tokens again, from the cache state they started from, with
+    each layer step followed by a look-ahead prefetch of the next layer's
+    predicted experts: the true top-8 of that layer's logits, each replaced
+    by a uniformly drawn expert with probability 1 - accuracy.  The whole
+    token is one graph; the prefetch copies fork to the cache's prefetch
+    stream and join at the next layer's admission."""
+    stream = torch.cuda.Stream()
+    x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
+    pr_st = torch.empty((L, K), dtype=torch.int32, device="cuda")
+    out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for l in range(L):
+            lay.decode(l, x_st[l], lg_st[l], K, out[l], stream=stream)
+            if l + 1 < L:
+                m.moe_prefetch(lay.cache, l + 1, pr_st[l + 1], stream=stream)
+        m.moe_prefetch_join(lay.cache, stream)
+    true_ids = torch.topk(lg_all[:, :, 0, :], K, dim=-1).indices.to(torch.int32)
+    res = []
+    for acc in LOOKAHEAD_ACCURACY:
+        rng = np.random.default_rng([seed, int(round(acc * 1000))])
+        keep = torch.from_numpy(rng.random((n_tok, L, K)) < acc).cuda()
+        rnd = torch.from_numpy(rng.integers(0, E, (n_tok, L, K)).astype(np.int32)).cuda()
+        pred = torch.where(keep, true_ids, rnd)
+        m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"],
+                                freq=snap["freq"], dlast=snap["dlast"],
+                                last_demand=snap["last_demand"])
+        st0 = m.moe_cache_stats(lay.cache)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(first, n_tok):
+            x_st.copy_(x_all[t])
+            lg_st.copy_(lg_all[t])
+            pr_st.copy_(pred[t])
+            graph.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        d = m.moe_cache_stats(lay.cache) - st0
+        n = n_tok - first
+        res.append({"predictor_accuracy": acc,
+                    "value": round(L * n / dt, 1),
+                    "ms_per_step": round(dt / n * 1000.0, 4),
+                    "demand_fetches_per_token": round(float(d[m.MOE_STAT_MISSED] - d[m.MOE_STAT_OVERFLOW]) / n, 2),
+                    "prefetch_fills_per_token": round(float(d[m.MOE_STAT_PF_FILLED]) / n, 2),
+                    "prefetch_drops_per_token": round(float(d[m.MOE_STAT_PF_DROPPED]) / n, 2)})
+        log(f"[bench] look-ahead, accuracy {acc}: {res[-1]}")
+    return res
+
+
 def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
     """The oracle, single-threaded, on tokens [warm, warm + sample) of the
     same trace after replaying the first `warm` tokens' admissions and
@@ -307,7 +362,8 @@ def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
 
 DECODE_KERNELS = ("admit_fast_kernel", "admit_kernel", "topk_kernel", "stage1_kernel", "stage2_kernel",
                   "gather_kernel", "up_kernel", "down_d_kernel", "down_fused_kernel",
-                  "group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "combine_kernel")
+                  "group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "combine_kernel",
+                  "prefetch_kernel")
 
 
 def _short(name: str) -> str:
@@ -399,7 +455,9 @@ def summarize_trace(csv_path, log_path):
       f"events), an instrumented pass over the same {log['steps']} tokens from the same cache state "
       f"(HIP events captured around each layer's launches), {log['layers']} layer steps per token, "
       f"then the routed-GEMV phase ({log['gemv_calls']} moe_routed_decode calls over resident slots, "
-      f"the last {log['gemv_timed_calls']} timed) and the admission-only benchmark.\n")
+      f"the last {log['gemv_timed_calls']} timed), the admission-only benchmark"
+      + (", and the look-ahead runs (the timed tokens again per predictor accuracy)"
+         if (line.get("lookahead") if (line := log.get("line", {})) else None) else "") + ".\n")
     stats = csv_path.replace("kernel_trace.csv", "kernel_stats.csv")
     if stats != csv_path and os.path.exists(stats):
         import csv
@@ -438,6 +496,23 @@ def summarize_trace(csv_path, log_path):
         p(f"| routed GEMV, {name}: group_count + up_mfma + down_mfma + combine ({parts}) | {len(wc)} | "
           f"{tot.mean():.2f} | {wl.get(name, {}).get('us_per_call')} |")
     p("")
+    pf = [d["us"] for d in disp if d["k"] == "prefetch_kernel"]
+    if pf:
+        pg = [d["us"] for d in disp if d["k"] == "gather_kernel"]
+        p("## Look-ahead runs (each layer step followed by a prefetch of the next layer)\n")
+        p("| launch | launches | rocprofv3 mean µs | max µs |")
+        p("|---|---|---|---|")
+        p(f"| prefetch_kernel (victims, LFRU guard, fill plan) | {len(pf)} | {np.mean(pf):.2f} | "
+          f"{np.max(pf):.2f} |")
+        if pg:
+            p(f"| gather_kernel on the prefetch stream (copies of the fills) | {len(pg)} | "
+              f"{np.mean(pg):.2f} | {np.max(pg):.2f} |")
+        for r in line.get("lookahead") or []:
+            p(f"\nPredictor accuracy {r['predictor_accuracy']}: {r['value']} layer-steps/s "
+              f"({r['ms_per_step']} ms per token), {r['demand_fetches_per_token']} demand fetches, "
+              f"{r['prefetch_fills_per_token']} prefetch fills and {r['prefetch_drops_per_token']} "
+              "drops per token.")
+        p("")
     p("The roofline interval is read between event-record nodes captured around the launch in the "
       f"graph ({rl.get('avg_launch_us_events')} µs); the nodes add their own processing to it, "
       f"which an empty pair of nodes recorded before every layer step measures "
@@ -527,6 +602,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-admission", action="store_true")
     ap.add_argument("--no-wide", action="store_true", help="skip the wide-step routed GEMV shapes")
+    ap.add_argument("--no-lookahead", action="store_true", help="skip the look-ahead prefetch runs")
     ap.add_argument("--cpu-sample-tokens", type=int, default=6)
     ap.add_argument("--overlap", type=int, default=2,
                     help="layer-step schedule passed to the cache (0 serial, 1 side-stream "
@@ -714,6 +790,7 @@ def main():
         del a, b
     wide = None if args.no_wide else wide_gemv_benchmark(torch, m)
     adm = None if args.no_admission else admission_benchmark(torch, m, W)
+    look = None if args.no_lookahead else lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, W_, n_tok)
     lay.close()
     del lay
     cpu = None
@@ -764,6 +841,7 @@ def main():
                           "d2d_copy_same_bytes_gbs": round(d2d_gbs, 1)},
         "admission_us": adm,
         "routed_gemv_wide": wide,
+        "lookahead": look,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
