@@ -80,6 +80,7 @@ def lib():
             "moe_cache_create": (st, [P, P]),
             "moe_cache_destroy": (None, [P]),
             "moe_cache_pool": (st, [P, P]),
+            "moe_cache_set_schedule": (st, [P, i32]),
             "moe_topk": (st, [P, i32, i32, i32, P, P, P]),
             "moe_admit": (st, [P, i32, P, i32, i32, P]),
             "moe_gather_misses": (st, [P, P]),
@@ -237,6 +238,10 @@ def moe_cache_destroy(cache: Cache) -> None:
     if cache.handle:
         lib().moe_cache_destroy(cache.handle)
         cache.handle = None
+
+
+def moe_cache_set_schedule(cache: Cache, overlap: int) -> None:
+    _check(lib().moe_cache_set_schedule(cache.handle, overlap))
 
 
 def moe_cache_pool(cache: Cache) -> moe_pool_t:

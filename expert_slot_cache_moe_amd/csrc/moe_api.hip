@@ -220,18 +220,27 @@ moe_status_t pool_view_of(const moe_pool_t *pool, PoolView &pv) {
 }
 
 // The routed experts + combine on one stream (no argument checks).
+// The routed experts and the combine.  `join`, if given, is waited for on
+// `s` right before the launch that adds `addend` (the shared term another
+// stream produces).
 hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t *idx,
                            const float *w, int T, int K, const float *addend, uint16_t *out,
-                           uint8_t *ws, hipStream_t s) {
-    if (T == 0) return hipSuccess;
+                           uint8_t *ws, hipStream_t s, hipEvent_t join = nullptr) {
+    if (T == 0) return join ? hipStreamWaitEvent(s, join, 0) : hipSuccess;
     const RoutedWs L = routed_ws(pv.H, pv.F, T, K);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     const int n = T * K;
+    auto wait_join = [&]() { return join ? hipStreamWaitEvent(s, join, 0) : hipSuccess; };
     if (T == 1 && stage_supported(pv.fmt, pv.H, pv.F)) {
         // the decode schedule's two stage launches, with no gather and no
         // shared expert (identical arithmetic to the kernels below)
+        hipError_t e = launch_stages(GatherParams{}, 0, nullptr, pv, idx, w, nullptr, K, x, h, nullptr,
+                                     nullptr, nullptr, nullptr, addend, out, 1, s);
+        hipError_t je = wait_join();
+        if (e != hipSuccess) return e;
+        if (je != hipSuccess) return je;
         return launch_stages(GatherParams{}, 0, nullptr, pv, idx, w, nullptr, K, x, h, nullptr, nullptr,
-                             nullptr, nullptr, addend, out, 3, s);
+                             nullptr, nullptr, addend, out, 2, s);
     }
     if (T == 1) {
         Items it{};
@@ -240,7 +249,9 @@ hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t 
         it.n = n;
         it.idx = idx;
         hipError_t e = launch_up(pv, it, n, x, h, nullptr, nullptr, s);
+        hipError_t je = wait_join();
         if (e != hipSuccess) return e;
+        if (je != hipSuccess) return je;
         return launch_down_fused(pv, idx, w, T, K, h, addend, nullptr, nullptr, out, s);
     }
     int32_t *ng = reinterpret_cast<int32_t *>(ws + L.ngroups);
@@ -252,7 +263,10 @@ hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t 
     hipError_t e = group_count_supported(pv.num_rows, n)
                        ? launch_group_count(idx, n, pv.num_rows, ng, grow, gstart, gcount, groutes, s)
                        : launch_group_routes(idx, n, pv.num_rows, ng, grow, gstart, gcount, groutes, s);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+        (void)wait_join();
+        return e;
+    }
     Items it{};
     it.mode = ITEM_GROUP;
     it.K = K;
@@ -265,14 +279,14 @@ hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t 
     const int max_items = std::min(n, pv.num_rows);
     if (group_mfma_supported(pv.fmt, pv.H, pv.F)) {
         e = launch_up_mfma(pv, it, max_items, x, h, s);
-        if (e != hipSuccess) return e;
-        e = launch_down_mfma(pv, it, max_items, h, d, s);
+        if (e == hipSuccess) e = launch_down_mfma(pv, it, max_items, h, d, s);
     } else {
         e = launch_up(pv, it, max_items, x, h, nullptr, nullptr, s);
-        if (e != hipSuccess) return e;
-        e = launch_down_to_d(pv, it, max_items, h, d, nullptr, s);
+        if (e == hipSuccess) e = launch_down_to_d(pv, it, max_items, h, d, nullptr, s);
     }
+    hipError_t je = wait_join();
     if (e != hipSuccess) return e;
+    if (je != hipSuccess) return je;
     return launch_combine(idx, w, T, K, pv.H, pv.num_rows, d, addend, out, s);
 }
 
@@ -458,8 +472,8 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     if (d->one_call_width < 1 || d->query_width < 1)
         return fail(MOE_INVALID_ARG, "one_call_width and query_width must be >= 1");
     if (d->max_routes < 1) return fail(MOE_INVALID_ARG, "max_routes must be >= 1");
-    if (d->overlap < 0 || d->overlap > 2)
-        return fail(MOE_INVALID_ARG, "overlap must be 0, 1 or 2, got %d", d->overlap);
+    if (d->overlap < 0 || d->overlap > 3)
+        return fail(MOE_INVALID_ARG, "overlap must be 0, 1, 2 or 3, got %d", d->overlap);
     if (d->max_tokens < 0 || d->max_top_k < 0)
         return fail(MOE_INVALID_ARG, "max_tokens/max_top_k must be >= 0");
     if (d->gather_workgroups < 0) return fail(MOE_INVALID_ARG, "gather_workgroups < 0");
@@ -636,6 +650,14 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
     return MOE_OK;
 }
 
+moe_status_t moe_cache_set_schedule(moe_cache_t *c, int32_t overlap) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    if (overlap < 0 || overlap > 3)
+        return fail(MOE_INVALID_ARG, "overlap must be 0, 1, 2 or 3, got %d", overlap);
+    c->d.overlap = overlap;
+    return MOE_OK;
+}
+
 void moe_cache_destroy(moe_cache_t *c) {
     if (!c) return;
     (void)hipDeviceSynchronize();
@@ -780,6 +802,44 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
     // Few token rows: the top-k runs inside the admission kernel.
     const bool fused_topk =
         T <= kFusedTopkRows && admit_fused_topk_supported(c->d.num_experts, c->d.num_slots, K);
+    if (c->d.overlap == 3 && shared && T > 0) {
+        // The #678 split: the shared expert and its gate on the side stream,
+        // forked here; top-k, admission, gather and the routed experts on the
+        // compute stream, joined right before the launch that adds the shared
+        // term.  Every exit after the fork joins, so no side work outlives
+        // the step.
+        const uint16_t *xb = static_cast<const uint16_t *>(x);
+        HIP_TRY(hipEventRecord(c->ready, s), "record ready");
+        HIP_TRY(hipStreamWaitEvent(c->side, c->ready, 0), "side waits ready");
+        hipError_t e = shared_sequence(shared, c->d.hidden, Fs, xb, T, c->ws_addend, c->ws_shared, c->side);
+        const hipError_t re = hipEventRecord(c->done, c->side);
+        auto joined = [&](moe_status_t r) {
+            (void)hipStreamWaitEvent(s, c->done, 0);
+            return r;
+        };
+        if (e != hipSuccess || re != hipSuccess)
+            return joined(hip_fail(e != hipSuccess ? e : re, "shared expert on the side stream"));
+        auto mark = [&](int i) { return timing ? record_timing(tev[i], s) : hipSuccess; };
+        if (!fused_topk && (e = launch_topk(logits, T, c->d.num_experts, K, ids, w, s)) != hipSuccess)
+            return joined(hip_fail(e, "top-k launch"));
+        if ((e = mark(0)) != hipSuccess) return joined(hip_fail(e, "timing"));
+        moe_status_t st = fused_topk
+                              ? launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan,
+                                                     logits, T, K, w)
+                              : launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan);
+        if (st != MOE_OK) return joined(st);
+        if ((e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess) return joined(hip_fail(e, "timing"));
+        if ((st = launch_gather_checked(c, s)) != MOE_OK) return joined(st);
+        if ((e = mark(3)) != hipSuccess || (e = mark(4)) != hipSuccess) return joined(hip_fail(e, "timing"));
+        e = routed_sequence(slot_pool_view(c), xb, ids, w, T, K, c->ws_addend,
+                            static_cast<uint16_t *>(out), c->ws_routed, s, c->done);
+        if (e != hipSuccess) return hip_fail(e, "routed launch");   // joined inside
+        if (timing) {
+            HIP_TRY(record_timing(tev[5], s), "timing");
+            c->trecorded[layer] = 1;
+        }
+        return MOE_OK;
+    }
     if (!fused_topk) HIP_TRY(launch_topk(logits, T, c->d.num_experts, K, ids, w, s), "top-k launch");
     if (timing) HIP_TRY(record_timing(tev[0], s), "timing");
     moe_status_t st = fused_topk ? launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan,

@@ -121,8 +121,16 @@ typedef struct {
                                     as disjoint workgroups of one kernel, the
                                     down projections and combine in a second
                                     (single-token bf16 steps; other steps run
-                                    as 0).  Results are bit-identical in all
-                                    three.  Other values are an error. */
+                                    as 0);
+                                 3: the split of the #678 variant [P2 "What we
+                                    changed", difference from #678]: the
+                                    shared expert and its gate on the side
+                                    stream, forked at the start of the step;
+                                    the gather and every routed launch on the
+                                    compute stream, joined before the launch
+                                    that adds the shared term.
+                                 Results are bit-identical in all four.
+                                 Other values are an error. */
     int32_t num_banks;        /* 0 (admission only: no gather, no experts) or
                                  the format's bank count (2 or 6)                */
     int32_t gather_workgroups;/* workgroups of the gather kernel; 0 = default   */
@@ -179,9 +187,14 @@ moe_status_t moe_query_widths(int32_t R, int32_t E, int32_t one_call_width, int3
  * layer workspace), creates its side stream and its ready/done events --
  * before any capture -- and leaves every slot empty.  Uses the current
  * device.  Errors: MOE_INVALID_ARG (bad sizes, null or unaligned
- * pointers, overlap not 0/1), MOE_UNSUPPORTED (shapes the kernels lack,
+ * pointers, overlap outside 0..3), MOE_UNSUPPORTED (shapes the kernels lack,
  * LDS overflow), MOE_OUT_OF_MEMORY, MOE_HIP_ERROR. */
 moe_status_t moe_cache_create(const moe_cache_desc_t *desc, moe_cache_t **out);
+
+/* Switches the schedule of later moe_layer_decode calls (the `overlap`
+ * field of the description; graphs captured before keep theirs).  Errors:
+ * MOE_INVALID_ARG (overlap outside 0..3). */
+moe_status_t moe_cache_set_schedule(moe_cache_t *cache, int32_t overlap);
 
 /* Synchronises the cache's streams and frees what create allocated. */
 void moe_cache_destroy(moe_cache_t *cache);

@@ -50,7 +50,7 @@ def test_bank_row_bytes():
         m.moe_bank_row_bytes(7, 64, 64)
 
 
-@pytest.mark.parametrize("bad", [dict(overlap=3), dict(overlap=-1), dict(num_slots=0), dict(query_width=0),
+@pytest.mark.parametrize("bad", [dict(overlap=4), dict(overlap=-1), dict(num_slots=0), dict(query_width=0),
                                  dict(max_routes=0), dict(num_layers=0)])
 def test_create_rejects_bad_descriptions_before_touching_the_gpu(bad):
     kw = dict(num_layers=1, num_experts=8, num_slots=4, overlap=1, query_width=128, max_routes=8)

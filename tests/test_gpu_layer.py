@@ -309,7 +309,7 @@ def test_wide_step_cached_equals_streamed_bit_for_bit(fmt, H, F, E, S, T, K, one
         lay.close()
 
 
-@pytest.mark.parametrize("overlap", [1, 2])
+@pytest.mark.parametrize("overlap", [1, 2, 3])
 def test_graph_replay_matches_eager_over_changing_routes(overlap):
     """A whole token (3 layers) captured as one graph and replayed over 40
     steps with changing routes equals the same steps run eagerly."""
@@ -412,11 +412,11 @@ def test_timed_staged_steps_match_untimed_ones():
 
 
 def test_all_schedules_are_bit_identical():
-    """Serial, two-stream and single-stream staged steps give the same bytes
-    at every step (the staged one rebuilds fetched experts' gate/up dots
-    inside the gather with the same reduction trees)."""
+    """Serial, two-stream, single-stream staged and shared-on-the-side-stream
+    steps give the same bytes at every step (the staged one rebuilds fetched
+    experts' gate/up dots inside the gather with the same reduction trees)."""
     L, E, S, H = 2, 32, 12, 64
-    lays = [_tiny_layers(ov, True, seed=9, L=L, E=E, S=S)[0] for ov in (0, 1, 2)]
+    lays = [_tiny_layers(ov, True, seed=9, L=L, E=E, S=S)[0] for ov in (0, 1, 2, 3)]
     g = W.rng(9, "serial")
     outs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in lays]
     try:
@@ -427,7 +427,7 @@ def test_all_schedules_are_bit_identical():
                 for lay, o in zip(lays, outs):
                     lay.decode(l, x, lg, 2, o)
                 torch.cuda.synchronize()
-                assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]), (t, l)
+                assert all(torch.equal(outs[0], o) for o in outs[1:]), (t, l)
         assert m.moe_cache_stats(lays[0].cache)[2] > 20      # the trace does miss
     finally:
         for lay in lays:
@@ -444,7 +444,7 @@ def test_shared_expert_decode_shape_staged():
     sh = [(W.normal_bf16(g, 2 * F * H, 0.02), W.normal_bf16(g, H * F, 0.02), W.normal_bf16(g, H, 0.02))
           for _ in range(L)]
     lays = [SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, host_rows=host, shared=sh,
-                            max_tokens=1, max_top_k=K, overlap=ov) for ov in (2, 0)]
+                            max_tokens=1, max_top_k=K, overlap=ov) for ov in (2, 0, 3)]
     oc = oracle.OracleCache(L, E, S)
     tr = W.DecodeTrace(15, L, E, K, stay=0.5)
     outs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in lays]
@@ -457,7 +457,7 @@ def test_shared_expert_decode_shape_staged():
                 for lay, o in zip(lays, outs):
                     lay.decode(l, _dev_u16(x), torch.from_numpy(lgs[l:l + 1]).cuda(), K, o)
                 torch.cuda.synchronize()
-                assert torch.equal(outs[0], outs[1]), (t, l)
+                assert all(torch.equal(outs[0], o) for o in outs[1:]), (t, l)
                 ref, _, _ = _oracle_layer(oc, host, sh, l, x, lgs[l:l + 1], K, 0, H, F)
                 _close(_bf16_to_f64(outs[0]), ref, f"token {t} layer {l}")
         assert m.moe_cache_stats(lays[0].cache)[2] > 40
@@ -493,3 +493,36 @@ def test_fused_topk_in_the_layer_step_handles_ties_and_nan():
             _close(_bf16_to_f64(out), ref, f"step {step}")
     finally:
         lay.close()
+
+
+@pytest.mark.parametrize("T,K,fmt", [(1, 2, 0), (5, 2, 0), (24, 2, 0), (3, 3, 1)])
+def test_shared_on_the_side_stream_equals_serial(T, K, fmt):
+    """The #678 split (shared expert on the side stream, gather and routed
+    experts on the compute stream, joined before the shared term is added)
+    equals the serial schedule bit for bit at one token, small batches
+    (grouped path) and 4-bit weights; switching a cache's schedule with
+    moe_cache_set_schedule gives the same bytes as creating it so."""
+    L, E, S, H, F = 2, 32, 12, 64, 128
+    lays = [_tiny_layers(ov, True, seed=19, fmt=fmt, L=L, E=E, S=S, H=H, F=F, T=T, K=K)[0]
+            for ov in (0, 3, 0)]
+    m.moe_cache_set_schedule(lays[2].cache, 3)
+    g = W.rng(19, "split678", T, fmt)
+    outs = [torch.empty((T, H), dtype=torch.int16, device="cuda") for _ in lays]
+    try:
+        for t in range(12):
+            for l in range(L):
+                x = _dev_u16(W.normal_bf16(g, (T, H)))
+                lg = torch.from_numpy(W.zipf_logits(g, T, E, 0.5)).cuda()
+                for lay, o in zip(lays, outs):
+                    lay.decode(l, x, lg, K, o)
+                torch.cuda.synchronize()
+                assert all(torch.equal(outs[0], o) for o in outs[1:]), (t, l)
+        a, b = (m.moe_cache_read_state(lay.cache) for lay in lays[:2])
+        for k in ("res", "own", "stamp", "stats", "freq", "order"):
+            np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+        assert m.moe_cache_stats(lays[0].cache)[2] > 10
+        with pytest.raises(m.MoeError):
+            m.moe_cache_set_schedule(lays[0].cache, 4)
+    finally:
+        for lay in lays:
+            lay.close()
