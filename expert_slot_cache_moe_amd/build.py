@@ -21,8 +21,17 @@ HIPCC_FLAGS = [
 ]
 
 
+# Host-only C++ (the CPU half of the hybrid decode step), built by the
+# host compiler for x86-64 with AVX2 and FMA.
+CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-pthread", "-mavx2", "-mfma"]
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+
+
+def cpp_sources():
+    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
@@ -45,6 +54,14 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         while len([p for p in procs if p.poll() is None]) >= jobs:
             procs[[p.poll() is None for p in procs].index(True)].wait()
         procs.append(subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True))
+    cxx = os.environ.get("CXX", "g++")
+    for src in cpp_sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = [cxx, *CXX_FLAGS, *inc, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True))
     errs = []
     for p in procs:
         _, err = p.communicate()
@@ -53,7 +70,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if errs:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     tmp = LIB + ".tmp%d" % os.getpid()
-    link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    link = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-pthread", "-o", tmp]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.check_call(link)

@@ -11,8 +11,10 @@
 #include <cstring>
 #include <numeric>
 #include <string>
+#include <functional>
 #include <vector>
 
+#include "cpu_experts.h"
 #include "moe_internal.h"
 
 using namespace moe;
@@ -142,6 +144,7 @@ struct moe_cache {
     int nb = 0;
     int64_t rb[MOE_MAX_BANKS] = {};
     std::vector<const uint8_t *> host_dev;  // [L * nb] device-visible host rows
+    std::vector<const uint8_t *> host_rows; // [L * nb] the same rows, host addresses
     // device state
     void *state = nullptr;
     int32_t *res = nullptr, *own = nullptr, *order = nullptr;
@@ -173,6 +176,15 @@ struct moe_cache {
     int pf_pending = 0;
     int last_layer = -1;
     int gather_wg = 64;
+    // hybrid decode: the host-core expert pool and its pinned staging
+    // (original expert ids, slot ids, weights, x, the CPU partial)
+    CpuExperts *cpu = nullptr;
+    void *hyb_host = nullptr;
+    int32_t *h_experts = nullptr, *h_slots = nullptr;
+    float *h_w = nullptr, *h_partial = nullptr, *d_partial = nullptr;
+    uint16_t *h_x = nullptr;
+    std::vector<int32_t> cpu_ids;
+    hipEvent_t hyb_ready = nullptr;
     // timing
     int timing = 0;
     std::vector<hipEvent_t> tev;     // [L * 6]: admission, gather, routed start/end
@@ -220,17 +232,20 @@ moe_status_t pool_view_of(const moe_pool_t *pool, PoolView &pv) {
 }
 
 // The routed experts + combine on one stream (no argument checks).
-// The routed experts and the combine.  `join`, if given, is waited for on
-// `s` right before the launch that adds `addend` (the shared term another
-// stream produces).
+// Work issued right before the launch that adds the fp32 term: a wait for
+// the stream producing it, or the hybrid step's CPU half.  Always called,
+// also after a failed launch, so a fork it closes is always joined.
+using BeforeAddend = std::function<hipError_t()>;
+
+// The routed experts and the combine.
 hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t *idx,
                            const float *w, int T, int K, const float *addend, uint16_t *out,
-                           uint8_t *ws, hipStream_t s, hipEvent_t join = nullptr) {
-    if (T == 0) return join ? hipStreamWaitEvent(s, join, 0) : hipSuccess;
+                           uint8_t *ws, hipStream_t s, const BeforeAddend *before = nullptr) {
+    auto wait_join = [&]() { return before ? (*before)() : hipSuccess; };
+    if (T == 0) return wait_join();
     const RoutedWs L = routed_ws(pv.H, pv.F, T, K);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     const int n = T * K;
-    auto wait_join = [&]() { return join ? hipStreamWaitEvent(s, join, 0) : hipSuccess; };
     if (T == 1 && stage_supported(pv.fmt, pv.H, pv.F)) {
         // the decode schedule's two stage launches, with no gather and no
         // shared expert (identical arithmetic to the kernels below)
@@ -510,6 +525,7 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
                 return bail(fail(MOE_INVALID_ARG, "slot bank %d is NULL or not 16-byte aligned", b));
         }
         c->host_dev.resize((size_t)d->num_layers * c->nb);
+        c->host_rows.resize((size_t)d->num_layers * c->nb);
         for (int l = 0; l < d->num_layers; ++l)
             for (int b = 0; b < c->nb; ++b) {
                 void *hp = const_cast<void *>(d->host_banks_host[(size_t)l * c->nb + b]);
@@ -526,6 +542,7 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
                                      l, b));
                 }
                 c->host_dev[(size_t)l * c->nb + b] = static_cast<const uint8_t *>(dp);
+                c->host_rows[(size_t)l * c->nb + b] = static_cast<const uint8_t *>(hp);
             }
     }
 
@@ -661,6 +678,9 @@ moe_status_t moe_cache_set_schedule(moe_cache_t *c, int32_t overlap) {
 void moe_cache_destroy(moe_cache_t *c) {
     if (!c) return;
     (void)hipDeviceSynchronize();
+    if (c->cpu) cpu_experts_destroy(c->cpu);
+    if (c->hyb_host) (void)hipHostFree(c->hyb_host);
+    if (c->hyb_ready) (void)hipEventDestroy(c->hyb_ready);
     for (hipEvent_t e : c->tev)
         if (e) (void)hipEventDestroy(e);
     if (c->ready) (void)hipEventDestroy(c->ready);
@@ -831,8 +851,9 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
         if ((e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess) return joined(hip_fail(e, "timing"));
         if ((st = launch_gather_checked(c, s)) != MOE_OK) return joined(st);
         if ((e = mark(3)) != hipSuccess || (e = mark(4)) != hipSuccess) return joined(hip_fail(e, "timing"));
+        const BeforeAddend join = [&]() { return hipStreamWaitEvent(s, c->done, 0); };
         e = routed_sequence(slot_pool_view(c), xb, ids, w, T, K, c->ws_addend,
-                            static_cast<uint16_t *>(out), c->ws_routed, s, c->done);
+                            static_cast<uint16_t *>(out), c->ws_routed, s, &join);
         if (e != hipSuccess) return hip_fail(e, "routed launch");   // joined inside
         if (timing) {
             HIP_TRY(record_timing(tev[5], s), "timing");
@@ -995,6 +1016,166 @@ moe_status_t moe_prefetch(moe_cache_t *c, int32_t layer, const int32_t *ids, int
 moe_status_t moe_prefetch_join(moe_cache_t *c, void *stream) {
     if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
     return join_prefetch(c, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_cache_set_cpu_threads(moe_cache_t *c, int32_t threads) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    if (threads < 0 || threads > 1024) return fail(MOE_INVALID_ARG, "threads %d outside [0, 1024]", threads);
+    if (threads > 0) {
+        if (c->nb == 0 || c->d.max_tokens < 1)
+            return fail(MOE_INVALID_ARG, "the hybrid step needs weight banks and max_tokens > 0");
+        if (c->d.weight_format != MOE_FMT_BF16 || c->d.hidden % 16 || c->d.ffn % 16)
+            return fail(MOE_UNSUPPORTED, "the CPU experts take bf16 rows with hidden and ffn multiples of 16");
+    }
+    HIP_TRY(hipDeviceSynchronize(), "sync");
+    if (c->cpu) {
+        cpu_experts_destroy(c->cpu);
+        c->cpu = nullptr;
+    }
+    if (threads == 0) return MOE_OK;
+    if (!c->hyb_host) {
+        const size_t TK = (size_t)c->d.max_tokens * c->d.max_top_k, TH = (size_t)c->d.max_tokens * c->d.hidden;
+        const size_t o_e = 0, o_s = align_up(TK * 4), o_w = o_s + align_up(TK * 4), o_x = o_w + align_up(TK * 4),
+                     o_p = o_x + align_up(TH * 2), total = o_p + align_up(TH * 4);
+        void *hp = nullptr;
+        hipError_t e = hipHostMalloc(&hp, total, hipHostMallocMapped);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(MOE_OUT_OF_MEMORY, "hybrid staging (%zu B pinned): %s", total, hipGetErrorString(e));
+        }
+        c->hyb_host = hp;
+        uint8_t *b = static_cast<uint8_t *>(hp);
+        c->h_experts = reinterpret_cast<int32_t *>(b + o_e);
+        c->h_slots = reinterpret_cast<int32_t *>(b + o_s);
+        c->h_w = reinterpret_cast<float *>(b + o_w);
+        c->h_x = reinterpret_cast<uint16_t *>(b + o_x);
+        c->h_partial = reinterpret_cast<float *>(b + o_p);
+        void *dp = nullptr;
+        HIP_TRY(hipHostGetDevicePointer(&dp, c->h_partial, 0), "map the hybrid partial");
+        c->d_partial = static_cast<float *>(dp);
+        c->cpu_ids.resize(TK);
+        HIP_TRY(hipEventCreateWithFlags(&c->hyb_ready, hipEventDisableTiming), "hybrid event");
+    }
+    c->cpu = cpu_experts_create(threads);
+    return MOE_OK;
+}
+
+moe_status_t moe_cpu_experts(int32_t threads, int32_t T, int32_t K, int32_t H, int32_t F,
+                             const int32_t *experts, const float *w, const void *x,
+                             const void *w13_rows, const void *w2_rows, float *partial) {
+    if (threads < 1 || threads > 1024 || T < 0 || K < 1 || H < 16 || F < 16 || H % 16 || F % 16)
+        return fail(MOE_INVALID_ARG, "bad CPU expert sizes (threads %d, T %d, K %d, H %d, F %d)", threads,
+                    T, K, H, F);
+    if (T == 0) return MOE_OK;
+    if (!experts || !w || !x || !w13_rows || !w2_rows || !partial)
+        return fail(MOE_INVALID_ARG, "NULL CPU expert buffer");
+    CpuRoutes r{};
+    r.T = T;
+    r.K = K;
+    r.H = H;
+    r.F = F;
+    r.expert = experts;
+    r.w = w;
+    r.x = static_cast<const uint16_t *>(x);
+    r.w13 = static_cast<const uint8_t *>(w13_rows);
+    r.w2 = static_cast<const uint8_t *>(w2_rows);
+    r.partial = partial;
+    CpuExperts *p = cpu_experts_create(threads);
+    cpu_experts_run(p, r);
+    cpu_experts_destroy(p);
+    return MOE_OK;
+}
+
+moe_status_t moe_layer_decode_hybrid(moe_cache_t *c, int32_t layer, const void *x, const float *logits,
+                                     int32_t T, int32_t K, const moe_shared_t *shared, int32_t max_fetch,
+                                     void *out, int32_t *ids_out, float *w_out, void *stream) {
+    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
+    if (!c->cpu) return fail(MOE_INVALID_ARG, "no CPU experts: call moe_cache_set_cpu_threads first");
+    if (layer < 0 || layer >= c->d.num_layers)
+        return fail(MOE_INVALID_ARG, "layer %d outside [0, %d)", layer, c->d.num_layers);
+    if (T < 0 || T > c->d.max_tokens) return fail(MOE_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, c->d.max_tokens);
+    if (K < 1 || K > c->d.max_top_k || K > c->d.num_experts)
+        return fail(MOE_INVALID_ARG, "K=%d outside [1, %d]", K, c->d.max_top_k);
+    if (T > 0 && (!x || !logits || !out)) return fail(MOE_INVALID_ARG, "NULL layer buffer");
+    if (T > 0 && !aligned16(x)) return fail(MOE_INVALID_ARG, "x must be 16-byte aligned");
+    int Fs = 0;
+    if (shared) {
+        moe_status_t st = check_shared(shared, c->d.hidden, c->d.ffn, &Fs);
+        if (st != MOE_OK) return st;
+        if (Fs > c->shared_ffn_cap)
+            return fail(MOE_UNSUPPORTED, "shared ffn %d > the cache's workspace width %d", Fs, c->shared_ffn_cap);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        HIP_TRY(hipStreamIsCapturing(s, &cs), "capture status");
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(MOE_INVALID_ARG, "the hybrid step waits on the host and cannot be captured");
+    }
+    const int H = c->d.hidden, E = c->d.num_experts, R = T * K;
+    int32_t *ids = ids_out ? ids_out : c->ws_ids;
+    float *w = w_out ? w_out : c->ws_w;
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    const size_t lb = (size_t)layer * c->nb;
+
+    // Cache decision: top-k, the original ids and x to the host, admission
+    // (capped fetch), the rewritten ids to the host.
+    HIP_TRY(launch_topk(logits, T, E, K, ids, w, s), "top-k launch");
+    HIP_TRY(hipMemcpyAsync(c->h_experts, ids, (size_t)R * 4, hipMemcpyDeviceToHost, s), "ids to host");
+    HIP_TRY(hipMemcpyAsync(c->h_w, w, (size_t)R * 4, hipMemcpyDeviceToHost, s), "weights to host");
+    HIP_TRY(hipMemcpyAsync(c->h_x, x, (size_t)T * H * 2, hipMemcpyDeviceToHost, s), "x to host");
+    moe_status_t st = launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan);
+    if (st != MOE_OK) return st;
+    HIP_TRY(hipMemcpyAsync(c->h_slots, ids, (size_t)R * 4, hipMemcpyDeviceToHost, s), "slots to host");
+    HIP_TRY(hipEventRecord(c->hyb_ready, s), "record hybrid ready");
+
+    // The CPU half: waits for the decision, then runs the -1 routes with a
+    // valid expert id on host cores into the pinned partial.  Folding the
+    // partial into the fp32 term is issued right before the combine.
+    auto cpu_half = [&]() -> hipError_t {
+        hipError_t e = hipEventSynchronize(c->hyb_ready);
+        if (e != hipSuccess) return e;
+        for (int i = 0; i < R; ++i) {
+            const int ex = c->h_experts[i];
+            c->cpu_ids[i] = (c->h_slots[i] < 0 && ex >= 0 && ex < E) ? ex : -1;
+        }
+        CpuRoutes r{};
+        r.T = T;
+        r.K = K;
+        r.H = H;
+        r.F = c->d.ffn;
+        r.expert = c->cpu_ids.data();
+        r.w = c->h_w;
+        r.x = c->h_x;
+        r.w13 = c->host_rows[lb + 0];
+        r.w2 = c->host_rows[lb + 1];
+        r.partial = c->h_partial;
+        cpu_experts_run(c->cpu, r);
+        return hipSuccess;
+    };
+    auto fold = [&]() { return launch_hybrid_add(c->ws_addend, c->d_partial, T * H, shared ? 1 : 0, s); };
+    const bool serial = c->d.overlap == 0;
+    if (serial) {
+        // the debug order: the CPU wait before the GPU work
+        hipError_t e = cpu_half();
+        if (e != hipSuccess) return hip_fail(e, "hybrid CPU half");
+    }
+    // GPU half: the capped gather, the shared term, the GPU routes; the CPU
+    // partial joins the fp32 term right before the combine adds it.
+    st = launch_gather_checked(c, s);
+    if (st != MOE_OK) return st;
+    if (shared) {
+        hipError_t e = shared_sequence(shared, H, Fs, xb, T, c->ws_addend, c->ws_shared, s);
+        if (e != hipSuccess) return hip_fail(e, "shared launch");
+    }
+    const BeforeAddend cpu_join = [&]() {
+        hipError_t e = serial ? hipSuccess : cpu_half();
+        return e != hipSuccess ? e : fold();
+    };
+    HIP_TRY(routed_sequence(slot_pool_view(c), xb, ids, w, T, K, c->ws_addend, static_cast<uint16_t *>(out),
+                            c->ws_routed, s, &cpu_join),
+            "hybrid routed launch");
+    return MOE_OK;
 }
 
 moe_status_t moe_cache_stats(moe_cache_t *c, int32_t layer, int64_t *out, void *stream) {

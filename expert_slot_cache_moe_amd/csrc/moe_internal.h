@@ -259,6 +259,10 @@ bool admit_fused_topk_supported(int E, int S, int K);
 // Bytes of the LRU order buffer for S slots (padded for whole-vector loads).
 size_t admit_order_bytes(int S);
 bool admit_order_pairs(int S);
+// Hybrid step: addend[i] = (accumulate ? addend[i] : 0) + partial[i], the
+// partial read from device-mapped host memory.
+hipError_t launch_hybrid_add(float *addend, const float *partial, int n, int accumulate,
+                             hipStream_t s);
 size_t prefetch_lds_bytes(int E, int S);
 hipError_t launch_prefetch(const PrefetchParams &p, hipStream_t s);
 hipError_t launch_gather(const GatherParams &p, int workgroups, hipStream_t s);

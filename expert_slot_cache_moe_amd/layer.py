@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 from . import (MOE_FMT_BF16, make_pool, make_shared, moe_bank_row_bytes, moe_cache_create,
-               moe_cache_destroy, moe_layer_decode)
+               moe_cache_destroy, moe_layer_decode, moe_layer_decode_hybrid)
 
 
 def pinned(a: np.ndarray) -> torch.Tensor:
@@ -60,6 +60,12 @@ class SlotCacheLayers:
         sh = self.shared[layer] if self.shared is not None else None
         moe_layer_decode(self.cache, layer, x, logits, K, out, shared=sh, max_fetch=max_fetch,
                          ids_out=ids_out, w_out=w_out, stream=stream)
+
+    def decode_hybrid(self, layer, x, logits, K, out, ids_out=None, w_out=None, max_fetch=-1,
+                      stream=None):
+        sh = self.shared[layer] if self.shared is not None else None
+        moe_layer_decode_hybrid(self.cache, layer, x, logits, K, out, shared=sh, max_fetch=max_fetch,
+                                ids_out=ids_out, w_out=w_out, stream=stream)
 
     def streamed_pool(self, layer):
         """The whole layer's experts copied to device memory, rows = expert

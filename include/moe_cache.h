@@ -296,6 +296,55 @@ moe_status_t moe_layer_decode(moe_cache_t *cache, int32_t layer, const void *x_d
                               const moe_shared_t *shared, int32_t max_fetch, void *out_dev,
                               int32_t *ids_out_dev, float *w_out_dev, void *stream);
 
+/* Starts (threads >= 1) or stops (0) the cache's pool of host threads for
+ * moe_layer_decode_hybrid, and on first use allocates its pinned staging
+ * (max_tokens x (3 max_top_k + hidden/2 + hidden) x 4 bytes).  The calling
+ * thread of a hybrid step works too: threads - 1 workers are started.
+ * Synchronises the device.  Errors: MOE_INVALID_ARG (threads outside
+ * [0, 1024], a cache without banks or layer workspace), MOE_UNSUPPORTED
+ * (the CPU experts take bf16 rows with hidden and ffn multiples of 16),
+ * MOE_OUT_OF_MEMORY. */
+moe_status_t moe_cache_set_cpu_threads(moe_cache_t *cache, int32_t threads);
+
+/* The CPU half of the hybrid step on its own, on host memory only (no
+ * device call): partial[t] = sum over k ascending with experts[t][k] >= 0
+ * of w[t][k] * W2[e] (bf16(silu(W1[e] x_t) * (W3[e] x_t))), e =
+ * experts[t][k], in fp32 with the activation rounded to bf16.  experts:
+ * int32 [T][K] expert ids or -1; w: fp32 [T][K]; x: bf16 [T][H];
+ * w13_rows: a layer's bf16 gate/up rows [E][2F][H]; w2_rows: its down rows
+ * [E][H][F]; partial: fp32 [T][H] out.  Starts threads - 1 workers for
+ * the call.  The result does not depend on the thread count.  Errors:
+ * MOE_INVALID_ARG (threads outside [1, 1024], H or F not a multiple of
+ * 16, null pointers). */
+moe_status_t moe_cpu_experts(int32_t threads, int32_t T, int32_t K, int32_t H, int32_t F,
+                             const int32_t *experts_host, const float *w_host, const void *x_host,
+                             const void *w13_rows_host, const void *w2_rows_host,
+                             float *partial_host);
+
+/* The hybrid layer step [P1 sections 4-5]: routes the cache leaves at -1
+ * (misses beyond max_fetch, or with no victim) run on host cores over the
+ * pinned host store, overlapped with the GPU's capped gather, shared
+ * expert and cached routes, and the two partial results are added.
+ * Order: top-k -> original ids, weights and x copied to pinned host memory
+ * -> admission (max_fetch) -> rewritten ids copied -> gather -> shared
+ * expert -> GPU routes' gate/up -> [host: wait for the copies, compute
+ * the CPU routes (ascending k per token) into a pinned fp32 partial, fold
+ * it into the shared term] -> down projections and combine.  With the
+ * cache's schedule 0 the CPU half runs before the GPU work is issued (the
+ * pages' serial debug mode); otherwise it overlaps it.  The result:
+ *   out[t] = bf16( sum over GPU routes, ascending k, of w * expert(x_t)
+ *                  + (shared term + sum over CPU routes of w * expert(x_t)) )
+ * The call blocks the host until the admission has run (it needs the slot
+ * ids) and returns once the combine is issued; it cannot be captured in a
+ * graph (MOE_INVALID_ARG on a capturing stream).  Arguments as
+ * moe_layer_decode; ids_out_dev holds the slot ids, -1 for CPU routes.
+ * Errors: MOE_INVALID_ARG (also: no CPU threads started), as
+ * moe_layer_decode otherwise. */
+moe_status_t moe_layer_decode_hybrid(moe_cache_t *cache, int32_t layer, const void *x_dev,
+                                     const float *logits_dev, int32_t T, int32_t K,
+                                     const moe_shared_t *shared, int32_t max_fetch, void *out_dev,
+                                     int32_t *ids_out_dev, float *w_out_dev, void *stream);
+
 /* Look-ahead prefetch of a layer's predicted experts [P4 Consumer,
  * Eviction guard].  ids_dev: int32 [n] predicted expert ids of `layer`;
  * ids outside [0, E) are ignored, the rest taken once each, ascending.
