@@ -310,6 +310,86 @@ def lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok, seed=0
     return res
 
 
+# The layer-step schedules timed beside the default one (overlap = 2).
+SCHEDULES = ((0, "serial: gather, shared expert and routed experts in order on one stream"),
+             (1, "gather on the side stream, overlapping the shared expert and the resident routes"),
+             (3, "shared expert on the side stream, gather and routed experts on the compute stream"))
+
+
+def schedule_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok):
+    """The timed tokens again under each other schedule of the layer step,
+    from the same cache state (the cached experts, and so the fetches, are
+    the same in every schedule)."""
+    res = []
+    x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
+    out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    for ov, what in SCHEDULES:
+        m.moe_cache_set_schedule(lay.cache, ov)
+        graph = capture(torch, lay, x_st, lg_st, out)
+        m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"],
+                                freq=snap["freq"], dlast=snap["dlast"],
+                                last_demand=snap["last_demand"])
+        st0 = m.moe_cache_stats(lay.cache)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(first, n_tok):
+            x_st.copy_(x_all[t])
+            lg_st.copy_(lg_all[t])
+            graph.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        d = m.moe_cache_stats(lay.cache) - st0
+        n = n_tok - first
+        res.append({"overlap": ov, "schedule": what, "value": round(L * n / dt, 1),
+                    "ms_per_step": round(dt / n * 1000.0, 4),
+                    "misses_per_token": round(float(d[m.MOE_STAT_MISSED] - d[m.MOE_STAT_OVERFLOW]) / n, 2)})
+        log(f"[bench] schedule {ov}: {res[-1]['value']} layer-steps/s")
+        del graph
+    m.moe_cache_set_schedule(lay.cache, 2)
+    return res
+
+
+# Hybrid decode: host threads for the CPU routes, fetch caps timed, tokens.
+HYBRID_THREADS = 16
+HYBRID_CAPS = (0, 1, -1)
+HYBRID_TOKENS = 32
+
+
+def hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, first):
+    """The first HYBRID_TOKENS timed tokens again, eagerly, as hybrid steps:
+    misses beyond the fetch cap run on HYBRID_THREADS host threads over the
+    pinned host store while the GPU runs the rest.  Cap -1 fetches every
+    miss (no CPU route): the cost of the hybrid step's host orchestration
+    alone."""
+    m.moe_cache_set_cpu_threads(lay.cache, HYBRID_THREADS)
+    out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    ids = torch.empty((L, 1, K), dtype=torch.int32, device="cuda")
+    res = []
+    n = HYBRID_TOKENS
+    for cap in HYBRID_CAPS:
+        m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"],
+                                freq=snap["freq"], dlast=snap["dlast"],
+                                last_demand=snap["last_demand"])
+        st0 = m.moe_cache_stats(lay.cache)
+        cpu_routes = torch.zeros((), dtype=torch.int64, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(first, first + n):
+            for l in range(L):
+                lay.decode_hybrid(l, x_all[t, l], lg_all[t, l], K, out[l], ids_out=ids[l], max_fetch=cap)
+            cpu_routes += (ids < 0).sum()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        d = m.moe_cache_stats(lay.cache) - st0
+        res.append({"fetch_cap": cap, "value": round(L * n / dt, 1), "ms_per_step": round(dt / n * 1000.0, 4),
+                    "fetches_per_token": round(float(d[m.MOE_STAT_MISSED] - d[m.MOE_STAT_OVERFLOW]) / n, 2),
+                    "cpu_routes_per_token": round(float(cpu_routes.item()) / n, 2)})
+        log(f"[bench] hybrid, fetch cap {cap}: {res[-1]}")
+    m.moe_cache_set_cpu_threads(lay.cache, 0)
+    return {"threads": HYBRID_THREADS, "tokens": n, "runs": res}
+
+
 def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
     """The oracle, single-threaded, on tokens [warm, warm + sample) of the
     same trace after replaying the first `warm` tokens' admissions and
@@ -496,9 +576,12 @@ def summarize_trace(csv_path, log_path):
         p(f"| routed GEMV, {name}: group_count + up_mfma + down_mfma + combine ({parts}) | {len(wc)} | "
           f"{tot.mean():.2f} | {wl.get(name, {}).get('us_per_call')} |")
     p("")
-    pf = [d["us"] for d in disp if d["k"] == "prefetch_kernel"]
+    pfd = [d for d in disp if d["k"] == "prefetch_kernel"]
+    pf = [d["us"] for d in pfd]
     if pf:
-        pg = [d["us"] for d in disp if d["k"] == "gather_kernel"]
+        # each prefetch is followed by its copy; the other schedules' gathers come later
+        lo, hi = pfd[0]["id"], pfd[-1]["id"]
+        pg = [d["us"] for d in disp if d["k"] == "gather_kernel" and lo < d["id"] <= hi + 2]
         p("## Look-ahead runs (each layer step followed by a prefetch of the next layer)\n")
         p("| launch | launches | rocprofv3 mean µs | max µs |")
         p("|---|---|---|---|")
@@ -512,6 +595,26 @@ def summarize_trace(csv_path, log_path):
               f"({r['ms_per_step']} ms per token), {r['demand_fetches_per_token']} demand fetches, "
               f"{r['prefetch_fills_per_token']} prefetch fills and {r['prefetch_drops_per_token']} "
               "drops per token.")
+        p("")
+    if line.get("hybrid"):
+        hy = line["hybrid"]
+        p(f"## Hybrid CPU/GPU steps (eager, {hy['threads']} host threads, the first {hy['tokens']} timed "
+          "tokens again from the same cache state; wall time)\n")
+        p("| fetch cap | layer-steps/s | ms per token | fetches per token | CPU routes per token |")
+        p("|---|---|---|---|---|")
+        for r in hy["runs"]:
+            p(f"| {r['fetch_cap']} | {r['value']} | {r['ms_per_step']} | {r['fetches_per_token']} | "
+              f"{r['cpu_routes_per_token']} |")
+        p("")
+    if line.get("schedules"):
+        p("## Other layer-step schedules (the timed tokens again, same cache state; wall time)\n")
+        p("| overlap | schedule | layer-steps/s | ms per token |")
+        p("|---|---|---|---|")
+        p(f"| 2 (default, the line's value) | gather, shared expert and resident routes as disjoint "
+          f"workgroups of one launch; down projections and combine in a second | {line.get('value')} | "
+          f"{line.get('ms_per_step')} |")
+        for r in line["schedules"]:
+            p(f"| {r['overlap']} | {r['schedule']} | {r['value']} | {r['ms_per_step']} |")
         p("")
     p("The roofline interval is read between event-record nodes captured around the launch in the "
       f"graph ({rl.get('avg_launch_us_events')} µs); the nodes add their own processing to it, "
@@ -603,6 +706,8 @@ def main():
     ap.add_argument("--no-admission", action="store_true")
     ap.add_argument("--no-wide", action="store_true", help="skip the wide-step routed GEMV shapes")
     ap.add_argument("--no-lookahead", action="store_true", help="skip the look-ahead prefetch runs")
+    ap.add_argument("--no-schedules", action="store_true", help="skip the other layer-step schedules")
+    ap.add_argument("--no-hybrid", action="store_true", help="skip the hybrid CPU/GPU runs")
     ap.add_argument("--cpu-sample-tokens", type=int, default=6)
     ap.add_argument("--overlap", type=int, default=2,
                     help="layer-step schedule passed to the cache (0 serial, 1 side-stream "
@@ -791,6 +896,9 @@ def main():
     wide = None if args.no_wide else wide_gemv_benchmark(torch, m)
     adm = None if args.no_admission else admission_benchmark(torch, m, W)
     look = None if args.no_lookahead else lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, W_, n_tok)
+    sched = (None if args.no_schedules or args.overlap != 2
+             else schedule_benchmark(torch, m, lay, snap, x_all, lg_all, W_, n_tok))
+    hyb = None if args.no_hybrid else hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, W_)
     lay.close()
     del lay
     cpu = None
@@ -842,6 +950,8 @@ def main():
         "admission_us": adm,
         "routed_gemv_wide": wide,
         "lookahead": look,
+        "schedules": sched,
+        "hybrid": hyb,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
