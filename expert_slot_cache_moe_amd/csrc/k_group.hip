@@ -37,7 +37,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 16;                       // rows and tokens of one MFMA tile
 constexpr int kSlab = 128;                      // contraction elements per sweep step
-constexpr int kMWaves = 4;
+// One wave per workgroup: the waves of a group's row tiles share nothing
+// (each loads its own weight rows and token columns), and single-wave
+// workgroups let the dispatcher fill every free wave slot, which shortens
+// the tail of a launch with few groups (measured: the wide decode steps
+// run 7-10% faster than with four-wave workgroups).
+constexpr int kMWaves = 1;
 constexpr int kMThreads = kMWaves * kWave;
 constexpr int kRowsPerBlock = kMWaves * kTile;  // output rows of one workgroup
 
@@ -173,7 +178,7 @@ struct GroupEntry {
     }
 };
 
-// gate/up + SwiGLU, 64 rows j per workgroup, for the groups blockIdx.y,
+// gate/up + SwiGLU, 16 rows j per wave, for the groups blockIdx.y,
 // blockIdx.y + gridDim.y, ...: h[route][j] = bf16(silu(g) * u) for every
 // route of a group.  The grid holds about as many workgroups as the device
 // keeps resident; the group table is a prefix of valid groups followed by
