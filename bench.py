@@ -697,6 +697,26 @@ gather_traffic_ratio = {miss_traffic / stage1_kib:.4f}
 routed_traffic_ratio = {gemv_traffic / gemv_kib:.4f}""")
 
 
+def summarize_counters(csv_path):
+    """Mean value per dispatch of every counter of a rocprofv3 --pmc run,
+    per kernel of the library (template arguments kept: the weight format)."""
+    import csv
+    import re
+
+    acc = {}
+    for r in csv.DictReader(open(csv_path)):
+        name = r["Kernel_Name"]
+        k = _short(name)
+        if not k:
+            continue
+        m_ = re.search(r"<(\d)>", name)
+        key = k + (f"<{m_.group(1)}>" if m_ else "")
+        acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for key in sorted(acc):
+        vals = "  ".join(f"{c}={np.mean(v):.4g}" for c, v in sorted(acc[key].items()))
+        print(f"{key}  (dispatches {max(len(v) for v in acc[key].values())})  {vals}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -708,6 +728,10 @@ def main():
     ap.add_argument("--no-lookahead", action="store_true", help="skip the look-ahead prefetch runs")
     ap.add_argument("--no-schedules", action="store_true", help="skip the other layer-step schedules")
     ap.add_argument("--no-hybrid", action="store_true", help="skip the hybrid CPU/GPU runs")
+    ap.add_argument("--only-wide", action="store_true",
+                    help="run only the wide-step routed GEMV shapes (one JSON line each)")
+    ap.add_argument("--summarize-counters", default=None, metavar="COUNTER_CSV",
+                    help="per-kernel means of every counter in a rocprofv3 --pmc csv")
     ap.add_argument("--cpu-sample-tokens", type=int, default=6)
     ap.add_argument("--overlap", type=int, default=2,
                     help="layer-step schedule passed to the cache (0 serial, 1 side-stream "
@@ -727,6 +751,8 @@ def main():
         return summarize_trace(args.summarize_trace, args.launch_log)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, args.launch_log)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode step is data-parallel and this build runs "
               f"on a single MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
@@ -739,6 +765,11 @@ def main():
 
     m.lib()
     torch.cuda.set_device(0)
+    if args.only_wide:
+        # the wide-step shapes alone (for counter passes over their kernels)
+        for r in wide_gemv_benchmark(torch, m):
+            print(json.dumps(r), flush=True)
+        return None
     W_, K_ = args.warmup, args.steps
     lay = build_stack(torch, m, W, gather_workgroups=args.gather_workgroups, overlap=args.overlap)
     n_tok = W_ + K_
