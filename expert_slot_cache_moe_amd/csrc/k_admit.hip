@@ -849,20 +849,22 @@ __device__ __forceinline__ int64_t lfru_score(int64_t freq, uint32_t dlast, uint
 //    the slots used by this call follow in ascending slot order).
 __global__ __launch_bounds__(kThreads) void prefetch_kernel(PrefetchParams p) {
     extern __shared__ __align__(16) int32_t lds[];
-    const int E = p.E, S = p.S;
+    // M >= the distinct valid predictions of the call (min(n, E)): the
+    // per-prediction arrays hold at most that many entries
+    const int E = p.E, S = p.S, M = p.M;
     int32_t *wsum = lds;                                          // [32]
     int32_t *misc = lds + 32;                                     // [16]
-    int64_t *score_v = reinterpret_cast<int64_t *>(misc + 16);    // [E] candidate owner's score, -1: never protected
-    int64_t *score_p = score_v + E;                               // [E] missing prediction's score
-    int32_t *missl = reinterpret_cast<int32_t *>(score_p + E);    // [E] missing predictions, ascending
-    int32_t *vslot = missl + E;                                   // [E] candidates, least recently used first,
-    int32_t *vown = vslot + E;                                    // [E]   and their owners
-    int32_t *fslot = vown + E;                                    // [E] fills: slot,
-    int32_t *fold = fslot + E;                                    // [E]   previous owner,
-    int32_t *fexp = fold + E;                                     // [E]   expert
-    int32_t *tslot = fexp + E;                                    // [E] slots used by this call
-    int32_t *town = tslot + E;                                    // [E]   and their owners
-    uint8_t *want = reinterpret_cast<uint8_t *>(town + E);        // [E] predicted
+    int64_t *score_v = reinterpret_cast<int64_t *>(misc + 16);    // [M] candidate owner's score, -1: never protected
+    int64_t *score_p = score_v + M;                               // [M] missing prediction's score
+    int32_t *missl = reinterpret_cast<int32_t *>(score_p + M);    // [M] missing predictions, ascending
+    int32_t *vslot = missl + M;                                   // [M] candidates, least recently used first,
+    int32_t *vown = vslot + M;                                    // [M]   and their owners
+    int32_t *fslot = vown + M;                                    // [M] fills: slot,
+    int32_t *fold = fslot + M;                                    // [M]   previous owner,
+    int32_t *fexp = fold + M;                                     // [M]   expert
+    int32_t *tslot = fexp + M;                                    // [M] slots used by this call
+    int32_t *town = tslot + M;                                    // [M]   and their owners
+    uint8_t *want = reinterpret_cast<uint8_t *>(town + M);        // [E] predicted
     uint8_t *touched = want + E;                                  // [S] used by this call
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -1068,18 +1070,20 @@ size_t admit_lds_bytes(int E, int S, int max_routes) {
     return (std::max(general, fast) + 15) & ~(size_t)15;
 }
 
-size_t prefetch_lds_bytes(int E, int S) {
-    const size_t b = (32 + 16) * 4 + 16 * (size_t)E + 32 * (size_t)E + (size_t)E + (size_t)S;
+size_t prefetch_lds_bytes(int M, int E, int S) {
+    const size_t b = (32 + 16) * 4 + 16 * (size_t)M + 32 * (size_t)M + (size_t)E + (size_t)S;
     return (b + 15) & ~(size_t)15;
 }
 
+hipError_t prefetch_prepare(size_t lds_bytes) {
+    if (lds_bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&prefetch_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+}
+
 hipError_t launch_prefetch(const PrefetchParams &p, hipStream_t s) {
-    const size_t lds = prefetch_lds_bytes(p.E, p.S);
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefetch_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    if (p.M < std::min(p.n, p.E)) return hipErrorInvalidValue;
+    const size_t lds = prefetch_lds_bytes(p.M, p.E, p.S);
     hipLaunchKernelGGL(prefetch_kernel, dim3(1), dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }

@@ -174,6 +174,7 @@ struct moe_cache {
     hipStream_t pf_side = nullptr;
     hipEvent_t pf_ready = nullptr, pf_done = nullptr;
     int pf_pending = 0;
+    bool prefetch_ok = false;
     int last_layer = -1;
     int gather_wg = 64;
     // hybrid decode: the host-core expert pool and its pinned staging
@@ -503,7 +504,13 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
         moe_cache_destroy(c);
         return s;
     };
-    HIP_TRY(hipGetDevice(&c->device), "hipGetDevice");
+    // a failed HIP call after this point also frees what was made
+#define CREATE_TRY(call, what)                              \
+    do {                                                    \
+        hipError_t e_ = (call);                             \
+        if (e_ != hipSuccess) return bail(hip_fail(e_, what)); \
+    } while (0)
+    CREATE_TRY(hipGetDevice(&c->device), "hipGetDevice");
 
     // Weights.
     if (d->num_banks != 0) {
@@ -548,13 +555,13 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
 
     // Admission state.
     int max_lds = 0;
-    HIP_TRY(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device),
+    CREATE_TRY(hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device),
             "device attribute");
     c->admit_lds = admit_lds_bytes(d->num_experts, d->num_slots, d->max_routes);
     if (c->admit_lds > (size_t)max_lds)
         return bail(fail(MOE_UNSUPPORTED, "admission needs %zu B of LDS (E=%d, S=%d, max_routes=%d); device has %d",
                          c->admit_lds, d->num_experts, d->num_slots, d->max_routes, max_lds));
-    HIP_TRY(admit_prepare(c->admit_lds), "admission LDS attribute");
+    CREATE_TRY(admit_prepare(c->admit_lds), "admission LDS attribute");
 
     const size_t L = d->num_layers, E = d->num_experts, S = d->num_slots;
     c->plan_cap = (int)std::min<size_t>(E, (size_t)d->max_routes);
@@ -643,28 +650,33 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *d, moe_cache_t **out) {
         c->ws_shared_bytes = sw.total;
         const size_t glds = group_lds_bytes((int)(T * K));
         if (glds > (size_t)max_lds) return bail(fail(MOE_UNSUPPORTED, "route grouping LDS too large"));
-        HIP_TRY(group_prepare(glds), "grouping LDS attribute");
-        HIP_TRY(group_count_prepare(), "grouping LDS attribute");
+        CREATE_TRY(group_prepare(glds), "grouping LDS attribute");
+        CREATE_TRY(group_count_prepare(), "grouping LDS attribute");
         if ((int64_t)T * K > d->max_routes)
             return bail(fail(MOE_INVALID_ARG, "max_tokens * max_top_k > max_routes"));
     }
 
     // Side stream and the two events, made before any capture.
-    HIP_TRY(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking), "side stream");
-    HIP_TRY(hipEventCreateWithFlags(&c->ready, hipEventDisableTiming), "ready event");
-    HIP_TRY(hipEventCreateWithFlags(&c->done, hipEventDisableTiming), "done event");
-    HIP_TRY(hipStreamCreateWithFlags(&c->pf_side, hipStreamNonBlocking), "prefetch stream");
-    HIP_TRY(hipEventCreateWithFlags(&c->pf_ready, hipEventDisableTiming), "prefetch event");
-    HIP_TRY(hipEventCreateWithFlags(&c->pf_done, hipEventDisableTiming), "prefetch event");
-    if (prefetch_lds_bytes(d->num_experts, d->num_slots) > (size_t)max_lds)
-        return bail(fail(MOE_UNSUPPORTED, "prefetch needs %zu B of LDS (E=%d, S=%d); device has %d",
-                         prefetch_lds_bytes(d->num_experts, d->num_slots), d->num_experts,
-                         d->num_slots, max_lds));
+    CREATE_TRY(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking), "side stream");
+    CREATE_TRY(hipEventCreateWithFlags(&c->ready, hipEventDisableTiming), "ready event");
+    CREATE_TRY(hipEventCreateWithFlags(&c->done, hipEventDisableTiming), "done event");
+    CREATE_TRY(hipStreamCreateWithFlags(&c->pf_side, hipStreamNonBlocking), "prefetch stream");
+    CREATE_TRY(hipEventCreateWithFlags(&c->pf_ready, hipEventDisableTiming), "prefetch event");
+    CREATE_TRY(hipEventCreateWithFlags(&c->pf_done, hipEventDisableTiming), "prefetch event");
+    // the look-ahead prefetch of up to max_routes ids: usable only if its
+    // kernel fits the LDS (checked again by moe_prefetch)
+    {
+        const size_t pl = prefetch_lds_bytes(std::min(d->num_experts, d->max_routes), d->num_experts,
+                                             d->num_slots);
+        c->prefetch_ok = pl <= (size_t)max_lds;
+        if (c->prefetch_ok) CREATE_TRY(prefetch_prepare(pl), "prefetch LDS attribute");
+    }
     c->tev.assign((size_t)d->num_layers * 6, nullptr);
     c->trecorded.assign(d->num_layers, 0);
-    HIP_TRY(hipDeviceSynchronize(), "create sync");
+    CREATE_TRY(hipDeviceSynchronize(), "create sync");
     *out = c;
     return MOE_OK;
+#undef CREATE_TRY
 }
 
 moe_status_t moe_cache_set_schedule(moe_cache_t *c, int32_t overlap) {
@@ -977,6 +989,11 @@ moe_status_t moe_prefetch(moe_cache_t *c, int32_t layer, const int32_t *ids, int
         return fail(MOE_INVALID_ARG, "n=%d outside [0, max_routes=%d]", n, c->d.max_routes);
     if (n == 0) return MOE_OK;   // width 0 leaves everything as it is
     if (!ids) return fail(MOE_INVALID_ARG, "NULL ids");
+    if (!c->prefetch_ok)
+        return fail(MOE_UNSUPPORTED, "prefetch needs %zu B of LDS (E=%d, S=%d, max_routes=%d)",
+                    prefetch_lds_bytes(std::min(c->d.num_experts, c->d.max_routes), c->d.num_experts,
+                                       c->d.num_slots),
+                    c->d.num_experts, c->d.num_slots, c->d.max_routes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the kernel rewrites the fill plan the pending copy reads
     moe_status_t js = join_prefetch(c, s);
@@ -984,6 +1001,7 @@ moe_status_t moe_prefetch(moe_cache_t *c, int32_t layer, const int32_t *ids, int
     PrefetchParams p{};
     p.ids = ids;
     p.n = n;
+    p.M = std::min(n, c->d.num_experts);
     p.layer = layer;
     p.E = c->d.num_experts;
     p.S = c->d.num_slots;

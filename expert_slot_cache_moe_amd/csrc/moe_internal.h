@@ -190,6 +190,7 @@ struct AdmitParams {
 struct PrefetchParams {
     const int32_t *ids;    // [n]
     int32_t n;
+    int32_t M;             // capacity of the per-prediction LDS arrays, >= min(n, E)
     int32_t layer;
     int32_t E, S;
     int32_t pairs;         // order holds (slot, owner) pairs
@@ -263,7 +264,9 @@ bool admit_order_pairs(int S);
 // partial read from device-mapped host memory.
 hipError_t launch_hybrid_add(float *addend, const float *partial, int n, int accumulate,
                              hipStream_t s);
-size_t prefetch_lds_bytes(int E, int S);
+size_t prefetch_lds_bytes(int M, int E, int S);
+// Allows the prefetch kernel lds_bytes of dynamic LDS (needed above 64 KB).
+hipError_t prefetch_prepare(size_t lds_bytes);
 hipError_t launch_prefetch(const PrefetchParams &p, hipStream_t s);
 hipError_t launch_gather(const GatherParams &p, int workgroups, hipStream_t s);
 int gather_unit_bytes();

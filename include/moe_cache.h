@@ -372,7 +372,9 @@ moe_status_t moe_layer_decode_hybrid(moe_cache_t *cache, int32_t layer, const vo
  * graph capture, call moe_prefetch_join before ending a capture with a
  * prefetch still pending.  A cache without banks updates the state only.
  * Errors: MOE_INVALID_ARG (layer outside [0, L), n < 0 or n > max_routes,
- * null ids with n > 0). */
+ * null ids with n > 0), MOE_UNSUPPORTED (the prefetch kernel for
+ * min(max_routes, E) predictions does not fit the device's LDS: about
+ * 48 min(max_routes, E) + E + S bytes). */
 moe_status_t moe_prefetch(moe_cache_t *cache, int32_t layer, const int32_t *ids_dev, int32_t n,
                           void *stream);
 

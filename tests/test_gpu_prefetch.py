@@ -343,3 +343,29 @@ def test_captured_token_with_prefetches_replays_like_eager():
     finally:
         graph_l.close()
         eager_l.close()
+
+
+def test_many_experts_prefetch_is_sized_by_the_prediction_count():
+    """The prefetch kernel's LDS grows with the predictions a call may hold
+    (min(max_routes, E)), not with E alone: 3400 experts with calls of up to
+    300 ids work; a cache whose full-width prefetch would not fit the LDS is
+    still created, and only its prefetch is refused."""
+    g = np.random.default_rng(21)
+    L, E, S = 2, 3400, 3500
+    ops = [("d", l, g.choice(E, 200, replace=False).astype(np.int32), -1) for l in range(L)]
+    for _ in range(30):
+        kind = "p" if g.random() < 0.5 else "d"
+        ids = np.minimum(g.zipf(1.2, int(g.integers(1, 300))) - 1, E + 1).astype(np.int32)
+        ops.append((kind, int(g.integers(0, L)), ids, -1))
+    _mixed(L, E, S, 256, 128, ops, 300)
+
+    E2, S2 = 3300, 3400
+    gc = m.moe_cache_create(num_layers=1, num_experts=E2, num_slots=S2, max_routes=E2)
+    try:
+        m.moe_admit(gc, 0, _dev_i32(np.arange(100)))
+        with pytest.raises(m.MoeError) as e:
+            m.moe_prefetch(gc, 0, _dev_i32([5, 500]))
+        assert e.value.status == m.MOE_UNSUPPORTED
+        assert m.moe_cache_read_state(gc)["clock"] == 1
+    finally:
+        m.moe_cache_destroy(gc)
