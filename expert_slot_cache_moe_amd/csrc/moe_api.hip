@@ -174,6 +174,7 @@ struct moe_cache {
     hipStream_t pf_side = nullptr;
     hipEvent_t pf_ready = nullptr, pf_done = nullptr;
     int pf_pending = 0;
+    bool pf_captured = false;   // the pending copy was issued under stream capture
     bool prefetch_ok = false;
     int last_layer = -1;
     int gather_wg = 64;
@@ -344,9 +345,24 @@ moe_status_t check_shared(const moe_shared_t *sh, int H, int F, int *Fs) {
 
 // With logits set, the admission computes the top-k of T rows itself
 // (R = T * K) and writes the weights to w.
-// Orders `s` after the copy of a pending prefetch.
+// Orders `s` after the copy of a pending prefetch.  A copy issued outside
+// the capture that `s` is in cannot be waited for inside it (the graph would
+// not order itself after it): that is refused, loudly, instead of racing.
 moe_status_t join_prefetch(moe_cache *c, hipStream_t s) {
     if (!c->pf_pending) return MOE_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(s, &cs), "capture status");
+    const bool capturing = cs != hipStreamCaptureStatusNone;
+    if (capturing && !c->pf_captured)
+        return fail(MOE_INVALID_ARG,
+                    "a prefetch issued outside this capture is still pending: call moe_prefetch_join "
+                    "before beginning the capture");
+    if (!capturing && c->pf_captured) {
+        // left pending by a capture that ended without joining (that capture
+        // failed); its event belongs to no launched work
+        c->pf_pending = 0;
+        return MOE_OK;
+    }
     HIP_TRY(hipStreamWaitEvent(s, c->pf_done, 0), "wait for the prefetch copy");
     c->pf_pending = 0;
     return MOE_OK;
@@ -1027,7 +1043,10 @@ moe_status_t moe_prefetch(moe_cache_t *c, int32_t layer, const int32_t *ids, int
                           c->gather_wg, c->pf_side),
             "prefetch copy launch");
     HIP_TRY(hipEventRecord(c->pf_done, c->pf_side), "record prefetch done");
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(s, &cs), "capture status");
     c->pf_pending = 1;
+    c->pf_captured = cs != hipStreamCaptureStatusNone;
     return MOE_OK;
 }
 

@@ -370,7 +370,10 @@ moe_status_t moe_layer_decode_hybrid(moe_cache_t *cache, int32_t layer, const vo
  * (moe_admit, moe_layer_decode) first waits for that copy, on the device;
  * so does the next prefetch, whose kernel reuses the fill plan.  Under
  * graph capture, call moe_prefetch_join before ending a capture with a
- * prefetch still pending.  A cache without banks updates the state only.
+ * prefetch still pending, and before beginning one after an eager
+ * prefetch (a call that would wait inside a capture for a copy issued
+ * outside it fails with MOE_INVALID_ARG).  A cache without banks updates
+ * the state only.
  * Errors: MOE_INVALID_ARG (layer outside [0, L), n < 0 or n > max_routes,
  * null ids with n > 0), MOE_UNSUPPORTED (the prefetch kernel for
  * min(max_routes, E) predictions does not fit the device's LDS: about

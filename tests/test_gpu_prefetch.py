@@ -369,3 +369,36 @@ def test_many_experts_prefetch_is_sized_by_the_prediction_count():
         assert m.moe_cache_read_state(gc)["clock"] == 1
     finally:
         m.moe_cache_destroy(gc)
+
+
+def test_eager_prefetch_must_be_joined_before_a_capture():
+    """A prefetch issued eagerly and still pending when a capture begins
+    cannot be waited for inside the capture: the layer step refuses (it would
+    otherwise race with the copy); after moe_prefetch_join it captures."""
+    L, E, S, H, F, K = 2, 16, 10, 64, 128, 2
+    g = W.rng(45, "eager-then-capture")
+    host = [W.expert_rows(0, g, E, H, F) for _ in range(L)]
+    lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, host_rows=host,
+                          max_tokens=1, max_top_k=K, overlap=2)
+    x = _dev_u16(W.normal_bf16(g, (1, H)))
+    lg = torch.from_numpy(W.zipf_logits(g, 1, E, 0.7)).cuda()
+    out = torch.empty((1, H), dtype=torch.int16, device="cuda")
+    try:
+        lay.decode(0, x, lg, K, out)
+        m.moe_prefetch(lay.cache, 1, _dev_i32([3, 4]))
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with pytest.raises(m.MoeError):
+            with torch.cuda.graph(graph, stream=s):
+                lay.decode(1, x, lg, K, out, stream=s)
+        torch.cuda.synchronize()
+        m.moe_prefetch_join(lay.cache)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            lay.decode(1, x, lg, K, out, stream=s)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert m.moe_cache_read_state(lay.cache)["stats"][1][m.MOE_STAT_CALLS] == 1
+    finally:
+        lay.close()
