@@ -1,8 +1,9 @@
-// The C ABI (include/moe_cache.h): argument checks, the cache's device
-// state, and the launch sequence of one layer step on the compute and side
-// streams.  Every check happens on the host before any launch, so a
-// failing call launches nothing; launching calls never synchronise and
-// never allocate, so a whole token's layers capture into one hipGraph.
+// The C ABI (include/moe_cache.h), part 1: errors, the cache and its
+// device state, admission, gather, the routed and shared experts alone, and
+// inspection.  The layer step is in moe_layer.hip, the look-ahead prefetch
+// in moe_prefetch.hip.  Every check happens on the host before any launch,
+// so a failing call launches nothing; launching calls never synchronise
+// and never allocate, so a whole token's layers capture into one hipGraph.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -14,12 +15,13 @@
 #include <functional>
 #include <vector>
 
-#include "cpu_experts.h"
-#include "moe_internal.h"
+#include "moe_api_internal.h"
 
 using namespace moe;
+using namespace moe::api;
 
-namespace {
+namespace moe {
+namespace api {
 
 thread_local std::string g_last_error;
 
@@ -36,12 +38,6 @@ moe_status_t fail(moe_status_t s, const char *fmt, ...) {
 moe_status_t hip_fail(hipError_t e, const char *what) {
     return fail(MOE_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
 }
-
-#define HIP_TRY(call, what)                          \
-    do {                                             \
-        hipError_t e_ = (call);                      \
-        if (e_ != hipSuccess) return hip_fail(e_, what); \
-    } while (0)
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -70,11 +66,6 @@ void row_bytes_of(int fmt, int H, int F, int64_t rb[MOE_MAX_BANKS], int *nb) {
         *nb = 6;
     }
 }
-
-// Workspace of the routed experts for n = T*K routes.
-struct RoutedWs {
-    size_t h, d, ngroups, grp_row, grp_start, grp_count, grp_routes, total;
-};
 
 RoutedWs routed_ws(int H, int F, int T, int K) {
     RoutedWs w;
@@ -115,10 +106,6 @@ std::vector<int32_t> order_image(int S, const uint32_t *stamp, const int32_t *ow
     return img;
 }
 
-constexpr int kMaxTopK = 64;
-constexpr int kFusedTopkRows = 32;   // up to this many rows, top-k runs inside the admission
-constexpr int kMaxRoutedRoutes = 8192;
-
 // Records a timing event on `s`.  Under stream capture the event becomes an
 // event-record node of the graph being captured, appended after the
 // stream's current capture dependencies, so every replay re-records it.
@@ -136,64 +123,12 @@ hipError_t record_timing(hipEvent_t ev, hipStream_t s) {
     return hipStreamUpdateCaptureDependencies(s, &node, 1, hipStreamSetCaptureDependencies);
 }
 
-}  // namespace
+}  // namespace api
+}  // namespace moe
 
-struct moe_cache {
-    moe_cache_desc_t d{};
-    int device = 0;
-    int nb = 0;
-    int64_t rb[MOE_MAX_BANKS] = {};
-    std::vector<const uint8_t *> host_dev;  // [L * nb] device-visible host rows
-    std::vector<const uint8_t *> host_rows; // [L * nb] the same rows, host addresses
-    // device state
-    void *state = nullptr;
-    int32_t *res = nullptr, *own = nullptr, *order = nullptr;
-    int32_t *plan_slot = nullptr, *plan_expert = nullptr, *n_miss = nullptr;
-    uint32_t *stamp = nullptr, *clock = nullptr, *dlast = nullptr;
-    int64_t *stats = nullptr, *freq = nullptr;
-    int32_t *fill_slot = nullptr, *fill_expert = nullptr, *n_fill = nullptr;
-    int plan_cap = 0;
-    size_t admit_lds = 0;
-    // layer workspace
-    void *ws = nullptr;
-    int32_t *ws_ids = nullptr;
-    int32_t *ws_route_plan = nullptr;
-    float *ws_w = nullptr;
-    float *ws_addend = nullptr;
-    float *ws_gu = nullptr;          // [max_top_k][2F] fetched experts' gate/up dots
-    uint8_t *ws_routed = nullptr;
-    size_t ws_routed_bytes = 0;
-    uint8_t *ws_shared = nullptr;
-    size_t ws_shared_bytes = 0;
-    int shared_ffn_cap = 0;
-    // ordering
-    hipStream_t side = nullptr;
-    hipEvent_t ready = nullptr, done = nullptr;
-    // look-ahead prefetch: its copy stream, fork/join events, and whether a
-    // copy is still to be waited for
-    hipStream_t pf_side = nullptr;
-    hipEvent_t pf_ready = nullptr, pf_done = nullptr;
-    int pf_pending = 0;
-    bool pf_captured = false;   // the pending copy was issued under stream capture
-    bool prefetch_ok = false;
-    int last_layer = -1;
-    int gather_wg = 64;
-    // hybrid decode: the host-core expert pool and its pinned staging
-    // (original expert ids, slot ids, weights, x, the CPU partial)
-    CpuExperts *cpu = nullptr;
-    void *hyb_host = nullptr;
-    int32_t *h_experts = nullptr, *h_slots = nullptr;
-    float *h_w = nullptr, *h_partial = nullptr, *d_partial = nullptr;
-    uint16_t *h_x = nullptr;
-    std::vector<int32_t> cpu_ids;
-    hipEvent_t hyb_ready = nullptr;
-    // timing
-    int timing = 0;
-    std::vector<hipEvent_t> tev;     // [L * 6]: admission, gather, routed start/end
-    std::vector<int> trecorded;      // [L]
-};
 
-namespace {
+namespace moe {
+namespace api {
 
 PoolView slot_pool_view(const moe_cache *c) {
     PoolView pv{};
@@ -233,16 +168,10 @@ moe_status_t pool_view_of(const moe_pool_t *pool, PoolView &pv) {
     return MOE_OK;
 }
 
-// The routed experts + combine on one stream (no argument checks).
-// Work issued right before the launch that adds the fp32 term: a wait for
-// the stream producing it, or the hybrid step's CPU half.  Always called,
-// also after a failed launch, so a fork it closes is always joined.
-using BeforeAddend = std::function<hipError_t()>;
-
-// The routed experts and the combine.
+// The routed experts and the combine on one stream (no argument checks).
 hipError_t routed_sequence(const PoolView &pv, const uint16_t *x, const int32_t *idx,
                            const float *w, int T, int K, const float *addend, uint16_t *out,
-                           uint8_t *ws, hipStream_t s, const BeforeAddend *before = nullptr) {
+                           uint8_t *ws, hipStream_t s, const BeforeAddend *before) {
     auto wait_join = [&]() { return before ? (*before)() : hipSuccess; };
     if (T == 0) return wait_join();
     const RoutedWs L = routed_ws(pv.H, pv.F, T, K);
@@ -343,35 +272,12 @@ moe_status_t check_shared(const moe_shared_t *sh, int H, int F, int *Fs) {
     return MOE_OK;
 }
 
+
 // With logits set, the admission computes the top-k of T rows itself
 // (R = T * K) and writes the weights to w.
-// Orders `s` after the copy of a pending prefetch.  A copy issued outside
-// the capture that `s` is in cannot be waited for inside it (the graph would
-// not order itself after it): that is refused, loudly, instead of racing.
-moe_status_t join_prefetch(moe_cache *c, hipStream_t s) {
-    if (!c->pf_pending) return MOE_OK;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    HIP_TRY(hipStreamIsCapturing(s, &cs), "capture status");
-    const bool capturing = cs != hipStreamCaptureStatusNone;
-    if (capturing && !c->pf_captured)
-        return fail(MOE_INVALID_ARG,
-                    "a prefetch issued outside this capture is still pending: call moe_prefetch_join "
-                    "before beginning the capture");
-    if (!capturing && c->pf_captured) {
-        // left pending by a capture that ended without joining (that capture
-        // failed); its event belongs to no launched work
-        c->pf_pending = 0;
-        return MOE_OK;
-    }
-    HIP_TRY(hipStreamWaitEvent(s, c->pf_done, 0), "wait for the prefetch copy");
-    c->pf_pending = 0;
-    return MOE_OK;
-}
-
 moe_status_t launch_admit_checked(moe_cache *c, int layer, int32_t *ids, int R, int max_fetch,
-                                  hipStream_t s, int32_t *route_plan = nullptr,
-                                  const float *logits = nullptr, int T = 0, int K = 0,
-                                  float *w = nullptr) {
+                                  hipStream_t s, int32_t *route_plan, const float *logits, int T,
+                                  int K, float *w) {
     {
         moe_status_t js = join_prefetch(c, s);
         if (js != MOE_OK) return js;
@@ -439,7 +345,8 @@ moe_status_t launch_gather_checked(moe_cache *c, hipStream_t s) {
     return MOE_OK;
 }
 
-}  // namespace
+}  // namespace api
+}  // namespace moe
 
 // ====================================================================== ABI
 
@@ -820,400 +727,11 @@ moe_status_t moe_shared_expert(const moe_shared_t *sh, int32_t H, const void *x,
     return MOE_OK;
 }
 
-moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, const float *logits,
-                              int32_t T, int32_t K, const moe_shared_t *shared, int32_t max_fetch,
-                              void *out, int32_t *ids_out, float *w_out, void *stream) {
-    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
-    if (c->nb == 0) return fail(MOE_INVALID_ARG, "cache has no weight banks");
-    if (layer < 0 || layer >= c->d.num_layers)
-        return fail(MOE_INVALID_ARG, "layer %d outside [0, %d)", layer, c->d.num_layers);
-    if (T < 0 || T > c->d.max_tokens) return fail(MOE_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, c->d.max_tokens);
-    if (K < 1 || K > c->d.max_top_k || K > c->d.num_experts)
-        return fail(MOE_INVALID_ARG, "K=%d outside [1, %d]", K, c->d.max_top_k);
-    if ((int64_t)T * K > c->d.max_routes) return fail(MOE_INVALID_ARG, "T*K > max_routes");
-    if (T > 0 && (!x || !logits || !out)) return fail(MOE_INVALID_ARG, "NULL layer buffer");
-    if (T > 0 && !aligned16(x)) return fail(MOE_INVALID_ARG, "x must be 16-byte aligned");
-    int Fs = 0;
-    if (shared) {
-        moe_status_t s = check_shared(shared, c->d.hidden, c->d.ffn, &Fs);
-        if (s != MOE_OK) return s;
-        if (Fs > c->shared_ffn_cap)
-            return fail(MOE_UNSUPPORTED, "shared ffn %d > the cache's workspace width %d", Fs, c->shared_ffn_cap);
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int32_t *ids = ids_out ? ids_out : c->ws_ids;
-    float *w = w_out ? w_out : c->ws_w;
-    const int R = T * K;
-    const bool timing = c->timing != 0;
-    hipEvent_t *tev = timing ? &c->tev[(size_t)layer * 6] : nullptr;
 
-    // Few token rows: the top-k runs inside the admission kernel.
-    const bool fused_topk =
-        T <= kFusedTopkRows && admit_fused_topk_supported(c->d.num_experts, c->d.num_slots, K);
-    if (c->d.overlap == 3 && shared && T > 0) {
-        // The #678 split: the shared expert and its gate on the side stream,
-        // forked here; top-k, admission, gather and the routed experts on the
-        // compute stream, joined right before the launch that adds the shared
-        // term.  Every exit after the fork joins, so no side work outlives
-        // the step.
-        const uint16_t *xb = static_cast<const uint16_t *>(x);
-        HIP_TRY(hipEventRecord(c->ready, s), "record ready");
-        HIP_TRY(hipStreamWaitEvent(c->side, c->ready, 0), "side waits ready");
-        hipError_t e = shared_sequence(shared, c->d.hidden, Fs, xb, T, c->ws_addend, c->ws_shared, c->side);
-        const hipError_t re = hipEventRecord(c->done, c->side);
-        auto joined = [&](moe_status_t r) {
-            (void)hipStreamWaitEvent(s, c->done, 0);
-            return r;
-        };
-        if (e != hipSuccess || re != hipSuccess)
-            return joined(hip_fail(e != hipSuccess ? e : re, "shared expert on the side stream"));
-        auto mark = [&](int i) { return timing ? record_timing(tev[i], s) : hipSuccess; };
-        if (!fused_topk && (e = launch_topk(logits, T, c->d.num_experts, K, ids, w, s)) != hipSuccess)
-            return joined(hip_fail(e, "top-k launch"));
-        if ((e = mark(0)) != hipSuccess) return joined(hip_fail(e, "timing"));
-        moe_status_t st = fused_topk
-                              ? launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan,
-                                                     logits, T, K, w)
-                              : launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan);
-        if (st != MOE_OK) return joined(st);
-        if ((e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess) return joined(hip_fail(e, "timing"));
-        if ((st = launch_gather_checked(c, s)) != MOE_OK) return joined(st);
-        if ((e = mark(3)) != hipSuccess || (e = mark(4)) != hipSuccess) return joined(hip_fail(e, "timing"));
-        const BeforeAddend join = [&]() { return hipStreamWaitEvent(s, c->done, 0); };
-        e = routed_sequence(slot_pool_view(c), xb, ids, w, T, K, c->ws_addend,
-                            static_cast<uint16_t *>(out), c->ws_routed, s, &join);
-        if (e != hipSuccess) return hip_fail(e, "routed launch");   // joined inside
-        if (timing) {
-            HIP_TRY(record_timing(tev[5], s), "timing");
-            c->trecorded[layer] = 1;
-        }
-        return MOE_OK;
-    }
-    if (!fused_topk) HIP_TRY(launch_topk(logits, T, c->d.num_experts, K, ids, w, s), "top-k launch");
-    if (timing) HIP_TRY(record_timing(tev[0], s), "timing");
-    moe_status_t st = fused_topk ? launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan,
-                                                        logits, T, K, w)
-                                 : launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan);
-    if (st != MOE_OK) return st;
-    if (timing) HIP_TRY(record_timing(tev[1], s), "timing");
-    if (c->d.overlap == 2 && T == 1 && stage_supported(c->d.weight_format, c->d.hidden, c->d.ffn) &&
-        (!shared || Fs == c->d.ffn)) {
-        // One stream, two launches: the gather overlaps the shared expert and
-        // the resident routes inside stage 1.
-        const PoolView pv = slot_pool_view(c);
-        const RoutedWs rw = routed_ws(pv.H, pv.F, T, K);
-        PoolView spv{};
-        uint16_t *hs = nullptr;
-        float *gamma = nullptr;
-        if (shared) {
-            spv.fmt = MOE_FMT_BF16;
-            spv.H = c->d.hidden;
-            spv.F = Fs;
-            spv.num_rows = 1;
-            spv.bank[0] = static_cast<const uint8_t *>(shared->w13_dev);
-            spv.bank[1] = static_cast<const uint8_t *>(shared->w2_dev);
-            spv.rb[0] = (int64_t)4 * Fs * c->d.hidden;
-            spv.rb[1] = (int64_t)2 * c->d.hidden * Fs;
-            const RoutedWs sw = routed_ws(c->d.hidden, Fs, T, 1);
-            hs = reinterpret_cast<uint16_t *>(c->ws_shared + sw.h);
-            gamma = reinterpret_cast<float *>(c->ws_shared + sw.d);
-        }
-        for (int which = 1; which <= 2; ++which) {
-            if (timing) HIP_TRY(record_timing(tev[2 * which], s), "timing");
-            HIP_TRY(launch_stages(gather_params(c), c->gather_wg, c->ws_gu, pv, ids, w,
-                                  c->ws_route_plan, K, static_cast<const uint16_t *>(x),
-                                  reinterpret_cast<uint16_t *>(c->ws_routed + rw.h),
-                                  shared ? &spv : nullptr, hs,
-                                  shared ? static_cast<const uint16_t *>(shared->gate_dev)
-                                         : nullptr,
-                                  gamma, nullptr, static_cast<uint16_t *>(out), which, s),
-                    "stage launch");
-            if (timing) HIP_TRY(record_timing(tev[2 * which + 1], s), "timing");
-        }
-        if (timing) c->trecorded[layer] = 1;
-        return MOE_OK;
-    }
-    const bool two_streams = c->d.overlap == 1;
-    hipStream_t gs = s;
-    if (two_streams) {
-        HIP_TRY(hipEventRecord(c->ready, s), "record ready");
-        HIP_TRY(hipStreamWaitEvent(c->side, c->ready, 0), "side waits ready");
-        gs = c->side;
-    }
-    if (timing) HIP_TRY(record_timing(tev[2], gs), "timing");
-    st = launch_gather_checked(c, gs);
-    if (st != MOE_OK) return st;
-    if (timing) HIP_TRY(record_timing(tev[3], gs), "timing");
-    if (two_streams) HIP_TRY(hipEventRecord(c->done, c->side), "record done");
 
-    // Between fork and join, on the compute stream: the shared expert and
-    // its gate, and (single token) the routed experts whose slots were
-    // already resident -- none of these reads a slot the gather writes.
-    const PoolView pv = slot_pool_view(c);
-    const uint16_t *xb = static_cast<const uint16_t *>(x);
-    const bool split = two_streams && T == 1;
-    const RoutedWs rw = routed_ws(pv.H, pv.F, T, K);
-    uint16_t *h = reinterpret_cast<uint16_t *>(c->ws_routed + rw.h);
-    float *dr = reinterpret_cast<float *>(c->ws_routed + rw.d);
-    hipError_t e = hipSuccess;
-    if (shared) e = shared_sequence(shared, c->d.hidden, Fs, xb, T, c->ws_addend, c->ws_shared, s);
-    Items it{};
-    it.mode = ITEM_ROUTE;
-    it.K = K;
-    it.n = R;
-    it.idx = ids;
-    it.route_plan = c->ws_route_plan;
-    if (split && e == hipSuccess) {
-        it.want_fresh = 0;
-        e = launch_up(pv, it, R, xb, h, nullptr, nullptr, s);
-        if (e == hipSuccess) e = launch_down_to_d(pv, it, R, h, dr, nullptr, s);
-    }
-    // The join is issued even if a launch above failed, so the side stream
-    // never outlives the step.
-    if (two_streams) {
-        hipError_t je = hipStreamWaitEvent(s, c->done, 0);
-        if (e == hipSuccess) e = je;
-    }
-    if (e != hipSuccess) return hip_fail(e, "shared expert / resident routes / join");
 
-    if (timing) HIP_TRY(record_timing(tev[4], s), "timing");
-    const float *add = shared ? c->ws_addend : nullptr;
-    if (split) {
-        it.want_fresh = 1;
-        HIP_TRY(launch_up(pv, it, R, xb, h, nullptr, nullptr, s), "routed launch");
-        HIP_TRY(launch_down_fused(pv, ids, w, T, K, h, add, dr, c->ws_route_plan,
-                                  static_cast<uint16_t *>(out), s),
-                "routed launch");
-    } else {
-        HIP_TRY(routed_sequence(pv, xb, ids, w, T, K, add, static_cast<uint16_t *>(out),
-                                c->ws_routed, s),
-                "routed launch");
-    }
-    if (timing) {
-        HIP_TRY(record_timing(tev[5], s), "timing");
-        c->trecorded[layer] = 1;
-    }
-    return MOE_OK;
-}
 
-moe_status_t moe_prefetch(moe_cache_t *c, int32_t layer, const int32_t *ids, int32_t n,
-                          void *stream) {
-    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
-    if (layer < 0 || layer >= c->d.num_layers)
-        return fail(MOE_INVALID_ARG, "layer %d outside [0, %d)", layer, c->d.num_layers);
-    if (n < 0 || n > c->d.max_routes)
-        return fail(MOE_INVALID_ARG, "n=%d outside [0, max_routes=%d]", n, c->d.max_routes);
-    if (n == 0) return MOE_OK;   // width 0 leaves everything as it is
-    if (!ids) return fail(MOE_INVALID_ARG, "NULL ids");
-    if (!c->prefetch_ok)
-        return fail(MOE_UNSUPPORTED, "prefetch needs %zu B of LDS (E=%d, S=%d, max_routes=%d)",
-                    prefetch_lds_bytes(std::min(c->d.num_experts, c->d.max_routes), c->d.num_experts,
-                                       c->d.num_slots),
-                    c->d.num_experts, c->d.num_slots, c->d.max_routes);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    // the kernel rewrites the fill plan the pending copy reads
-    moe_status_t js = join_prefetch(c, s);
-    if (js != MOE_OK) return js;
-    PrefetchParams p{};
-    p.ids = ids;
-    p.n = n;
-    p.M = std::min(n, c->d.num_experts);
-    p.layer = layer;
-    p.E = c->d.num_experts;
-    p.S = c->d.num_slots;
-    p.pairs = admit_order_pairs(p.S) ? 1 : 0;
-    p.res = c->res;
-    p.own = c->own;
-    p.stamp = c->stamp;
-    p.order = c->order;
-    p.clock = c->clock;
-    p.stats = c->stats;
-    p.freq = c->freq;
-    p.dlast = c->dlast;
-    p.fill_slot = c->fill_slot;
-    p.fill_expert = c->fill_expert;
-    p.n_fill = c->n_fill;
-    HIP_TRY(launch_prefetch(p, s), "prefetch launch");
-    if (c->nb == 0) return MOE_OK;
-    // The copy forks off `s`: nothing on `s` waits for it until the next
-    // demand admission or prefetch.
-    HIP_TRY(hipEventRecord(c->pf_ready, s), "record prefetch fork");
-    HIP_TRY(hipStreamWaitEvent(c->pf_side, c->pf_ready, 0), "prefetch stream waits");
-    HIP_TRY(launch_gather(gather_params(c, layer, c->n_fill, c->fill_slot, c->fill_expert),
-                          c->gather_wg, c->pf_side),
-            "prefetch copy launch");
-    HIP_TRY(hipEventRecord(c->pf_done, c->pf_side), "record prefetch done");
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    HIP_TRY(hipStreamIsCapturing(s, &cs), "capture status");
-    c->pf_pending = 1;
-    c->pf_captured = cs != hipStreamCaptureStatusNone;
-    return MOE_OK;
-}
 
-moe_status_t moe_prefetch_join(moe_cache_t *c, void *stream) {
-    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
-    return join_prefetch(c, static_cast<hipStream_t>(stream));
-}
-
-moe_status_t moe_cache_set_cpu_threads(moe_cache_t *c, int32_t threads) {
-    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
-    if (threads < 0 || threads > 1024) return fail(MOE_INVALID_ARG, "threads %d outside [0, 1024]", threads);
-    if (threads > 0) {
-        if (c->nb == 0 || c->d.max_tokens < 1)
-            return fail(MOE_INVALID_ARG, "the hybrid step needs weight banks and max_tokens > 0");
-        if (c->d.weight_format != MOE_FMT_BF16 || c->d.hidden % 16 || c->d.ffn % 16)
-            return fail(MOE_UNSUPPORTED, "the CPU experts take bf16 rows with hidden and ffn multiples of 16");
-    }
-    HIP_TRY(hipDeviceSynchronize(), "sync");
-    if (c->cpu) {
-        cpu_experts_destroy(c->cpu);
-        c->cpu = nullptr;
-    }
-    if (threads == 0) return MOE_OK;
-    if (!c->hyb_host) {
-        const size_t TK = (size_t)c->d.max_tokens * c->d.max_top_k, TH = (size_t)c->d.max_tokens * c->d.hidden;
-        const size_t o_e = 0, o_s = align_up(TK * 4), o_w = o_s + align_up(TK * 4), o_x = o_w + align_up(TK * 4),
-                     o_p = o_x + align_up(TH * 2), total = o_p + align_up(TH * 4);
-        void *hp = nullptr;
-        hipError_t e = hipHostMalloc(&hp, total, hipHostMallocMapped);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(MOE_OUT_OF_MEMORY, "hybrid staging (%zu B pinned): %s", total, hipGetErrorString(e));
-        }
-        c->hyb_host = hp;
-        uint8_t *b = static_cast<uint8_t *>(hp);
-        c->h_experts = reinterpret_cast<int32_t *>(b + o_e);
-        c->h_slots = reinterpret_cast<int32_t *>(b + o_s);
-        c->h_w = reinterpret_cast<float *>(b + o_w);
-        c->h_x = reinterpret_cast<uint16_t *>(b + o_x);
-        c->h_partial = reinterpret_cast<float *>(b + o_p);
-        void *dp = nullptr;
-        HIP_TRY(hipHostGetDevicePointer(&dp, c->h_partial, 0), "map the hybrid partial");
-        c->d_partial = static_cast<float *>(dp);
-        c->cpu_ids.resize(TK);
-        HIP_TRY(hipEventCreateWithFlags(&c->hyb_ready, hipEventDisableTiming), "hybrid event");
-    }
-    c->cpu = cpu_experts_create(threads);
-    return MOE_OK;
-}
-
-moe_status_t moe_cpu_experts(int32_t threads, int32_t T, int32_t K, int32_t H, int32_t F,
-                             const int32_t *experts, const float *w, const void *x,
-                             const void *w13_rows, const void *w2_rows, float *partial) {
-    if (threads < 1 || threads > 1024 || T < 0 || K < 1 || H < 16 || F < 16 || H % 16 || F % 16)
-        return fail(MOE_INVALID_ARG, "bad CPU expert sizes (threads %d, T %d, K %d, H %d, F %d)", threads,
-                    T, K, H, F);
-    if (T == 0) return MOE_OK;
-    if (!experts || !w || !x || !w13_rows || !w2_rows || !partial)
-        return fail(MOE_INVALID_ARG, "NULL CPU expert buffer");
-    CpuRoutes r{};
-    r.T = T;
-    r.K = K;
-    r.H = H;
-    r.F = F;
-    r.expert = experts;
-    r.w = w;
-    r.x = static_cast<const uint16_t *>(x);
-    r.w13 = static_cast<const uint8_t *>(w13_rows);
-    r.w2 = static_cast<const uint8_t *>(w2_rows);
-    r.partial = partial;
-    CpuExperts *p = cpu_experts_create(threads);
-    cpu_experts_run(p, r);
-    cpu_experts_destroy(p);
-    return MOE_OK;
-}
-
-moe_status_t moe_layer_decode_hybrid(moe_cache_t *c, int32_t layer, const void *x, const float *logits,
-                                     int32_t T, int32_t K, const moe_shared_t *shared, int32_t max_fetch,
-                                     void *out, int32_t *ids_out, float *w_out, void *stream) {
-    if (!c) return fail(MOE_INVALID_ARG, "NULL cache");
-    if (!c->cpu) return fail(MOE_INVALID_ARG, "no CPU experts: call moe_cache_set_cpu_threads first");
-    if (layer < 0 || layer >= c->d.num_layers)
-        return fail(MOE_INVALID_ARG, "layer %d outside [0, %d)", layer, c->d.num_layers);
-    if (T < 0 || T > c->d.max_tokens) return fail(MOE_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, c->d.max_tokens);
-    if (K < 1 || K > c->d.max_top_k || K > c->d.num_experts)
-        return fail(MOE_INVALID_ARG, "K=%d outside [1, %d]", K, c->d.max_top_k);
-    if (T > 0 && (!x || !logits || !out)) return fail(MOE_INVALID_ARG, "NULL layer buffer");
-    if (T > 0 && !aligned16(x)) return fail(MOE_INVALID_ARG, "x must be 16-byte aligned");
-    int Fs = 0;
-    if (shared) {
-        moe_status_t st = check_shared(shared, c->d.hidden, c->d.ffn, &Fs);
-        if (st != MOE_OK) return st;
-        if (Fs > c->shared_ffn_cap)
-            return fail(MOE_UNSUPPORTED, "shared ffn %d > the cache's workspace width %d", Fs, c->shared_ffn_cap);
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        HIP_TRY(hipStreamIsCapturing(s, &cs), "capture status");
-        if (cs != hipStreamCaptureStatusNone)
-            return fail(MOE_INVALID_ARG, "the hybrid step waits on the host and cannot be captured");
-    }
-    const int H = c->d.hidden, E = c->d.num_experts, R = T * K;
-    int32_t *ids = ids_out ? ids_out : c->ws_ids;
-    float *w = w_out ? w_out : c->ws_w;
-    const uint16_t *xb = static_cast<const uint16_t *>(x);
-    const size_t lb = (size_t)layer * c->nb;
-
-    // Cache decision: top-k, the original ids and x to the host, admission
-    // (capped fetch), the rewritten ids to the host.
-    HIP_TRY(launch_topk(logits, T, E, K, ids, w, s), "top-k launch");
-    HIP_TRY(hipMemcpyAsync(c->h_experts, ids, (size_t)R * 4, hipMemcpyDeviceToHost, s), "ids to host");
-    HIP_TRY(hipMemcpyAsync(c->h_w, w, (size_t)R * 4, hipMemcpyDeviceToHost, s), "weights to host");
-    HIP_TRY(hipMemcpyAsync(c->h_x, x, (size_t)T * H * 2, hipMemcpyDeviceToHost, s), "x to host");
-    moe_status_t st = launch_admit_checked(c, layer, ids, R, max_fetch, s, c->ws_route_plan);
-    if (st != MOE_OK) return st;
-    HIP_TRY(hipMemcpyAsync(c->h_slots, ids, (size_t)R * 4, hipMemcpyDeviceToHost, s), "slots to host");
-    HIP_TRY(hipEventRecord(c->hyb_ready, s), "record hybrid ready");
-
-    // The CPU half: waits for the decision, then runs the -1 routes with a
-    // valid expert id on host cores into the pinned partial.  Folding the
-    // partial into the fp32 term is issued right before the combine.
-    auto cpu_half = [&]() -> hipError_t {
-        hipError_t e = hipEventSynchronize(c->hyb_ready);
-        if (e != hipSuccess) return e;
-        for (int i = 0; i < R; ++i) {
-            const int ex = c->h_experts[i];
-            c->cpu_ids[i] = (c->h_slots[i] < 0 && ex >= 0 && ex < E) ? ex : -1;
-        }
-        CpuRoutes r{};
-        r.T = T;
-        r.K = K;
-        r.H = H;
-        r.F = c->d.ffn;
-        r.expert = c->cpu_ids.data();
-        r.w = c->h_w;
-        r.x = c->h_x;
-        r.w13 = c->host_rows[lb + 0];
-        r.w2 = c->host_rows[lb + 1];
-        r.partial = c->h_partial;
-        cpu_experts_run(c->cpu, r);
-        return hipSuccess;
-    };
-    auto fold = [&]() { return launch_hybrid_add(c->ws_addend, c->d_partial, T * H, shared ? 1 : 0, s); };
-    const bool serial = c->d.overlap == 0;
-    if (serial) {
-        // the debug order: the CPU wait before the GPU work
-        hipError_t e = cpu_half();
-        if (e != hipSuccess) return hip_fail(e, "hybrid CPU half");
-    }
-    // GPU half: the capped gather, the shared term, the GPU routes; the CPU
-    // partial joins the fp32 term right before the combine adds it.
-    st = launch_gather_checked(c, s);
-    if (st != MOE_OK) return st;
-    if (shared) {
-        hipError_t e = shared_sequence(shared, H, Fs, xb, T, c->ws_addend, c->ws_shared, s);
-        if (e != hipSuccess) return hip_fail(e, "shared launch");
-    }
-    const BeforeAddend cpu_join = [&]() {
-        hipError_t e = serial ? hipSuccess : cpu_half();
-        return e != hipSuccess ? e : fold();
-    };
-    HIP_TRY(routed_sequence(slot_pool_view(c), xb, ids, w, T, K, c->ws_addend, static_cast<uint16_t *>(out),
-                            c->ws_routed, s, &cpu_join),
-            "hybrid routed launch");
-    return MOE_OK;
-}
 
 moe_status_t moe_cache_stats(moe_cache_t *c, int32_t layer, int64_t *out, void *stream) {
     if (!c || !out) return fail(MOE_INVALID_ARG, "NULL cache or output");
