@@ -57,11 +57,16 @@ def log(*a):
 
 
 def kernel_sources_hash() -> str:
+    """Hash of the device-code sources (kernels and the headers they
+    include); the host-side C-ABI files do not change what a kernel moves."""
     import glob
     import hashlib
 
+    csrc = os.path.join(ROOT, "expert_slot_cache_moe_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "k_*.hip")) + glob.glob(os.path.join(csrc, "*.inc"))
+                   + [os.path.join(csrc, "moe_internal.h")])
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "expert_slot_cache_moe_amd", "csrc", "*"))):
+    for f in files:
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
