@@ -56,14 +56,20 @@ class SlotCacheLayers:
             max_routes=max_routes, max_tokens=max_tokens, max_top_k=max_top_k, overlap=overlap,
             gather_workgroups=gather_workgroups, host_banks=self.host, slot_banks=self.slot_banks)
 
+    def _shared(self, layer):
+        # the library checks the layer; an out-of-range one gets no shared expert here
+        if self.shared is None or not 0 <= layer < len(self.shared):
+            return None
+        return self.shared[layer]
+
     def decode(self, layer, x, logits, K, out, ids_out=None, w_out=None, max_fetch=-1, stream=None):
-        sh = self.shared[layer] if self.shared is not None else None
+        sh = self._shared(layer)
         moe_layer_decode(self.cache, layer, x, logits, K, out, shared=sh, max_fetch=max_fetch,
                          ids_out=ids_out, w_out=w_out, stream=stream)
 
     def decode_hybrid(self, layer, x, logits, K, out, ids_out=None, w_out=None, max_fetch=-1,
                       stream=None):
-        sh = self.shared[layer] if self.shared is not None else None
+        sh = self._shared(layer)
         moe_layer_decode_hybrid(self.cache, layer, x, logits, K, out, shared=sh, max_fetch=max_fetch,
                                 ids_out=ids_out, w_out=w_out, stream=stream)
 

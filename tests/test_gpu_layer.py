@@ -526,3 +526,49 @@ def test_shared_on_the_side_stream_equals_serial(T, K, fmt):
     finally:
         for lay in lays:
             lay.close()
+
+
+@pytest.mark.parametrize("overlap", [0, 1, 2, 3])
+def test_empty_layer_step_ticks_the_clock_in_every_schedule(overlap):
+    """T = 0 through moe_layer_decode (and the hybrid step): one admission
+    of no routes (a clock tick and a call), nothing written to the output."""
+    lay, host, sh = _tiny_layers(overlap, True, seed=23, E=8, S=4, T=2, K=2)
+    oc = oracle.OracleCache(1, 8, 4)
+    out = torch.full((2, 64), 7, dtype=torch.int16, device="cuda")
+    x = torch.zeros((2, 64), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((2, 8), dtype=torch.float32, device="cuda")
+    try:
+        lay.decode(0, x[:0], lg[:0], 2, out[:0])
+        oc.admit(0, [])
+        m.moe_cache_set_cpu_threads(lay.cache, 2)
+        lay.decode_hybrid(0, x[:0], lg[:0], 2, out[:0])
+        oc.admit(0, [])
+        torch.cuda.synchronize()
+        st = m.moe_cache_read_state(lay.cache)
+        assert st["clock"] == oc.state()["clock"] == 2
+        np.testing.assert_array_equal(st["stats"], oc.state()["stats"])
+        assert (out == 7).all()
+    finally:
+        lay.close()
+
+
+def test_layer_step_rejects_bad_arguments_before_launching():
+    lay, host, sh = _tiny_layers(2, True, seed=24, E=8, S=4, T=2, K=2)
+    x = torch.zeros((4, 64), dtype=torch.int16, device="cuda")
+    lg = torch.zeros((4, 8), dtype=torch.float32, device="cuda")
+    out = torch.empty((4, 64), dtype=torch.int16, device="cuda")
+    try:
+        with pytest.raises(m.MoeError):
+            lay.decode(0, x[:2], lg[:2], 3, out[:2])         # K > max_top_k
+        with pytest.raises(m.MoeError):
+            lay.decode(0, x, lg, 2, out)                     # T > max_tokens
+        with pytest.raises(m.MoeError):
+            lay.decode(1, x[:1], lg[:1], 2, out[:1])         # layer outside [0, L)
+        xb = torch.zeros(2 * 64 + 1, dtype=torch.int16, device="cuda")[1:].view(2, 64)
+        with pytest.raises(m.MoeError):
+            lay.decode(0, xb, lg[:2], 2, out[:2])            # x not 16-byte aligned
+        with pytest.raises(m.MoeError):
+            m.moe_cache_set_schedule(lay.cache, -1)
+        assert m.moe_cache_read_state(lay.cache)["clock"] == 0
+    finally:
+        lay.close()
