@@ -184,9 +184,12 @@ moe_status_t moe_query_widths(int32_t R, int32_t E, int32_t one_call_width, int3
 
 /* Validates the description, allocates the cache's device state (slot map,
  * slot owners, stamps, LRU order, clock, miss plan, statistics, histogram,
- * layer workspace), creates its side stream and its ready/done events --
- * before any capture -- and leaves every slot empty.  Uses the current
- * device.  Errors: MOE_INVALID_ARG (bad sizes, null or unaligned
+ * demand recency, prefetch fill plan, layer workspace), creates its side
+ * stream, its prefetch stream and their events -- before any capture --
+ * and leaves every slot empty.  Uses the current device.  A cache whose
+ * full-width prefetch kernel would not fit the LDS is still created (only
+ * moe_prefetch refuses).  The cache is not thread-safe: one caller issues
+ * its calls, on one compute stream.  Errors: MOE_INVALID_ARG (bad sizes, null or unaligned
  * pointers, overlap outside 0..3), MOE_UNSUPPORTED (shapes the kernels lack,
  * LDS overflow), MOE_OUT_OF_MEMORY, MOE_HIP_ERROR. */
 moe_status_t moe_cache_create(const moe_cache_desc_t *desc, moe_cache_t **out);
@@ -196,7 +199,8 @@ moe_status_t moe_cache_create(const moe_cache_desc_t *desc, moe_cache_t **out);
  * MOE_INVALID_ARG (overlap outside 0..3). */
 moe_status_t moe_cache_set_schedule(moe_cache_t *cache, int32_t overlap);
 
-/* Synchronises the cache's streams and frees what create allocated. */
+/* Synchronises the device, stops the cache's host threads, and frees what
+ * create and moe_cache_set_cpu_threads allocated. */
 void moe_cache_destroy(moe_cache_t *cache);
 
 /* The cache's slot banks as a pool for moe_routed_decode. */
