@@ -68,7 +68,7 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build the HIP library first "
-                "(python -c 'import __graft_entry__ as g; g.build()')")
+                "(python -m expert_slot_cache_moe_amd.build)")
         L = C.CDLL(LIB_PATH)
         P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         st = C.c_int
