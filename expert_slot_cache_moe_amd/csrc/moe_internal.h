@@ -116,6 +116,31 @@ __device__ __forceinline__ float group_total(float v) {
     return __uint_as_float(u);
 }
 
+// Exclusive prefix count of `f` over a workgroup of THREADS threads;
+// `total` gets the sum.  Every thread must call it: it holds two barriers.
+// wsum: THREADS / 64 ints of LDS.
+template <int THREADS>
+__device__ __forceinline__ int block_scan_flags(bool f, int32_t *wsum, int &total) {
+    constexpr int kW = THREADS / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const uint64_t m = __ballot(f);
+    const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (lane == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        const int v = wsum[w];
+        off += (w < wave) ? v : 0;
+        tot += v;
+    }
+    __syncthreads();
+    total = tot;
+    return off + pre;
+}
+
 // Maximum of a 32-bit unsigned value over the wave, returned to every lane:
 // a max-scan with the shift/broadcast pattern (lane 63 ends with the
 // maximum), then read back from lane 63.
