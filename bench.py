@@ -20,7 +20,9 @@ Also reported:
   roofline_gemv  the routed expert kernels (gate/up + down) against HBM.
   admission_us   admission-only benchmark: 48 per-layer caches of 512
                  experts pre-filled into 2100 slots, 48 admissions per
-                 graph, 40 replays, microseconds per admission by routes.
+                 graph, 40 replays, microseconds per admission by routes;
+                 admission_us_one_call_width_128 repeats 130, 160 and 240
+                 routes with the one-call width at 128 (chunked queries).
   cpu_baseline   the oracle (plain C, one thread) on a bounded sample of
                  the same decode workload.
 
@@ -223,16 +225,23 @@ def wide_gemv_benchmark(torch, m, seed=0):
     return res
 
 
-def admission_benchmark(torch, m, W, replays=40, layers=48):
+# The one-call/chunked crossover re-measured: these batches (130, 160 and
+# 240 routes) again with the one-call width lowered to 128, so that they
+# are admitted in 128-expert chunks instead of one query.
+ADMISSION_CHUNKED_BATCHES = (13, 16, 24)
+
+
+def admission_benchmark(torch, m, W, replays=40, layers=48, one_call_width=256, batches=None):
     res = {}
-    caches = [m.moe_cache_create(num_layers=1, num_experts=512, num_slots=2100, max_routes=1280)
+    caches = [m.moe_cache_create(num_layers=1, num_experts=512, num_slots=2100, max_routes=1280,
+                                 one_call_width=one_call_width)
               for _ in range(layers)]
     try:
         full = torch.arange(512, dtype=torch.int32, device="cuda")
         for c in caches:
             m.moe_admit(c, 0, full.clone())
         torch.cuda.synchronize()
-        for req in W.ADMISSION_BATCHES:
+        for req in (batches or W.ADMISSION_BATCHES):
             R = req * 10
             src = torch.from_numpy(np.stack([W.admission_ids(l, req) for l in range(layers)])).cuda()
             work = torch.empty_like(src)
@@ -931,6 +940,8 @@ def main():
         del a, b
     wide = None if args.no_wide else wide_gemv_benchmark(torch, m)
     adm = None if args.no_admission else admission_benchmark(torch, m, W)
+    adm_chunked = None if args.no_admission else admission_benchmark(
+        torch, m, W, one_call_width=128, batches=ADMISSION_CHUNKED_BATCHES)
     look = None if args.no_lookahead else lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, W_, n_tok)
     sched = (None if args.no_schedules or args.overlap != 2
              else schedule_benchmark(torch, m, lay, snap, x_all, lg_all, W_, n_tok))
@@ -984,6 +995,7 @@ def main():
                           "launches": GEMV_REPLAYS * GEMV_PASSES * L,
                           "d2d_copy_same_bytes_gbs": round(d2d_gbs, 1)},
         "admission_us": adm,
+        "admission_us_one_call_width_128": adm_chunked,
         "routed_gemv_wide": wide,
         "lookahead": look,
         "schedules": sched,
