@@ -44,7 +44,6 @@ constexpr int kSlab = 128;                      // contraction elements per swee
 // run 7-10% faster than with four-wave workgroups).
 constexpr int kMWaves = 1;
 constexpr int kMThreads = kMWaves * kWave;
-constexpr int kRowsPerBlock = kMWaves * kTile;  // output rows of one workgroup
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -154,12 +153,15 @@ __device__ __forceinline__ void load_b(const uint16_t *row, int e0, u32x4 (&b)[4
     for (int i = 0; i < 4; ++i) b[i] = src[i];
 }
 
-// Slabs a wave keeps in flight: a bf16 slab carries 8 KB of a wave's gate
-// and up rows, a 4-bit one 2.3 KB, so 4-bit waves run four slabs ahead and
-// bf16 waves two.  Slab s lives in buffer s % NB; once it is consumed, the
-// buffer is refilled with slab s + NB, so loads stay in flight while the
-// matrix cores work.
-template <int FMT> struct Ahead { static constexpr int v = FMT == MOE_FMT_BF16 ? 2 : 4; };
+// A gate/up wave takes UT row tiles (16 gate and 16 up rows each) that share
+// the activation operand, and keeps NB slabs of them in flight: slab s lives
+// in buffer s % NB; once it is consumed, the buffer is refilled with slab
+// s + NB, so loads stay in flight while the matrix cores work.  A bf16 slab
+// of one tile carries 8 KB, a 4-bit one 2.3 KB.  The launcher picks (UT, NB)
+// per format and width: measured on MI355X, E2M1 runs best with one tile
+// and three slabs ahead, MXFP4 with two tiles and two slabs, bf16 with one
+// tile and two slabs, or two tiles at FFN widths of 1024 and more (3% on
+// the prefill chunks, 4% slower at width 256).
 
 // The group table entry gi (row -1 past the last group).
 struct GroupEntry {
@@ -178,7 +180,7 @@ struct GroupEntry {
     }
 };
 
-// gate/up + SwiGLU, 16 rows j per wave, for the groups blockIdx.y,
+// gate/up + SwiGLU, 16 * UT rows j per wave, for the groups blockIdx.y,
 // blockIdx.y + gridDim.y, ...: h[route][j] = bf16(silu(g) * u) for every
 // route of a group.  The grid holds about as many workgroups as the device
 // keeps resident; the group table is a prefix of valid groups followed by
@@ -187,15 +189,14 @@ struct GroupEntry {
 // are requested before its route list and token rows (two dependent
 // loads) are read.  Tokens go through the matrix cores 16 at a time; a
 // group of more than 16 routes streams its rows once per 16.
-template <int FMT>
+template <int FMT, int UT, int NB>
 __global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, Items items,
                                                                const uint16_t *__restrict__ x,
                                                                uint16_t *__restrict__ h) {
-    constexpr int NB = Ahead<FMT>::v;
     const int H = pool.H, F = pool.F, K = items.K;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int c = lane & (kTile - 1), q = lane / kTile;
-    const int j0 = blockIdx.x * kRowsPerBlock + wave * kTile;
+    const int j0 = (blockIdx.x * kMWaves + wave) * kTile * UT;
     if (j0 >= F) return;
     const int gmax = min(items.n, pool.num_rows);
     const int nslab = H / kSlab;
@@ -207,12 +208,15 @@ __global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, It
         const int64_t row = cur.row;
         const int32_t *list = items.grp_routes + cur.start;
         for (int base = 0; base < cur.count; base += kTile) {
-            ASlab<FMT> wg[NB], wu[NB];
+            ASlab<FMT> wg[NB][UT], wu[NB][UT];
             u32x4 xb[NB][4];
             auto load_w = [&](int s, int bfr) {
                 const int e0 = s * kSlab + 32 * q;
-                wg[bfr].load(pool, row, 0, j0 + c, e0);
-                wu[bfr].load(pool, row, 0, F + j0 + c, e0);
+#pragma unroll
+                for (int t = 0; t < UT; ++t) {
+                    wg[bfr][t].load(pool, row, 0, j0 + kTile * t + c, e0);
+                    wu[bfr][t].load(pool, row, 0, F + j0 + kTile * t + c, e0);
+                }
             };
 #pragma unroll
             for (int bfr = 0; bfr < NB; ++bfr)
@@ -223,19 +227,24 @@ __global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, It
 #pragma unroll
             for (int bfr = 0; bfr < NB; ++bfr)
                 if (bfr < nslab) load_b(xr, bfr * kSlab + 32 * q, xb[bfr]);
-            f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
+            f32x4 ag[UT], au[UT];
+#pragma unroll
+            for (int t = 0; t < UT; ++t) ag[t] = au[t] = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int s0 = 0; s0 < nslab; s0 += NB) {
 #pragma unroll
                 for (int bfr = 0; bfr < NB; ++bfr) {
                     const int s = s0 + bfr;
                     if (s < nslab) {
-                        u32x4 ga[4], ua[4];
-                        wg[bfr].expand(ga);
-                        wu[bfr].expand(ua);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            ag = mfma(ga[i], xb[bfr][i], ag);
-                            au = mfma(ua[i], xb[bfr][i], au);
+                        for (int t = 0; t < UT; ++t) {
+                            u32x4 ga[4], ua[4];
+                            wg[bfr][t].expand(ga);
+                            wu[bfr][t].expand(ua);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                ag[t] = mfma(ga[i], xb[bfr][i], ag[t]);
+                                au[t] = mfma(ua[i], xb[bfr][i], au[t]);
+                            }
                         }
                         if (s + NB < nslab) {
                             load_w(s + NB, bfr);
@@ -244,14 +253,16 @@ __global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, It
                     }
                 }
             }
-            // lane holds rows j0 + 4q + i (i < 4) of token column c
+            // lane holds rows j0 + 16t + 4q + i (i < 4) of token column c
             if (base + c < cur.count) {
                 const int64_t r = list[base + c];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float g = ag[i] * glob, u = au[i] * glob;
-                    h[r * F + j0 + 4 * q + i] = f32_to_bf16(silu_mul(g, u));
-                }
+                for (int t = 0; t < UT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float g = ag[t][i] * glob, u = au[t][i] * glob;
+                        h[r * F + j0 + kTile * t + 4 * q + i] = f32_to_bf16(silu_mul(g, u));
+                    }
             }
         }
         cur = nxt;
@@ -468,25 +479,31 @@ int group_rows(int max_items, int cols, int resident_wgs) {
     if (resident_wgs <= 0) return max_items;
     return std::max(1, std::min(max_items, resident_wgs / std::max(cols, 1)));
 }
+
+// F is a multiple of kSlab (group_mfma_supported), so every wave's UT row
+// tiles lie inside the FFN width.
+template <int FMT, int UT, int NB>
+hipError_t launch_up_shape(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
+                           uint16_t *h, hipStream_t s) {
+    using namespace mfma_detail;
+    static_assert(kSlab % (kMWaves * kTile * UT) == 0, "row tiles of a workgroup divide a slab");
+    static int res[16];
+    const int rows = kMWaves * kTile * UT;
+    const int cols = pool.F / rows;
+    const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<FMT, UT, NB>, res)));
+    hipLaunchKernelGGL((up_mfma_kernel<FMT, UT, NB>), grid, dim3(kMThreads), 0, s, pool, items, x, h);
+    return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_up_mfma(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
                           uint16_t *h, hipStream_t s) {
     using namespace mfma_detail;
     if (max_items <= 0) return hipSuccess;
-    static int res_bf16[16], res_e2m1[16], res_mx[16];
-    const int cols = (pool.F + kRowsPerBlock - 1) / kRowsPerBlock;
-    if (pool.fmt == MOE_FMT_MXFP4) {
-        const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<MOE_FMT_MXFP4>, res_mx)));
-        hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_MXFP4>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
-    } else if (pool.fmt == MOE_FMT_BF16) {
-        const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<MOE_FMT_BF16>, res_bf16)));
-        hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_BF16>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
-    } else {
-        const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<MOE_FMT_E2M1>, res_e2m1)));
-        hipLaunchKernelGGL(up_mfma_kernel<MOE_FMT_E2M1>, grid, dim3(kMThreads), 0, s, pool, items, x, h);
-    }
-    return hipGetLastError();
+    if (pool.fmt == MOE_FMT_MXFP4) return launch_up_shape<MOE_FMT_MXFP4, 2, 2>(pool, items, max_items, x, h, s);
+    if (pool.fmt == MOE_FMT_E2M1) return launch_up_shape<MOE_FMT_E2M1, 1, 3>(pool, items, max_items, x, h, s);
+    if (pool.F >= 1024) return launch_up_shape<MOE_FMT_BF16, 2, 2>(pool, items, max_items, x, h, s);
+    return launch_up_shape<MOE_FMT_BF16, 1, 2>(pool, items, max_items, x, h, s);
 }
 
 hipError_t launch_down_mfma(const PoolView &pool, const Items &items, int max_items, const uint16_t *h,
