@@ -129,15 +129,28 @@ def make_trace(torch, W, n, seed=0):
     return (torch.from_numpy(lg).cuda(), torch.from_numpy(xs.view(np.int16)).cuda())
 
 
-def capture(torch, lay, x_st, lg_st, out, ids=None, w=None, pairs=None):
-    """The 40-layer token graph; with `pairs` (two lists of L created
-    events), each layer step is preceded by an empty event pair (two
-    event-record nodes back to back)."""
+def stage_inputs(torch, pairs, step):
+    """Inside a capture: each (source [tokens, ...], staging [...]) pair's
+    row `step` (a one-element device tensor) copied into the staging
+    buffer, then the step advanced, so that a replay of the token graph
+    needs no host-issued work: the device-side counter picks the token."""
+    for src, dst in pairs:
+        torch.index_select(src, 0, step, out=dst.unsqueeze(0))
+    step.add_(1)
+
+
+def capture(torch, lay, x_st, lg_st, out, inputs, ids=None, w=None, pairs=None):
+    """The 40-layer token graph, starting with the token's inputs staged by
+    the device-side step counter (inputs = (x_all, lg_all, step)); with
+    `pairs` (two lists of L created events), each layer step is preceded
+    by an empty event pair (two event-record nodes back to back)."""
     import expert_slot_cache_moe_amd as m
 
+    x_all, lg_all, step = inputs
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
+        stage_inputs(torch, ((x_all, x_st), (lg_all, lg_st)), step)
         for l in range(L):
             if pairs is not None:
                 m.moe_record_event(pairs[0][l], stream)
@@ -284,9 +297,12 @@ def lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok, seed=0
     x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
     lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
     pr_st = torch.empty((L, K), dtype=torch.int32, device="cuda")
+    pred = torch.empty((n_tok, L, K), dtype=torch.int32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int64, device="cuda")
     out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
+        stage_inputs(torch, ((x_all, x_st), (lg_all, lg_st), (pred, pr_st)), step)
         for l in range(L):
             lay.decode(l, x_st[l], lg_st[l], K, out[l], stream=stream)
             if l + 1 < L:
@@ -298,7 +314,8 @@ def lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok, seed=0
         rng = np.random.default_rng([seed, int(round(acc * 1000))])
         keep = torch.from_numpy(rng.random((n_tok, L, K)) < acc).cuda()
         rnd = torch.from_numpy(rng.integers(0, E, (n_tok, L, K)).astype(np.int32)).cuda()
-        pred = torch.where(keep, true_ids, rnd)
+        pred.copy_(torch.where(keep, true_ids, rnd))
+        step.fill_(first)
         m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"],
                                 freq=snap["freq"], dlast=snap["dlast"],
                                 last_demand=snap["last_demand"])
@@ -306,9 +323,6 @@ def lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok, seed=0
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(first, n_tok):
-            x_st.copy_(x_all[t])
-            lg_st.copy_(lg_all[t])
-            pr_st.copy_(pred[t])
             graph.replay()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
@@ -338,9 +352,11 @@ def schedule_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok):
     x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
     lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
     out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    step = torch.zeros(1, dtype=torch.int64, device="cuda")
     for ov, what in SCHEDULES:
         m.moe_cache_set_schedule(lay.cache, ov)
-        graph = capture(torch, lay, x_st, lg_st, out)
+        graph = capture(torch, lay, x_st, lg_st, out, (x_all, lg_all, step))
+        step.fill_(first)
         m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"],
                                 freq=snap["freq"], dlast=snap["dlast"],
                                 last_demand=snap["last_demand"])
@@ -348,8 +364,6 @@ def schedule_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(first, n_tok):
-            x_st.copy_(x_all[t])
-            lg_st.copy_(lg_all[t])
             graph.replay()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
@@ -793,12 +807,11 @@ def main():
     x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
     lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
     out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
-    graph = capture(torch, lay, x_st, lg_st, out)
+    tok = torch.zeros(1, dtype=torch.int64, device="cuda")   # the device-side step counter
+    graph = capture(torch, lay, x_st, lg_st, out, (x_all, lg_all, tok))
 
     def step(t):
-        x_st.copy_(x_all[t])
-        lg_st.copy_(lg_all[t])
-        graph.replay()
+        graph.replay()                     # stages token t: the counter holds t
 
     for t in range(W_):
         step(t)
@@ -831,13 +844,12 @@ def main():
     for e in pairs[0] + pairs[1]:
         e.record()                              # creates the events before capture
     torch.cuda.synchronize()
-    tgraph = capture(torch, lay, x_st, lg_st, out, ids_l, w_l, pairs)
+    tgraph = capture(torch, lay, x_st, lg_st, out, (x_all, lg_all, tok), ids_l, w_l, pairs)
+    tok.fill_(W_)
     staged = args.overlap == 2
     k1_ms, pair_ms, fetch_l = [], [], []
     prev = m.moe_cache_read_state(lay.cache)["stats"]
     for t in range(W_, n_tok):
-        x_st.copy_(x_all[t])
-        lg_st.copy_(lg_all[t])
         tgraph.replay()
         torch.cuda.synchronize()
         ms = m.moe_cache_timing(lay.cache).astype(np.float64)
