@@ -88,6 +88,8 @@ def _routed_gpu(pool, x, idx, w, H, addend=None):
     (1, 1024, 256, 40, 1, 2),       # e2m1, decode path
     (1, 1024, 256, 40, 33, 2),      # e2m1, grouped path
     (0, 4096, 1024, 10, 7, 6),      # prefill-chunk shape
+    (0, 128, 1024, 3, 40, 2),       # FFN 1024 (two gate/up row tiles per wave), groups of 20+ routes
+    (2, 256, 1024, 3, 40, 2),       # mxfp4 at FFN 1024, groups of 20+ routes
     (1, 64, 64, 6, 3, 3),           # e2m1, smallest rows
     (2, 1024, 256, 40, 1, 2),       # mxfp4, decode path
     (2, 2048, 512, 12, 1, 8),       # mxfp4, shared-expert decode shape
