@@ -24,7 +24,8 @@ Also reported:
                  admission_us_one_call_width_128 repeats 130, 160 and 240
                  routes with the one-call width at 128 (chunked queries).
   cpu_baseline   the oracle (plain C, one thread) on a bounded sample of
-                 the same decode workload.
+                 the same decode workload; its "admission" entry times the
+                 oracle's admission alone on the admission-only workload.
 
 Profile summaries: with --launch-log the run also writes which launches
 the timed and instrumented passes made (and this line); the summaries in
@@ -416,6 +417,38 @@ def hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, first):
         log(f"[bench] hybrid, fetch cap {cap}: {res[-1]}")
     m.moe_cache_set_cpu_threads(lay.cache, 0)
     return {"threads": HYBRID_THREADS, "tokens": n, "runs": res}
+
+
+# Oracle admission timing: the admission-only workload's one-layer cache
+# (512 experts pre-filled into 2100 slots), single-threaded, µs per
+# admission at these batches (10, 480 and 1280 routes).
+CPU_ADMISSION_BATCHES = (1, 48, 128)
+
+
+def cpu_admission_baseline(W, steps=200):
+    """The oracle's admission alone (it is sequential), on the same ids the
+    GPU admission-only benchmark uses: µs per admission by routes."""
+    import oracle
+
+    res = {}
+    warm = oracle.OracleCache(1, 512, 2100)      # warm-up (library, caches, clocks), not timed
+    warm.admit(0, np.arange(512, dtype=np.int32))
+    for i in range(100):
+        warm.admit(0, W.admission_ids(i, 48))
+    for req in CPU_ADMISSION_BATCHES:
+        oc = oracle.OracleCache(1, 512, 2100)
+        oc.admit(0, np.arange(512, dtype=np.int32))
+        ids = [W.admission_ids(i, req) for i in range(steps)]
+        for r in ids[:10]:                       # warm-up, not timed
+            oc.admit(0, r)
+        t0 = time.perf_counter()
+        for r in ids:
+            oc.admit(0, r)
+        res[str(req * 10)] = round((time.perf_counter() - t0) / steps * 1e6, 2)
+    return {"value": res["480"], "unit": "µs/admission at 480 routes", "by_routes": res, "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} admissions per batch size on one cache of 512 experts pre-filled into 2100 "
+                      "slots (all hits), single-threaded C oracle"}
 
 
 def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
@@ -963,6 +996,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(W, W_, args.cpu_sample_tokens)
+        cpu["admission"] = cpu_admission_baseline(W)
 
     ratios = traffic_ratios()
     value = L * K_ / dt
