@@ -758,24 +758,43 @@ gather_traffic_ratio = {miss_traffic / stage1_kib:.4f}
 routed_traffic_ratio = {gemv_traffic / gemv_kib:.4f}""")
 
 
-def summarize_counters(csv_path):
-    """Mean value per dispatch of every counter of a rocprofv3 --pmc run,
-    per kernel of the library (template arguments kept: the weight format)."""
+def summarize_counters(csv_paths):
+    """Mean value per dispatch of every counter of one or more rocprofv3
+    --pmc runs, per kernel of the library (template arguments kept: weight
+    format, row tiles, slabs ahead), then per wave of the grouped kernels:
+    the share of wave cycles stalled on outstanding loads
+    (SQ_WAIT_INST_ANY) and issuing VALU, VALU and MFMA instructions."""
     import csv
     import re
 
     acc = {}
-    for r in csv.DictReader(open(csv_path)):
-        name = r["Kernel_Name"]
-        k = _short(name)
-        if not k:
-            continue
-        m_ = re.search(r"<(\d)>", name)
-        key = k + (f"<{m_.group(1)}>" if m_ else "")
-        acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            k = _short(name)
+            if not k:
+                continue
+            m_ = re.search(r"<([0-9, ]+)>", name)
+            key = k + (f"<{m_.group(1)}>" if m_ else "")
+            acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     for key in sorted(acc):
         vals = "  ".join(f"{c}={np.mean(v):.4g}" for c, v in sorted(acc[key].items()))
         print(f"{key}  (dispatches {max(len(v) for v in acc[key].values())})  {vals}")
+    need = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU",
+            "SQ_INSTS_MFMA")
+    rows = []
+    for key in sorted(acc):
+        c = {n: np.mean(v) for n, v in acc[key].items()}
+        if "mfma" not in key or any(n not in c for n in need) or c["SQ_WAVES"] <= 0:
+            continue
+        rows.append(f"#   {key}: {c['SQ_WAVES']:.0f} waves a dispatch; stalled on outstanding loads "
+                    f"{100 * c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.0f}% of wave cycles, VALU issuing "
+                    f"{100 * c['SQ_ACTIVE_INST_VALU'] / c['SQ_WAVE_CYCLES']:.0f}%; "
+                    f"{c['SQ_INSTS_VALU'] / c['SQ_WAVES']:.0f} VALU and {c['SQ_INSTS_MFMA'] / c['SQ_WAVES']:.0f} "
+                    f"MFMA instructions per wave")
+    if rows:
+        print("#\n# Per wave of the grouped kernels:")
+        print("\n".join(rows))
 
 
 def main():
@@ -791,8 +810,8 @@ def main():
     ap.add_argument("--no-hybrid", action="store_true", help="skip the hybrid CPU/GPU runs")
     ap.add_argument("--only-wide", action="store_true",
                     help="run only the wide-step routed GEMV shapes (one JSON line each)")
-    ap.add_argument("--summarize-counters", default=None, metavar="COUNTER_CSV",
-                    help="per-kernel means of every counter in a rocprofv3 --pmc csv")
+    ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="COUNTER_CSV",
+                    help="per-kernel means of every counter in rocprofv3 --pmc csv files")
     ap.add_argument("--cpu-sample-tokens", type=int, default=6)
     ap.add_argument("--overlap", type=int, default=2,
                     help="layer-step schedule passed to the cache (0 serial, 1 side-stream "
