@@ -834,7 +834,7 @@ def main():
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the decode step is data-parallel and this build runs "
+        print(f"bench.py measures one GPU: the decode step is data-parallel and the library runs "
               f"on a single MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
