@@ -59,6 +59,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Untimed token replays before the timed ones, whatever --warmup asks for:
+# the 3164-slot cache starts empty and needs this many tokens to reach its
+# steady state of ~28 misses per token (the pages' figure is taken after a
+# warm-up too).  --warmup only adds graph warm-up beyond it.
+CACHE_WARM_TOKENS = 64
+
+
+def token_plan(warmup: int, steps: int):
+    """(untimed tokens, trace length, first timed token) for a run of
+    `steps` timed tokens: the trace holds the cache warm-up, then exactly
+    the timed tokens."""
+    n_warm = max(int(warmup), CACHE_WARM_TOKENS)
+    return n_warm, n_warm + int(steps), n_warm
+
+
+def leg_tokens(first: int, n_tok: int, limit=None) -> range:
+    """The tokens a replay leg runs again: the timed tokens [first, n_tok),
+    at most `limit` of them; never an index past the trace."""
+    n = max(0, n_tok - first)
+    if limit is not None:
+        n = min(n, int(limit))
+    return range(first, first + n)
+
+
+def run_leg(name, fn, *a, **kw):
+    """A side leg of the bench: its result, or {"error": ...} if it raised,
+    so that one leg's failure never loses the result line."""
+    import traceback
+
+    try:
+        return fn(*a, **kw)
+    except Exception as e:  # noqa: BLE001 - reported in the line
+        log(f"[bench] leg {name} failed:")
+        log(traceback.format_exc())
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def kernel_sources_hash() -> str:
     """Hash of the device-code sources (kernels and the headers they
     include); the host-side C-ABI files do not change what a kernel moves."""
@@ -96,19 +133,15 @@ def build_stack(torch, m, W, seed=0, gather_workgroups=0, overlap=1):
     from expert_slot_cache_moe_amd.layer import SlotCacheLayers
 
     t0 = time.time()
-    g = W.rng(seed, "bench", "experts")
-    distinct = 64
-    base = [torch.from_numpy(b) for b in W.bf16_expert_rows(g, distinct, H, F)]
-    rb = m.moe_bank_row_bytes(0, H, F)
     host = []
     for l in range(L):
-        idx = (torch.arange(l * E, (l + 1) * E) * 7919) % distinct
-        banks = []
-        for b in range(2):
-            t = torch.empty((E, rb[b]), dtype=torch.uint8, pin_memory=True)
-            torch.index_select(base[b], 0, idx, out=t)
-            banks.append(t)
-        host.append(banks)
+        # every expert of every layer drawn afresh (N(0, 0.02) as bf16), on the
+        # device, then copied into the layer's pinned host rows
+        dev = W.device_expert_rows(0, (seed, "bench", l), E, H, F)
+        host.append([W.pinned_copy(b) for b in dev])
+        del dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     log(f"[bench] pinned host store {L * E * ROW_BYTES / 1e9:.1f} GB in {time.time() - t0:.1f}s")
     gs = W.rng(seed, "bench", "shared")
     shared = [(W.normal_bf16(gs, 2 * F * H, 0.02), W.normal_bf16(gs, H * F, 0.02),
@@ -323,12 +356,13 @@ def lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok, seed=0
         st0 = m.moe_cache_stats(lay.cache)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for t in range(first, n_tok):
+        toks = leg_tokens(first, n_tok)
+        for t in toks:
             graph.replay()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         d = m.moe_cache_stats(lay.cache) - st0
-        n = n_tok - first
+        n = len(toks)
         res.append({"predictor_accuracy": acc,
                     "value": round(L * n / dt, 1),
                     "ms_per_step": round(dt / n * 1000.0, 4),
@@ -364,12 +398,13 @@ def schedule_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok):
         st0 = m.moe_cache_stats(lay.cache)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for t in range(first, n_tok):
+        toks = leg_tokens(first, n_tok)
+        for t in toks:
             graph.replay()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         d = m.moe_cache_stats(lay.cache) - st0
-        n = n_tok - first
+        n = len(toks)
         res.append({"overlap": ov, "schedule": what, "value": round(L * n / dt, 1),
                     "ms_per_step": round(dt / n * 1000.0, 4),
                     "misses_per_token": round(float(d[m.MOE_STAT_MISSED] - d[m.MOE_STAT_OVERFLOW]) / n, 2)})
@@ -385,8 +420,9 @@ HYBRID_CAPS = (0, 1, -1)
 HYBRID_TOKENS = 32
 
 
-def hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, first):
-    """The first HYBRID_TOKENS timed tokens again, eagerly, as hybrid steps:
+def hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok):
+    """The first HYBRID_TOKENS timed tokens again (fewer if fewer were
+    timed), eagerly, as hybrid steps:
     misses beyond the fetch cap run on HYBRID_THREADS host threads over the
     pinned host store while the GPU runs the rest.  Cap -1 fetches every
     miss (no CPU route): the cost of the hybrid step's host orchestration
@@ -395,7 +431,8 @@ def hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, first):
     out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
     ids = torch.empty((L, 1, K), dtype=torch.int32, device="cuda")
     res = []
-    n = HYBRID_TOKENS
+    toks = leg_tokens(first, n_tok, HYBRID_TOKENS)
+    n = len(toks)
     for cap in HYBRID_CAPS:
         m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"],
                                 freq=snap["freq"], dlast=snap["dlast"],
@@ -404,7 +441,7 @@ def hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, first):
         cpu_routes = torch.zeros((), dtype=torch.int64, device="cuda")
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for t in range(first, first + n):
+        for t in toks:
             for l in range(L):
                 lay.decode_hybrid(l, x_all[t, l], lg_all[t, l], K, out[l], ids_out=ids[l], max_fetch=cap)
             cpu_routes += (ids < 0).sum()
@@ -538,7 +575,7 @@ def _split(log, moe):
     (timed layer steps, instrumented layer steps, routed-GEMV calls): a
     staged layer step is admission, stage 1, stage 2; a routed-GEMV call is
     stage 1, stage 2."""
-    L, W_, K_ = log["layers"], log["warmup"], log["steps"]
+    L, W_, K_ = log["layers"], log.get("warm_tokens", log["warmup"]), log["steps"]
     n_steps = (W_ + 2 * K_) * L
     dec = moe[:3 * n_steps]
     steps = [dec[i:i + 3] for i in range(0, len(dec), 3)]
@@ -557,7 +594,7 @@ def _split(log, moe):
 def _wide_calls(log, moe):
     """Per wide shape, its timed calls' dispatches (grouping, gate/up, down,
     combine), following the decode and routed-GEMV phases."""
-    L, W_, K_ = log["layers"], log["warmup"], log["steps"]
+    L, W_, K_ = log["layers"], log.get("warm_tokens", log["warmup"]), log["steps"]
     pos = 3 * (W_ + 2 * K_) * L + 2 * log["gemv_calls"]
     out = []
     kinds = ["group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "combine_kernel"]
@@ -851,8 +888,10 @@ def main():
             print(json.dumps(r), flush=True)
         return None
     W_, K_ = args.warmup, args.steps
+    if K_ < 1:
+        raise SystemExit("--steps must be at least 1")
+    n_warm, n_tok, first = token_plan(W_, K_)
     lay = build_stack(torch, m, W, gather_workgroups=args.gather_workgroups, overlap=args.overlap)
-    n_tok = W_ + K_
     t0 = time.time()
     lg_all, x_all = make_trace(torch, W, n_tok)
     log(f"[bench] trace of {n_tok} tokens in {time.time() - t0:.1f}s")
@@ -865,13 +904,13 @@ def main():
     def step(t):
         graph.replay()                     # stages token t: the counter holds t
 
-    for t in range(W_):
+    for t in range(n_warm):                # cache warm-up (and graph warm-up): untimed
         step(t)
     torch.cuda.synchronize()
     snap = m.moe_cache_read_state(lay.cache)
     st0 = m.moe_cache_stats(lay.cache)
     t0 = time.perf_counter()
-    for t in range(W_, n_tok):
+    for t in range(first, n_tok):
         step(t)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
@@ -897,11 +936,11 @@ def main():
         e.record()                              # creates the events before capture
     torch.cuda.synchronize()
     tgraph = capture(torch, lay, x_st, lg_st, out, (x_all, lg_all, tok), ids_l, w_l, pairs)
-    tok.fill_(W_)
+    tok.fill_(first)
     staged = args.overlap == 2
     k1_ms, pair_ms, fetch_l = [], [], []
     prev = m.moe_cache_read_state(lay.cache)["stats"]
-    for t in range(W_, n_tok):
+    for t in range(first, n_tok):
         tgraph.replay()
         torch.cuda.synchronize()
         ms = m.moe_cache_timing(lay.cache).astype(np.float64)
@@ -1002,20 +1041,26 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    wide = None if args.no_wide else wide_gemv_benchmark(torch, m)
-    adm = None if args.no_admission else admission_benchmark(torch, m, W)
-    adm_chunked = None if args.no_admission else admission_benchmark(
-        torch, m, W, one_call_width=128, batches=ADMISSION_CHUNKED_BATCHES)
-    look = None if args.no_lookahead else lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, W_, n_tok)
+    # The headline, its roofline and the routed-GEMV figure are in hand;
+    # every side leg below reports an error field instead of raising.
+    wide = None if args.no_wide else run_leg("wide", wide_gemv_benchmark, torch, m)
+    adm = None if args.no_admission else run_leg("admission", admission_benchmark, torch, m, W)
+    adm_chunked = None if args.no_admission else run_leg(
+        "admission chunked", admission_benchmark, torch, m, W, one_call_width=128,
+        batches=ADMISSION_CHUNKED_BATCHES)
+    look = None if args.no_lookahead else run_leg(
+        "look-ahead", lookahead_benchmark, torch, m, lay, snap, x_all, lg_all, first, n_tok)
     sched = (None if args.no_schedules or args.overlap != 2
-             else schedule_benchmark(torch, m, lay, snap, x_all, lg_all, W_, n_tok))
-    hyb = None if args.no_hybrid else hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, W_)
+             else run_leg("schedules", schedule_benchmark, torch, m, lay, snap, x_all, lg_all, first, n_tok))
+    hyb = None if args.no_hybrid else run_leg(
+        "hybrid", hybrid_benchmark, torch, m, lay, snap, x_all, lg_all, first, n_tok)
     lay.close()
     del lay
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(W, W_, args.cpu_sample_tokens)
-        cpu["admission"] = cpu_admission_baseline(W)
+        cpu = run_leg("cpu baseline", cpu_baseline, W, n_warm, args.cpu_sample_tokens)
+        if "error" not in cpu:
+            cpu["admission"] = run_leg("cpu admission baseline", cpu_admission_baseline, W)
 
     ratios = traffic_ratios()
     value = L * K_ / dt
@@ -1038,7 +1083,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload,
                    "layers": L, "experts": E, "top_k": K, "hidden": H, "ffn": F, "slots": S,
-                   "batch": 1, "misses_per_token": round(fetched / K_, 2)},
+                   "batch": 1, "cache_warm_tokens": n_warm, "misses_per_token": round(fetched / K_, 2)},
         "roofline": {"kernel": ("stage1_kernel (miss gather + gate/up), layer-steps with misses" if staged
                                 else "gather_kernel (miss gather, pinned host -> device slots)"),
                      "bound": "host-link", "achieved": round(gather_gbs, 2),
@@ -1070,7 +1115,7 @@ def main():
     print(json.dumps(line), flush=True)
     if args.launch_log:
         with open(args.launch_log, "w") as f:
-            json.dump({"workload": workload, "layers": L, "warmup": W_, "steps": K_,
+            json.dump({"workload": workload, "layers": L, "warmup": W_, "warm_tokens": n_warm, "steps": K_,
                        "overlap": args.overlap, "fetched": fetch_l.astype(int).tolist(),
                        "gemv_calls": (1 + GEMV_REPLAYS) * GEMV_PASSES * L,
                        "gemv_timed_calls": GEMV_REPLAYS * GEMV_PASSES * L,
