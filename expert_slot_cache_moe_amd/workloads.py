@@ -122,6 +122,113 @@ def expert_rows(fmt: int, g, rows, H, F, std=0.02):
     return mxfp4_expert_rows(g, rows, H, F, std)
 
 
+# ---------------------------------------------------------------- weights drawn on the device
+
+def _torch_generator(device, seed, *purpose) -> torch.Generator:
+    key = zlib.crc32(repr((seed,) + purpose).encode())
+    gen = torch.Generator(device=device)
+    gen.manual_seed(key)
+    return gen
+
+
+def _quantize_e2m1_torch(w: torch.Tensor):
+    """The numpy E2M1 recipe (_quantize_e2m1) in torch, on w's device."""
+    n, cols = w.shape
+    blk = w.reshape(n, cols // 16, 16)
+    amax = blk.abs().amax(dim=2)
+    sc8 = (amax / 6.0).to(torch.float8_e4m3fn)
+    scale = sc8.float()
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    mag = blk.abs() / safe[:, :, None]
+    vals = torch.tensor(E2M1_VALUES, dtype=torch.float32, device=w.device)
+    mids = (vals[1:] + vals[:-1]) / 2
+    code = torch.bucketize(mag, mids).to(torch.uint8)           # same ties as searchsorted 'left'
+    code |= (blk < 0).to(torch.uint8) << 3
+    code = code.reshape(n, cols)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), sc8.view(torch.uint8).contiguous()
+
+
+def _quantize_mxfp4_torch(w: torch.Tensor):
+    """The numpy MXFP4 recipe (_quantize_mxfp4) in torch, on w's device."""
+    n, cols = w.shape
+    blk = w.reshape(n, cols // 32, 32).double()
+    amax = blk.abs().amax(dim=2)
+    pos = amax > 0
+    e = torch.where(pos, torch.floor(torch.log2(torch.where(pos, amax, torch.ones_like(amax)))) - 2,
+                    torch.full_like(amax, -127.0))
+    code8 = torch.clamp(e + 127, 0, 254).to(torch.uint8)
+    scale = torch.ldexp(torch.ones_like(amax), code8.to(torch.int64) - 127)
+    mag = blk.abs() / scale[:, :, None]
+    vals = torch.tensor(E2M1_VALUES, dtype=torch.float64, device=w.device)
+    mids = (vals[1:] + vals[:-1]) / 2
+    code = torch.bucketize(mag, mids).to(torch.uint8)
+    code |= (blk < 0).to(torch.uint8) << 3
+    code = code.reshape(n, cols)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), code8.contiguous()
+
+
+def e2m1_global_scales(rows: int, matrix: int) -> np.ndarray:
+    """Per-expert fp32 global scales of the E2M1 pools drawn on the device,
+    distinct for up to 509 experts: 1 + (e mod 509) / 512 for w13 and
+    1 - (e mod 509) / 1024 for w2 (exact in fp32)."""
+    e = np.arange(rows) % 509
+    g = 1.0 + e / 512.0 if matrix == 0 else 1.0 - e / 1024.0
+    return g.astype(np.float32)
+
+
+def device_expert_rows(fmt: int, seed, rows: int, H: int, F: int, device="cuda", std=0.02,
+                       chunk_rows: int = 16):
+    """Banks [rows, bytes] (uint8 tensors on `device`) in which every
+    expert's weights are drawn afresh: N(0, std) from torch's seeded
+    generator, stored as bf16 or quantized with the same E2M1 / MXFP4
+    recipes as the numpy generators.  E2M1 pools get distinct per-expert
+    global scales (e2m1_global_scales), so no two experts share bytes.
+    Full-size pools (gigabytes) are drawn this way in seconds."""
+    gen = _torch_generator(device, seed, "device-experts", fmt, rows, H, F)
+    shapes = ((2 * F, H), (H, F))
+    if fmt == 0:
+        banks = [torch.empty((rows, 2 * nr * nc), dtype=torch.uint8, device=device) for nr, nc in shapes]
+    elif fmt == 1:
+        banks = []
+        for nr, nc in shapes:
+            banks += [torch.empty((rows, nr * nc // 2), dtype=torch.uint8, device=device),
+                      torch.empty((rows, nr * nc // 16), dtype=torch.uint8, device=device),
+                      torch.empty((rows, 4), dtype=torch.uint8, device=device)]
+    else:
+        banks = []
+        for nr, nc in shapes:
+            banks += [torch.empty((rows, nr * nc // 2), dtype=torch.uint8, device=device),
+                      torch.empty((rows, nr * nc // 32), dtype=torch.uint8, device=device)]
+    for r0 in range(0, rows, chunk_rows):
+        n = min(chunk_rows, rows - r0)
+        for m, (nr, nc) in enumerate(shapes):
+            w = torch.randn((n * nr, nc), generator=gen, device=device, dtype=torch.float32).mul_(std)
+            if fmt == 0:
+                banks[m][r0:r0 + n] = w.to(torch.bfloat16).view(torch.uint8).reshape(n, -1)
+            elif fmt == 1:
+                codes, scales = _quantize_e2m1_torch(w)
+                banks[3 * m][r0:r0 + n] = codes.reshape(n, -1)
+                banks[3 * m + 1][r0:r0 + n] = scales.reshape(n, -1)
+            else:
+                codes, scales = _quantize_mxfp4_torch(w)
+                banks[2 * m][r0:r0 + n] = codes.reshape(n, -1)
+                banks[2 * m + 1][r0:r0 + n] = scales.reshape(n, -1)
+    if fmt == 1:
+        for m in range(2):
+            g = torch.from_numpy(e2m1_global_scales(rows, m).view(np.uint8).reshape(rows, 4))
+            banks[3 * m + 2].copy_(g)
+    return banks
+
+
+def pinned_copy(t: torch.Tensor) -> torch.Tensor:
+    """A pinned host copy of a device tensor."""
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
 # ---------------------------------------------------------------- routing
 
 def zipf_bias(g: np.random.Generator, E: int, s: float) -> np.ndarray:
@@ -207,7 +314,8 @@ class DecodeTrace:
     the working set on top (+bonus), so the router selects it."""
 
     # stay = 0.73 gives ~28 misses per token on 40 x 256 experts, top-8,
-    # 3164 slots (oracle/calibrate_decode_trace.py).
+    # 3164 slots after a 64-token warm-up (checked against the oracle's
+    # admission in the tests).
     def __init__(self, seed: int, layers: int, experts: int, top_k: int, s: float = 1.05,
                  stay: float = 0.73):
         self.L, self.E, self.K, self.stay = layers, experts, top_k, stay

@@ -11,8 +11,8 @@ import pytest
 import expert_slot_cache_moe_amd as m
 from expert_slot_cache_moe_amd import workloads as W
 import oracle
+from parity import check_close
 
-TOL = 2e-2
 
 
 def _case(seed, E, H, F, T, K, cpu_frac):
@@ -36,8 +36,7 @@ def test_cpu_routes_match_the_oracle(E, H, F, T, K, frac):
     got = m.moe_cpu_experts(4, cpu, w, x, banks[0], banks[1], H, F)
     ref = oracle.routed(oracle.Pool(0, H, F, banks), cpu, w.astype(np.float64), x)
     assert (got[(cpu < 0).all(axis=1)] == 0).all()       # tokens with no CPU route add nothing
-    scale = max(np.abs(ref).max(), 1e-30)
-    assert np.abs(got - ref).max() <= TOL * scale
+    check_close(got, ref, "CPU experts")
 
 
 def test_result_does_not_depend_on_the_thread_count():

@@ -13,10 +13,9 @@ import expert_slot_cache_moe_amd as m
 from expert_slot_cache_moe_amd import workloads as W
 from expert_slot_cache_moe_amd.layer import SlotCacheLayers
 import oracle
+from parity import check_close, oracle_routed_rows
 
 pytestmark = pytest.mark.gpu
-
-TOL = 2e-2
 
 
 def _bf16_to_f64(t):
@@ -24,9 +23,7 @@ def _bf16_to_f64(t):
 
 
 def _close(got, ref, what=""):
-    scale = np.abs(ref).max()
-    err = np.abs(got - ref).max()
-    assert err <= TOL * scale, f"{what}: max err {err:.3e} > {TOL} * {scale:.3e}"
+    check_close(got, ref, what)
 
 
 def _dev_u16(a):
@@ -259,26 +256,35 @@ def test_tiny_layer_decode_32_steps(overlap, shared):
         lay.close()
 
 
-def _replicated_rows(fmt, g, E, H, F, distinct):
-    """E expert rows built from `distinct` random rows (row e = row e mod
-    distinct) -- the full-size pools without drawing every weight."""
-    base = W.expert_rows(fmt, g, distinct, H, F)
-    return [np.ascontiguousarray(np.tile(b, (E // distinct + 1, 1))[:E]) for b in base]
+def _covering_rows(chosen, E):
+    """Token rows that between them route to every expert of the step
+    (greedy): one checked route per group of the grouped kernels."""
+    need, rows = set(chosen.reshape(-1).tolist()), []
+    for t in np.argsort([-len(set(r)) for r in chosen.tolist()], kind="stable"):
+        if need & set(chosen[t].tolist()):
+            rows.append(int(t))
+            need -= set(chosen[t].tolist())
+        if not need:
+            break
+    return np.sort(np.asarray(rows))
 
 
-@pytest.mark.parametrize("fmt,H,F,E,S,T,K,one,qw,distinct,sample", [
-    (0, 1024, 256, 160, 160, 150, 2, 256, 128, 160, 150),   # wide bf16 step
-    (1, 1024, 256, 160, 1100, 600, 2, 256, 128, 40, 64),    # wide e2m1 step over 1100 slots
-    (1, 1024, 256, 160, 160, 600, 2, 3, 3, 40, 64),         # ... one layer's experts, 3 per query
-    (2, 1024, 256, 160, 1100, 600, 2, 256, 128, 40, 64),    # the wide 4-bit step as MXFP4
-    (0, 4096, 1024, 256, 256, 42, 6, 3, 3, 8, 6),           # prefill chunk, 3 per query
-    (0, 4096, 1024, 640, 640, 50, 6, 256, 128, 8, 4),       # prefill chunk over 640 experts
+@pytest.mark.parametrize("fmt,H,F,E,S,T,K,one,qw,rows", [
+    (0, 1024, 256, 160, 160, 150, 2, 256, 128, "all"),      # wide bf16 step
+    (1, 1024, 256, 160, 1100, 600, 2, 256, 128, "cover"),   # wide e2m1 step over 1100 slots
+    (1, 1024, 256, 160, 160, 600, 2, 3, 3, "cover"),        # ... one layer's experts, 3 per query
+    (2, 1024, 256, 160, 1100, 600, 2, 256, 128, "cover"),   # the wide 4-bit step as MXFP4
+    (0, 4096, 1024, 256, 256, 42, 6, 3, 3, "all"),          # prefill chunk, 3 per query
+    (0, 4096, 1024, 640, 640, 50, 6, 256, 128, "all"),      # prefill chunk over 640 experts
 ])
-def test_wide_step_cached_equals_streamed_bit_for_bit(fmt, H, F, E, S, T, K, one, qw, distinct, sample):
+def test_wide_step_cached_equals_streamed_bit_for_bit(fmt, H, F, E, S, T, K, one, qw, rows):
     """[P3 Tests] the GEMV over the slots equals the one over the streamed
-    layer exactly; sampled tokens match the oracle."""
+    layer exactly; token rows match the oracle (every row, or rows that
+    between them route to every expert of the step).  Every expert's bytes
+    are drawn afresh, so a read of the wrong slot cannot pass."""
     g = W.rng(7, "wide", fmt, E, T)
-    host = [_replicated_rows(fmt, g, E, H, F, distinct)]
+    print(f"wide step fmt {fmt} H {H} F {F} E {E} S {S} T {T} K {K} widths ({one}, {qw})", flush=True)
+    host = [[W.pinned_copy(b) for b in W.device_expert_rows(fmt, (7, "wide", E, T), E, H, F)]]
     lay = SlotCacheLayers(layers=1, experts=E, slots=S, hidden=H, ffn=F, fmt=fmt, host_rows=host,
                           max_tokens=T, max_top_k=K, one_call_width=one, query_width=qw)
     try:
@@ -303,10 +309,11 @@ def test_wide_step_cached_equals_streamed_bit_for_bit(fmt, H, F, E, S, T, K, one
         m.moe_routed_decode(lay.streamed_pool(0), _dev_u16(x), torch.from_numpy(experts).cuda(), w, out2, ws)
         torch.cuda.synchronize()
         assert torch.equal(out, out2)
-        rows = np.sort(g.choice(T, min(sample, T), replace=False))
-        ref = oracle.routed(oracle.Pool(fmt, H, F, host[0]), experts[rows],
-                            w.cpu().numpy()[rows].astype(np.float64), x[rows])
-        _close(_bf16_to_f64(out)[rows], ref, "wide")
+        sel = np.arange(T) if rows == "all" else _covering_rows(experts, E)
+        assert len(set(experts[sel].reshape(-1).tolist())) == st[1]      # every group checked
+        ref = oracle_routed_rows(oracle.Pool(fmt, H, F, [b.numpy() for b in host[0]]), experts[sel],
+                                 w.cpu().numpy()[sel].astype(np.float64), x[sel])
+        _close(_bf16_to_f64(out)[sel], ref, "wide")
     finally:
         lay.close()
 
@@ -442,7 +449,7 @@ def test_shared_expert_decode_shape_staged():
     for bit and the oracle within tolerance."""
     L, E, S, H, F, K = 2, 256, 24, 2048, 512, 8
     g = W.rng(15, "c3-shape")
-    host = [_replicated_rows(0, g, E, H, F, 8) for _ in range(L)]
+    host = [[W.pinned_copy(b) for b in W.device_expert_rows(0, (15, l), E, H, F)] for l in range(L)]
     sh = [(W.normal_bf16(g, 2 * F * H, 0.02), W.normal_bf16(g, H * F, 0.02), W.normal_bf16(g, H, 0.02))
           for _ in range(L)]
     lays = [SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, host_rows=host, shared=sh,
@@ -460,7 +467,8 @@ def test_shared_expert_decode_shape_staged():
                     lay.decode(l, _dev_u16(x), torch.from_numpy(lgs[l:l + 1]).cuda(), K, o)
                 torch.cuda.synchronize()
                 assert all(torch.equal(outs[0], o) for o in outs[1:]), (t, l)
-                ref, _, _ = _oracle_layer(oc, host, sh, l, x, lgs[l:l + 1], K, 0, H, F)
+                ref, _, _ = _oracle_layer(oc, [[b.numpy() for b in hl] for hl in host], sh, l, x,
+                                          lgs[l:l + 1], K, 0, H, F)
                 _close(_bf16_to_f64(outs[0]), ref, f"token {t} layer {l}")
         assert m.moe_cache_stats(lays[0].cache)[2] > 40
     finally:

@@ -18,11 +18,11 @@ import expert_slot_cache_moe_amd as m
 from expert_slot_cache_moe_amd import workloads as W
 from expert_slot_cache_moe_amd.layer import SlotCacheLayers
 import oracle
+from parity import check_close
 
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-TOL = 2e-2
 
 
 def _golden():
@@ -277,8 +277,7 @@ def test_layer_steps_with_lookahead_match_the_oracle(overlap, fmt):
                 torch.cuda.synchronize()
                 np.testing.assert_array_equal(ids.cpu().numpy(), slots, err_msg=f"token {t} layer {l}")
                 got = out.view(torch.bfloat16).double().cpu().numpy()
-                err = np.abs(got - ref).max()
-                assert err <= TOL * np.abs(ref).max(), (t, l, err)
+                check_close(got, ref, f"token {t} layer {l}")
         m.moe_prefetch_join(lay.cache)
         _same(lay.cache, oc)
         st = m.moe_cache_read_state(lay.cache)["stats"]
