@@ -86,6 +86,7 @@ def lib():
             "moe_gather_misses": (st, [P, P]),
             "moe_routed_workspace_bytes": (i64, [i32, i32, i32, i32, i32]),
             "moe_routed_decode": (st, [P, P, P, P, i32, i32, P, P, P, i64, P]),
+            "moe_routed_decode_noalloc": (st, [P, P, P, P, i32, i32, P, P, P]),
             "moe_shared_expert": (st, [P, i32, P, i32, P, P, i64, P]),
             "moe_layer_decode": (st, [P, i32, P, P, i32, i32, P, i32, P, P, P, P]),
             "moe_cache_stats": (st, [P, i32, P, P]),
@@ -297,6 +298,18 @@ def moe_routed_decode(pool: moe_pool_t, x, idx, w, out, workspace, addend=None, 
         C.byref(pool), _dev_ptr(x), _dev_ptr(idx), _dev_ptr(w), T, K, _dev_ptr(addend),
         _dev_ptr(out), _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def moe_routed_decode_noalloc(pool: moe_pool_t, x, idx, w, out, addend=None, stream=None) -> None:
+    """moe_routed_decode on the library's own per-GPU scratch (no workspace
+    argument, no allocation); calls on one GPU must not overlap."""
+    T, K = idx.shape
+    _check(lib().moe_routed_decode_noalloc(
+        C.byref(pool), _dev_ptr(x), _dev_ptr(idx), _dev_ptr(w), T, K, _dev_ptr(addend),
+        _dev_ptr(out), _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def moe_shared_expert(shared: moe_shared_t, hidden: int, x, addend, workspace, stream=None) -> None:

@@ -13,6 +13,7 @@
 #include <numeric>
 #include <string>
 #include <functional>
+#include <mutex>
 #include <vector>
 
 #include "moe_api_internal.h"
@@ -674,9 +675,15 @@ int64_t moe_routed_workspace_bytes(int32_t weight_format, int32_t hidden, int32_
     return (int64_t)routed_ws(hidden, ffn, T, K).total;
 }
 
-moe_status_t moe_routed_decode(const moe_pool_t *pool, const void *x, const int32_t *idx,
-                               const float *w, int32_t T, int32_t K, const float *addend, void *out,
-                               void *ws, int64_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_routed_decode's body, for a workspace of ws_bytes at ws (caller
+// memory, or the allocation-free entry point's scratch).
+moe_status_t routed_decode_into(const moe_pool_t *pool, const void *x, const int32_t *idx,
+                                const float *w, int32_t T, int32_t K, const float *addend, void *out,
+                                void *ws, int64_t ws_bytes, void *stream) {
     PoolView pv;
     moe_status_t s = pool_view_of(pool, pv);
     if (s != MOE_OK) return s;
@@ -707,6 +714,70 @@ moe_status_t moe_routed_decode(const moe_pool_t *pool, const void *x, const int3
     return MOE_OK;
 }
 
+// The allocation-free entry point's workspace: a file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in): each
+// device's copy is looked up once with hipGetSymbolAddress, with that
+// device current, and that address is what the kernels get.
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kScratchDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+moe_status_t scratch_of_current_device(void **out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(MOE_UNSUPPORTED, "device %d: the scratch table holds %d devices", dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(MOE_HIP_ERROR, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        }
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_routed_decode(const moe_pool_t *pool, const void *x, const int32_t *idx,
+                               const float *w, int32_t T, int32_t K, const float *addend, void *out,
+                               void *ws, int64_t ws_bytes, void *stream) {
+    return routed_decode_into(pool, x, idx, w, T, K, addend, out, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_routed_decode_noalloc(const moe_pool_t *pool, const void *x, const int32_t *idx,
+                                       const float *w, int32_t T, int32_t K, const float *addend,
+                                       void *out, void *stream) {
+    if (!pool) return fail(MOE_INVALID_ARG, "NULL pool");
+    if (T < 0 || K < 1 || K > kMaxTopK) return fail(MOE_INVALID_ARG, "bad T=%d K=%d", T, K);
+    if (T == 0) return MOE_OK;
+    const size_t need = routed_ws(pool->hidden, pool->ffn, T, K).total;
+    if (pool->hidden < 1 || pool->ffn < 1 || need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_INVALID_ARG,
+                    "T=%d K=%d at hidden %d, ffn %d needs %zu B of workspace, more than the %d B "
+                    "the allocation-free entry point holds; use moe_routed_decode",
+                    T, K, pool->hidden, pool->ffn, need, (int)MOE_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    moe_status_t s = scratch_of_current_device(&ws);
+    if (s != MOE_OK) return s;
+    return routed_decode_into(pool, x, idx, w, T, K, addend, out, ws, (int64_t)MOE_NOALLOC_SCRATCH_BYTES,
+                              stream);
+}
+
 moe_status_t moe_shared_expert(const moe_shared_t *sh, int32_t H, const void *x, int32_t T,
                                float *addend, void *ws, int64_t ws_bytes, void *stream) {
     if (!sh) return fail(MOE_INVALID_ARG, "NULL shared expert");
@@ -726,12 +797,6 @@ moe_status_t moe_shared_expert(const moe_shared_t *sh, int32_t H, const void *x,
             "shared launch");
     return MOE_OK;
 }
-
-
-
-
-
-
 
 moe_status_t moe_cache_stats(moe_cache_t *c, int32_t layer, int64_t *out, void *stream) {
     if (!c || !out) return fail(MOE_INVALID_ARG, "NULL cache or output");

@@ -271,6 +271,29 @@ moe_status_t moe_routed_decode(const moe_pool_t *pool, const void *x_dev, const 
                                void *out_dev, void *workspace_dev, int64_t workspace_bytes,
                                void *stream);
 
+/* Workspace held by moe_routed_decode_noalloc on each GPU: 16 MiB. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+/* moe_routed_decode for callers that cannot allocate device memory or pass
+ * a workspace: code under hipGraph capture that may not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * arithmetic, kernels and results as moe_routed_decode, bit for bit, but
+ * the workspace is the library's own static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (one per GPU, held until the process ends).
+ * The call allocates nothing: the first call on a device only looks up
+ * that device's array address (hipGetSymbolAddress).  Every call on one
+ * GPU shares that array and leaves its contents behind; nothing in it
+ * needs to start at zero.  Calls that overlap on one GPU -- on different
+ * streams, or from different threads, without an order between them --
+ * race on the array and give undefined results; order them (one stream,
+ * or events).  Errors: as moe_routed_decode, and MOE_INVALID_ARG when
+ * moe_routed_workspace_bytes(...) for T, K and the pool's widths exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES. */
+moe_status_t moe_routed_decode_noalloc(const moe_pool_t *pool, const void *x_dev,
+                                       const int32_t *idx_dev, const float *w_dev, int32_t T,
+                                       int32_t K, const float *addend_dev, void *out_dev,
+                                       void *stream);
+
 /* (5) Gated shared expert alone [P2 "Problem in upstream today"]:
  * addend[t] = sigmoid(x_t . gate) * shared(x_t), fp32 [T][H], the term
  * moe_routed_decode adds.  workspace: moe_routed_workspace_bytes(BF16, H,
