@@ -87,6 +87,7 @@ def lib():
             "moe_routed_workspace_bytes": (i64, [i32, i32, i32, i32, i32]),
             "moe_routed_decode": (st, [P, P, P, P, i32, i32, P, P, P, i64, P]),
             "moe_routed_decode_noalloc": (st, [P, P, P, P, i32, i32, P, P, P]),
+            "moe_trace_layer_steps": (st, [P, i32, i32, i32, i32, i32, P, i64, P]),
             "moe_shared_expert": (st, [P, i32, P, i32, P, P, i64, P]),
             "moe_layer_decode": (st, [P, i32, P, P, i32, i32, P, i32, P, P, P, P]),
             "moe_cache_stats": (st, [P, i32, P, P]),
@@ -310,6 +311,26 @@ def moe_routed_decode_noalloc(pool: moe_pool_t, x, idx, w, out, addend=None, str
 
 
 MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def moe_trace_layer_steps(*, num_layers, num_experts, num_slots, hidden, ffn, T, K, overlap,
+                          weight_format=MOE_FMT_BF16, with_shared=True, prefetch_width=0, tokens=2,
+                          one_call_width=256, query_width=128, max_routes=None) -> list:
+    """The stream operations of a run of layer steps, recorded on the host
+    with no device (see include/moe_cache.h): a list of op lines."""
+    d = moe_cache_desc_t()
+    d.num_layers, d.num_experts, d.num_slots = num_layers, num_experts, num_slots
+    d.hidden, d.ffn, d.weight_format = hidden, ffn, weight_format
+    d.one_call_width, d.query_width = one_call_width, query_width
+    d.max_routes = max_routes if max_routes is not None else max(T * K, prefetch_width, 1)
+    d.max_tokens, d.max_top_k, d.overlap = max(T, 1), K, overlap
+    n = C.c_int64(0)
+    _check(lib().moe_trace_layer_steps(C.byref(d), T, K, int(with_shared), prefetch_width, tokens,
+                                       None, 0, C.byref(n)))
+    buf = C.create_string_buffer(n.value + 1)
+    _check(lib().moe_trace_layer_steps(C.byref(d), T, K, int(with_shared), prefetch_width, tokens,
+                                       buf, n.value + 1, C.byref(n)))
+    return buf.value.decode().splitlines()
 
 
 def moe_shared_expert(shared: moe_shared_t, hidden: int, x, addend, workspace, stream=None) -> None:

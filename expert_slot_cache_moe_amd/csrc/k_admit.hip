@@ -847,6 +847,14 @@ hipError_t admit_prepare(size_t lds_bytes) {
 }
 
 hipError_t launch_admit(const AdmitParams &p, size_t lds_bytes, hipStream_t s) {
+    if (rec::on())
+        // the state (slot map, owners, stamps, order, clock, statistics,
+        // histogram, demand recency) is read and rewritten; the plan, the
+        // route plan, the rewritten ids and (fused top-k) the weights written
+        return rec::launch("admit_kernel", s,
+                           {{p.logits, rec::kRead}, {p.ids, p.logits ? rec::kWrite : rec::kReadWrite},
+                            {p.res, rec::kReadWrite}, {p.plan_slot, rec::kWrite},
+                            {p.route_plan, rec::kWrite}, {p.w_out, rec::kWrite}});
     switch (fast_p(p.S)) {
     case 1: hipLaunchKernelGGL(admit_fast_kernel<1>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
     case 2: hipLaunchKernelGGL(admit_fast_kernel<2>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;

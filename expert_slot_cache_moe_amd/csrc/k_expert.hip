@@ -186,6 +186,10 @@ hipError_t group_prepare(size_t lds_bytes) {
 hipError_t launch_group_routes(const int32_t *idx, int routes, int num_rows, int32_t *n_groups,
                                int32_t *grp_row, int32_t *grp_start, int32_t *grp_count,
                                int32_t *grp_routes, hipStream_t s) {
+    if (rec::on())
+        return rec::launch("group_kernel", s,
+                           {{idx, rec::kRead}, {n_groups, rec::kWrite}, {grp_row, rec::kWrite},
+                            {grp_start, rec::kWrite}, {grp_count, rec::kWrite}, {grp_routes, rec::kWrite}});
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), group_lds_bytes(routes), s, idx,
                        routes, num_rows, n_groups, grp_row, grp_start, grp_count, grp_routes);
     return hipGetLastError();
@@ -194,6 +198,12 @@ hipError_t launch_group_routes(const int32_t *idx, int routes, int num_rows, int
 hipError_t launch_up(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
                      uint16_t *h, const uint16_t *gate_vec, float *gamma, hipStream_t s) {
     if (max_items <= 0) return hipSuccess;
+    if (rec::on())
+        return rec::launch("up_kernel", s,
+                           {{x, rec::kRead}, {pool.bank[0], rec::kRead, rec::items_part(items.route_plan, items.want_fresh)},
+                            {items.idx, rec::kRead}, {items.route_plan, rec::kRead}, {items.n_groups, rec::kRead},
+                            {items.grp_row, rec::kRead}, {gate_vec, rec::kRead}, {h, rec::kWrite},
+                            {gamma, rec::kWrite}});
     using namespace expert_detail;
     if (pool.fmt == MOE_FMT_MXFP4)
         return launch_up_fmt<MOE_FMT_MXFP4>(pool, items, max_items, x, h, gate_vec, gamma, s);
@@ -205,6 +215,11 @@ hipError_t launch_up(const PoolView &pool, const Items &items, int max_items, co
 hipError_t launch_down_to_d(const PoolView &pool, const Items &items, int max_items,
                             const uint16_t *h, float *d, const float *gamma, hipStream_t s) {
     if (max_items <= 0) return hipSuccess;
+    if (rec::on())
+        return rec::launch("down_d_kernel", s,
+                           {{h, rec::kRead}, {pool.bank[0], rec::kRead, rec::items_part(items.route_plan, items.want_fresh)},
+                            {items.idx, rec::kRead}, {items.route_plan, rec::kRead}, {items.n_groups, rec::kRead},
+                            {items.grp_row, rec::kRead}, {gamma, rec::kRead}, {d, rec::kWrite}});
     using namespace expert_detail;
     if (pool.fmt == MOE_FMT_MXFP4)
         return launch_down_to_d_fmt<MOE_FMT_MXFP4>(pool, items, max_items, h, d, gamma, s);
@@ -217,6 +232,13 @@ hipError_t launch_down_fused(const PoolView &pool, const int32_t *idx, const flo
                              int K, const uint16_t *h, const float *addend, const float *d,
                              const int32_t *route_plan, uint16_t *out, hipStream_t s) {
     if (T <= 0) return hipSuccess;
+    if (rec::on())
+        // with a route plan, routes not filled this step take their down
+        // projection from d; only the fresh routes read their slots
+        return rec::launch("down_fused_kernel", s,
+                           {{h, rec::kRead}, {pool.bank[0], rec::kRead, rec::items_part(route_plan, 1)},
+                            {idx, rec::kRead}, {w, rec::kRead}, {addend, rec::kRead}, {d, rec::kRead},
+                            {route_plan, rec::kRead}, {out, rec::kWrite}});
     using namespace expert_detail;
     if (pool.fmt == MOE_FMT_MXFP4)
         return launch_down_fused_fmt<MOE_FMT_MXFP4>(pool, idx, w, T, K, h, addend, d, route_plan, out, s);
@@ -229,6 +251,10 @@ hipError_t launch_down_fused(const PoolView &pool, const int32_t *idx, const flo
 hipError_t launch_combine(const int32_t *idx, const float *w, int T, int K, int H, int num_rows,
                           const float *d, const float *addend, uint16_t *out, hipStream_t s) {
     if (T <= 0) return hipSuccess;
+    if (rec::on())
+        return rec::launch("combine_kernel", s,
+                           {{idx, rec::kRead}, {w, rec::kRead}, {d, rec::kRead}, {addend, rec::kRead},
+                            {out, rec::kWrite}});
     dim3 grid((H + kThreads - 1) / kThreads, T);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, idx, w, K, H, num_rows, d,
                        addend, out);

@@ -60,6 +60,10 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherParams p) {
 int gather_unit_bytes() { return kUnitBytes; }
 
 hipError_t launch_gather(const GatherParams &p, int workgroups, hipStream_t s) {
+    if (rec::on())
+        return rec::launch("gather_kernel", s,
+                           {{p.n_miss, rec::kRead}, {p.host[0], rec::kRead},
+                            {p.slot[0], rec::kWrite, rec::kFreshSlots}});
     hipLaunchKernelGGL(gather_kernel, dim3(workgroups), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }

@@ -504,6 +504,11 @@ hipError_t launch_up_mfma(const PoolView &pool, const Items &items, int max_item
                           uint16_t *h, hipStream_t s) {
     using namespace mfma_detail;
     if (max_items <= 0) return hipSuccess;
+    if (rec::on())
+        return rec::launch("up_mfma_kernel", s,
+                           {{x, rec::kRead}, {pool.bank[0], rec::kRead, rec::items_part(items.route_plan, items.want_fresh)},
+                            {items.idx, rec::kRead}, {items.n_groups, rec::kRead}, {items.grp_row, rec::kRead},
+                            {h, rec::kWrite}});
     if (pool.fmt == MOE_FMT_MXFP4) return launch_up_shape<MOE_FMT_MXFP4, 2, 2>(pool, items, max_items, x, h, s);
     if (pool.fmt == MOE_FMT_E2M1) return launch_up_shape<MOE_FMT_E2M1, 1, 3>(pool, items, max_items, x, h, s);
     if (pool.F >= 1024) return launch_up_shape<MOE_FMT_BF16, 2, 2>(pool, items, max_items, x, h, s);
@@ -514,6 +519,11 @@ hipError_t launch_down_mfma(const PoolView &pool, const Items &items, int max_it
                             float *d, hipStream_t s) {
     using namespace mfma_detail;
     if (max_items <= 0) return hipSuccess;
+    if (rec::on())
+        return rec::launch("down_mfma_kernel", s,
+                           {{h, rec::kRead}, {pool.bank[0], rec::kRead, rec::items_part(items.route_plan, items.want_fresh)},
+                            {items.idx, rec::kRead}, {items.n_groups, rec::kRead}, {items.grp_row, rec::kRead},
+                            {d, rec::kWrite}});
     // One slab in flight: measured on MI355X, the smaller register demand
     // (152 VGPRs for the 4-bit formats against 221 with two) lets three
     // waves share a SIMD, which beats a second buffer (E2M1 wide step 3%,
@@ -539,6 +549,10 @@ hipError_t launch_group_count(const int32_t *idx, int routes, int num_rows, int3
                               int32_t *grp_row, int32_t *grp_start, int32_t *grp_count,
                               int32_t *grp_routes, hipStream_t s) {
     using namespace mfma_detail;
+    if (rec::on())
+        return rec::launch("group_count_kernel", s,
+                           {{idx, rec::kRead}, {n_groups, rec::kWrite}, {grp_row, rec::kWrite},
+                            {grp_start, rec::kWrite}, {grp_count, rec::kWrite}, {grp_routes, rec::kWrite}});
     hipLaunchKernelGGL(group_count_kernel, dim3(1), dim3(kCountThreads), group_count_lds_bytes(num_rows),
                        s, idx, routes, num_rows, n_groups, grp_row, grp_start, grp_count, grp_routes);
     return hipGetLastError();

@@ -252,6 +252,9 @@ hipError_t prefetch_prepare(size_t lds_bytes) {
 
 hipError_t launch_prefetch(const PrefetchParams &p, hipStream_t s) {
     if (p.M < std::min(p.n, p.E)) return hipErrorInvalidValue;
+    if (rec::on())
+        return rec::launch("prefetch_kernel", s,
+                           {{p.ids, rec::kRead}, {p.res, rec::kReadWrite}, {p.fill_slot, rec::kWrite}});
     const size_t lds = prefetch_lds_bytes(p.M, p.E, p.S);
     hipLaunchKernelGGL(prefetch_kernel, dim3(1), dim3(kThreads), lds, s, p);
     return hipGetLastError();

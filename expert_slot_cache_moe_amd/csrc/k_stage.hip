@@ -368,6 +368,32 @@ hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, co
     }
     b.addend = addend;
     b.out = out;
+    if (rec::on()) {
+        const bool gather = gather_blocks > 0;
+        hipError_t e = hipSuccess;
+        if (which & 1)
+            // gather role: plan rows over the host link into fresh slots, the
+            // fetched rows' gate/up dots into gu; resident routes' gate/up
+            // from their slots (every route's when nothing is fetched); the
+            // shared expert's gate/up and gate
+            e = rec::launch("stage1_kernel", s,
+                            {{x, rec::kRead}, {idx, rec::kRead}, {route_plan, rec::kRead},
+                             {slots.bank[0], rec::kRead, route_plan ? rec::kResidentSlots : rec::kAllSlots},
+                             {gather ? g.n_miss : nullptr, rec::kRead}, {gather ? g.host[0] : nullptr, rec::kRead},
+                             {gather ? g.slot[0] : nullptr, rec::kWrite, rec::kFreshSlots},
+                             {gather ? gu : nullptr, rec::kWrite}, {h, rec::kWrite},
+                             {shared ? shared->bank[0] : nullptr, rec::kRead}, {gate_vec, rec::kRead},
+                             {shared ? hs : nullptr, rec::kWrite}, {shared ? gamma : nullptr, rec::kWrite}});
+        if (e == hipSuccess && (which & 2))
+            // every route's down rows from its slot, the fetched routes'
+            // activations from gu, the shared expert's down rows
+            e = rec::launch("stage2_kernel", s,
+                            {{h, rec::kRead}, {route_plan ? gu : nullptr, rec::kRead}, {idx, rec::kRead},
+                             {w, rec::kRead}, {route_plan, rec::kRead}, {slots.bank[0], rec::kRead, rec::kAllSlots},
+                             {shared ? shared->bank[0] : nullptr, rec::kRead}, {shared ? hs : nullptr, rec::kRead},
+                             {shared ? gamma : nullptr, rec::kRead}, {addend, rec::kRead}, {out, rec::kWrite}});
+        return e;
+    }
     const int ch = slots.H / 8, cf = slots.F / 8;
 #define MOE_STAGE_CALL(CH, LH, NH, CF, LF, NF) \
     if (ch == CH && cf == CF) return launch_shape<LH, NH, LF, NF>(a, b, which, s);

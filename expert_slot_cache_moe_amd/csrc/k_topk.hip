@@ -78,6 +78,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void topk_kernel(const float
 hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
                        hipStream_t s) {
     if (T == 0) return hipSuccess;
+    if (rec::on())
+        return rec::launch("topk_kernel", s, {{logits, rec::kRead}, {ids, rec::kWrite}, {w, rec::kWrite}});
     const int blocks = (T + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(topk_kernel, dim3(blocks), dim3(kRowsPerBlock * kWave), 0, s, logits, T, E,
                        K, ids, w);

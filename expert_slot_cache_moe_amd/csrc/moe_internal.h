@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "moe_cache.h"
+#include "moe_record.h"
 
 namespace moe {
 

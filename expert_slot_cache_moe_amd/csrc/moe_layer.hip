@@ -44,12 +44,12 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
         // term.  Every exit after the fork joins, so no side work outlives
         // the step.
         const uint16_t *xb = static_cast<const uint16_t *>(x);
-        HIP_TRY(hipEventRecord(c->ready, s), "record ready");
-        HIP_TRY(hipStreamWaitEvent(c->side, c->ready, 0), "side waits ready");
+        HIP_TRY(rec::event_record(c->ready, s), "record ready");
+        HIP_TRY(rec::stream_wait(c->side, c->ready), "side waits ready");
         hipError_t e = shared_sequence(shared, c->d.hidden, Fs, xb, T, c->ws_addend, c->ws_shared, c->side);
-        const hipError_t re = hipEventRecord(c->done, c->side);
+        const hipError_t re = rec::event_record(c->done, c->side);
         auto joined = [&](moe_status_t r) {
-            (void)hipStreamWaitEvent(s, c->done, 0);
+            (void)rec::stream_wait(s, c->done);
             return r;
         };
         if (e != hipSuccess || re != hipSuccess)
@@ -66,7 +66,7 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
         if ((e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess) return joined(hip_fail(e, "timing"));
         if ((st = launch_gather_checked(c, s)) != MOE_OK) return joined(st);
         if ((e = mark(3)) != hipSuccess || (e = mark(4)) != hipSuccess) return joined(hip_fail(e, "timing"));
-        const BeforeAddend join = [&]() { return hipStreamWaitEvent(s, c->done, 0); };
+        const BeforeAddend join = [&]() { return rec::stream_wait(s, c->done); };
         e = routed_sequence(slot_pool_view(c), xb, ids, w, T, K, c->ws_addend,
                             static_cast<uint16_t *>(out), c->ws_routed, s, &join);
         if (e != hipSuccess) return hip_fail(e, "routed launch");   // joined inside
@@ -123,15 +123,15 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
     const bool two_streams = c->d.overlap == 1;
     hipStream_t gs = s;
     if (two_streams) {
-        HIP_TRY(hipEventRecord(c->ready, s), "record ready");
-        HIP_TRY(hipStreamWaitEvent(c->side, c->ready, 0), "side waits ready");
+        HIP_TRY(rec::event_record(c->ready, s), "record ready");
+        HIP_TRY(rec::stream_wait(c->side, c->ready), "side waits ready");
         gs = c->side;
     }
     if (timing) HIP_TRY(record_timing(tev[2], gs), "timing");
     st = launch_gather_checked(c, gs);
     if (st != MOE_OK) return st;
     if (timing) HIP_TRY(record_timing(tev[3], gs), "timing");
-    if (two_streams) HIP_TRY(hipEventRecord(c->done, c->side), "record done");
+    if (two_streams) HIP_TRY(rec::event_record(c->done, c->side), "record done");
 
     // Between fork and join, on the compute stream: the shared expert and
     // its gate, and (single token) the routed experts whose slots were
@@ -158,7 +158,7 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
     // The join is issued even if a launch above failed, so the side stream
     // never outlives the step.
     if (two_streams) {
-        hipError_t je = hipStreamWaitEvent(s, c->done, 0);
+        hipError_t je = rec::stream_wait(s, c->done);
         if (e == hipSuccess) e = je;
     }
     if (e != hipSuccess) return hip_fail(e, "shared expert / resident routes / join");

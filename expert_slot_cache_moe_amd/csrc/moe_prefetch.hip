@@ -15,7 +15,7 @@ namespace api {
 moe_status_t join_prefetch(moe_cache *c, hipStream_t s) {
     if (!c->pf_pending) return MOE_OK;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    HIP_TRY(hipStreamIsCapturing(s, &cs), "capture status");
+    HIP_TRY(rec::is_capturing(s, &cs), "capture status");
     const bool capturing = cs != hipStreamCaptureStatusNone;
     if (capturing && !c->pf_captured)
         return fail(MOE_INVALID_ARG,
@@ -27,7 +27,7 @@ moe_status_t join_prefetch(moe_cache *c, hipStream_t s) {
         c->pf_pending = 0;
         return MOE_OK;
     }
-    HIP_TRY(hipStreamWaitEvent(s, c->pf_done, 0), "wait for the prefetch copy");
+    HIP_TRY(rec::stream_wait(s, c->pf_done), "wait for the prefetch copy");
     c->pf_pending = 0;
     return MOE_OK;
 }
@@ -78,14 +78,14 @@ moe_status_t moe_prefetch(moe_cache_t *c, int32_t layer, const int32_t *ids, int
     if (c->nb == 0) return MOE_OK;
     // The copy forks off `s`: nothing on `s` waits for it until the next
     // demand admission or prefetch.
-    HIP_TRY(hipEventRecord(c->pf_ready, s), "record prefetch fork");
-    HIP_TRY(hipStreamWaitEvent(c->pf_side, c->pf_ready, 0), "prefetch stream waits");
+    HIP_TRY(rec::event_record(c->pf_ready, s), "record prefetch fork");
+    HIP_TRY(rec::stream_wait(c->pf_side, c->pf_ready), "prefetch stream waits");
     HIP_TRY(launch_gather(gather_params(c, layer, c->n_fill, c->fill_slot, c->fill_expert),
                           c->gather_wg, c->pf_side),
             "prefetch copy launch");
-    HIP_TRY(hipEventRecord(c->pf_done, c->pf_side), "record prefetch done");
+    HIP_TRY(rec::event_record(c->pf_done, c->pf_side), "record prefetch done");
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    HIP_TRY(hipStreamIsCapturing(s, &cs), "capture status");
+    HIP_TRY(rec::is_capturing(s, &cs), "capture status");
     c->pf_pending = 1;
     c->pf_captured = cs != hipStreamCaptureStatusNone;
     return MOE_OK;

@@ -470,6 +470,37 @@ moe_status_t moe_cache_timing(moe_cache_t *cache, float *ms_host, int32_t *layer
  * sequence of launches inside one graph time them with nothing between. */
 moe_status_t moe_record_event(void *event, void *stream);
 
+/* ---------------------------------------------------------------- verification */
+
+/* The stream operations of a run of layer steps, recorded on the host
+ * instead of issued, with no device involved [P2 "Correctness evidence":
+ * the fork/join is checked on the CPU with fake streams].  A cache shaped
+ * by *desc (its host and slot banks ignored) lives on the host only, with
+ * placeholder device addresses; `tokens` tokens of num_layers layer steps
+ * (moe_layer_decode of T x K routes, with a shared expert if with_shared,
+ * in desc->overlap's schedule) are run, each followed, when
+ * prefetch_width > 0, by moe_prefetch of the next layer's prefetch_width
+ * predictions; a final moe_prefetch_join ends the run.  Every kernel
+ * launch, event record and stream wait is written as one text line to
+ * out_host (NUL-terminated, at most cap - 1 bytes; *len_out gets the full
+ * length):
+ *   S <token> <layer>                 a layer step begins
+ *   P <token> <layer>                 a prefetch of that layer begins
+ *   J                                 the final join
+ *   L <stream> <kernel> <reads> <writes>   a launch; buffer names joined
+ *                                     by ',' or '-' for none; "slots:fresh"
+ *                                     / "slots:resident" are the slots the
+ *                                     step's plan fills / that already held
+ *                                     their expert, "slots" all of them
+ *   E <stream> <event>                hipEventRecord
+ *   W <stream> <event>                hipStreamWaitEvent
+ * Streams: compute, side, prefetch; events: ready, done, pf_ready,
+ * pf_done.  Errors: MOE_INVALID_ARG, MOE_UNSUPPORTED, as
+ * moe_layer_decode for T and K. */
+moe_status_t moe_trace_layer_steps(const moe_cache_desc_t *desc, int32_t T, int32_t K,
+                                   int32_t with_shared, int32_t prefetch_width, int32_t tokens,
+                                   char *out_host, int64_t cap, int64_t *len_out);
+
 #ifdef __cplusplus
 }
 #endif
