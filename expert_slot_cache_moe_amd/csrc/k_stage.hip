@@ -1,4 +1,5 @@
-// The single-token layer step in two launches on one stream (bf16 experts).
+// The single-token layer step in two launches on one stream (bf16, E2M1
+// or MXFP4 routed experts; the shared expert is bf16).
 //
 // FreeToken issue #753 (section "What we changed") overlaps the miss
 // gather with the shared expert by forking a side stream and joining it
@@ -23,9 +24,11 @@
 //
 // Bit-exactness with the serial path: resident routes and the shared expert
 // run the same device code; a fetched expert's gate/up dot products are
-// built from the same 8-element chunk partials combined by the same trees
-// (tree_sum over a lane's chunks, then the xor tree over lanes), so every
-// float matches.
+// built from the same 16-byte chunk partials combined by the same trees
+// (tree_sum over a lane's chunks, then the lane tree), so every float
+// matches.  A 4-bit chunk's partial needs its scales: the gather unit that
+// carries a run of gate/up codes also carries (and copies) the run of the
+// scale bank that belongs to them, so nothing is read over the link twice.
 #include "k_expert.inc"
 
 namespace moe {
@@ -36,15 +39,15 @@ using namespace expert_detail;
 struct Stage1Params {
     GatherParams g;            // the step's miss plan and banks
     int gather_blocks;
-    float *gu;                 // [plan entries][2F] fetched experts' gate/up dots
-    PoolView slots;            // routed pool (bf16)
+    float *gu;                 // [plan entries][2F] fetched experts' gate/up dots (no global scale)
+    PoolView slots;            // routed pool
     const int32_t *idx;        // [K] slot ids
     const int32_t *route_plan; // [K] plan entry of a fetched route, or -1
     int K;
     int a_tiles;               // gate/up tiles per route
     const uint16_t *x;         // [H]
     uint16_t *h;               // [K][F]
-    PoolView shared;           // one row; shared F == routed F
+    PoolView shared;           // one bf16 row; shared F == routed F
     int s_tiles;               // 0: no shared expert
     uint16_t *hs;              // [F]
     const uint16_t *gate_vec;  // [H]
@@ -68,29 +71,55 @@ struct Stage2Params {
 };
 
 constexpr int kGatherUnit = kThreads * 16 * 4;  // 16 KiB, as the gather kernel
-constexpr int kUnitChunks = kGatherUnit / 16;   // 1024 chunks of 8 bf16
+constexpr int kUnitChunks = kGatherUnit / 16;   // 1024 chunks of 16 bytes
 
-// gate/up rows jj and F + jj of one expert with x -> h[j] (bf16)
-template <int LPR, int NCH>
+// gate/up rows jj and F + jj of one expert with x -> h[j] (bf16), the
+// arithmetic of up_kernel for one route
+template <int FMT, int LPR, int NCH>
 __device__ __forceinline__ void up_rows(const PoolView &pool, int64_t prow, int j, int li,
                                         const uint16_t *x, uint16_t *h) {
     const int F = pool.F;
     const bool jok = j < F;
     const int jj = jok ? j : F - 1;
-    WSeg<MOE_FMT_BF16, NCH> wg, wu;
+    WSeg<FMT, NCH> wg, wu;
     wg.load(pool, prow, 0, jj, li, LPR);
     wu.load(pool, prow, 0, F + jj, li, LPR);
-    XSeg<MOE_FMT_BF16, NCH> xs;
+    XSeg<FMT, NCH> xs;
     xs.load(x, li, LPR);
     __builtin_amdgcn_sched_barrier(0);  // all of the row pair's loads issue before any math
-    const float g = group_total<LPR>(seg_dot(wg, xs)) * wg.glob(pool, prow, 0);
-    const float u = group_total<LPR>(seg_dot(wu, xs)) * wg.glob(pool, prow, 0);
+    const float glob = wg.glob(pool, prow, 0);
+    const float g = group_total<LPR>(seg_dot(wg, xs)) * glob;
+    const float u = group_total<LPR>(seg_dot(wu, xs)) * glob;
     if (jok && li == LPR - 1) h[j] = f32_to_bf16(silu_mul(g, u));
 }
 
-template <int LPRH, int NCHH>
+// The partial dot of one 16-byte gate/up chunk with x, as seg_dot takes it.
+template <int FMT>
+__device__ __forceinline__ float chunk_part(u32x4 codes, uint32_t sc, const uint16_t *x, int c);
+
+template <>
+__device__ __forceinline__ float chunk_part<MOE_FMT_BF16>(u32x4 w, uint32_t, const uint16_t *x, int c) {
+    return chunk_dot_bf16(w, *reinterpret_cast<const u32x4 *>(x + 8 * c));
+}
+template <>
+__device__ __forceinline__ float chunk_part<MOE_FMT_E2M1>(u32x4 w, uint32_t sc, const uint16_t *x, int c) {
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x + 32 * c);
+    const u32x4 xs[4] = {xv[0], xv[1], xv[2], xv[3]};
+    return chunk_dot_e2m1(w, sc, xs);
+}
+template <>
+__device__ __forceinline__ float chunk_part<MOE_FMT_MXFP4>(u32x4 w, uint32_t sc, const uint16_t *x, int c) {
+    const u32x4 *xv = reinterpret_cast<const u32x4 *>(x + 32 * c);
+    const u32x4 xs[4] = {xv[0], xv[1], xv[2], xv[3]};
+    return chunk_dot_mxfp4(w, sc, xs);
+}
+
+// Stage 1.  FMT, LPRH x NCHH: the routed gate/up rows (16-byte chunks per
+// row); SLPRH x SNCHH: the shared expert's bf16 gate/up rows.
+template <int FMT, int LPRH, int NCHH, int SLPRH, int SNCHH>
 __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
     __shared__ float part[kUnitChunks];
+    __shared__ __align__(16) uint8_t scl[kUnitChunks * 2];   // a 4-bit unit's scales
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid & (kWave - 1);
     const int H = p.slots.H, F = p.slots.F;
@@ -107,9 +136,17 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
             while (b + 1 < g.nb && uu >= g.unit_start[b + 1]) ++b;
             const int64_t rb = g.rb[b];
             const int64_t off = (int64_t)(uu - g.unit_start[b]) * kGatherUnit;
-            const uint8_t *src = g.host[b] + (int64_t)g.plan_expert[entry] * rb + off;
-            uint8_t *dst = g.slot[b] + (int64_t)g.plan_slot[entry] * rb + off;
+            const int expert = g.plan_expert[entry], slot = g.plan_slot[entry];
+            const uint8_t *src = g.host[b] + (int64_t)expert * rb + off;
+            uint8_t *dst = g.slot[b] + (int64_t)slot * rb + off;
             const int64_t len = min((int64_t)kGatherUnit, rb - off);
+            if (rb & 15) {
+                // a bank of sub-16-byte rows (the fp32 global scale): 4 B per lane
+                for (int64_t o = (int64_t)tid * 4; o < len; o += kThreads * 4)
+                    *reinterpret_cast<uint32_t *>(dst + o) =
+                        __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(src + o));
+                continue;
+            }
             const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
             u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
             u32x4 v[4];
@@ -117,19 +154,40 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
             for (int k = 0; k < 4; ++k)
                 if ((int64_t)(tid + k * kThreads) * 16 < len)
                     v[k] = __builtin_nontemporal_load(s4 + tid + k * kThreads);
+            // a 4-bit unit of gate/up codes carries their scales: one E4M3
+            // pair (2 B) or E8M0 (1 B) per chunk, a contiguous run of the
+            // scale bank at the unit's chunk index
+            const int64_t chunk0 = off / 16;
+            const int carry = (b == 0) ? g.carry_scales : 0;
+            const int64_t sbytes = carry * (len / 16);
+            u32x4 sv{};
+            const bool sload = carry && (int64_t)tid * 16 < sbytes;
+            if (sload)
+                sv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    g.host[1] + (int64_t)expert * g.rb[1] + carry * chunk0 + (int64_t)tid * 16));
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 if ((int64_t)(tid + k * kThreads) * 16 < len) d4[tid + k * kThreads] = v[k];
             if (b != 0) continue;
+            if (carry) {
+                if (sload) {
+                    *reinterpret_cast<u32x4 *>(g.slot[1] + (int64_t)slot * g.rb[1] + carry * chunk0 +
+                                               (int64_t)tid * 16) = sv;
+                    *reinterpret_cast<u32x4 *>(scl + tid * 16) = sv;
+                }
+                __syncthreads();
+            }
             // Gate/up rows of a fetched expert: chunk partials with x ...
-            const int64_t chunk0 = off / 16;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int f = tid + k * kThreads;
                 float pv = 0.f;
                 if ((int64_t)f * 16 < len) {
                     const int c = (int)((chunk0 + f) % C);
-                    pv = chunk_dot_bf16(v[k], *reinterpret_cast<const u32x4 *>(p.x + 8 * c));
+                    uint32_t sc = 0;
+                    if constexpr (FMT == MOE_FMT_E2M1) sc = *reinterpret_cast<const uint16_t *>(scl + 2 * f);
+                    if constexpr (FMT == MOE_FMT_MXFP4) sc = scl[f];
+                    pv = chunk_part<FMT>(v[k], sc, p.x, c);
                 }
                 part[f] = pv;
             }
@@ -144,19 +202,20 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
                 float q[NCHH];
 #pragma unroll
                 for (int i = 0; i < NCHH; ++i) q[i] = r < rows ? part[r * C + li + LPRH * i] : 0.f;
-                const float s = group_total<LPRH>(tree_sum<NCHH>(q));
-                if (r < rows && li == LPRH - 1) p.gu[(int64_t)entry * 2 * F + row0 + r] = s;
+                const float sum = group_total<LPRH>(tree_sum<NCHH>(q));
+                if (r < rows && li == LPRH - 1) p.gu[(int64_t)entry * 2 * F + row0 + r] = sum;
             }
             __syncthreads();
         }
         return;
     }
 
-    constexpr int JT = kWavesPerBlock * (kWave / LPRH);
-    const int sub = lane / LPRH, li = lane % LPRH;
     int b = blockIdx.x - p.gather_blocks;
     if (b < p.s_tiles) {
-        up_rows<LPRH, NCHH>(p.shared, 0, b * JT + wave * (kWave / LPRH) + sub, li, p.x, p.hs);
+        constexpr int SJT = kWavesPerBlock * (kWave / SLPRH);
+        const int sub = lane / SLPRH, li = lane % SLPRH;
+        up_rows<MOE_FMT_BF16, SLPRH, SNCHH>(p.shared, 0, b * SJT + wave * (kWave / SLPRH) + sub, li, p.x,
+                                            p.hs);
         if (b == 0 && wave == 0) {
             float z = 0.f;
             for (int c = lane; c < H / 8; c += kWave) {
@@ -170,54 +229,58 @@ __global__ __launch_bounds__(kThreads) void stage1_kernel(Stage1Params p) {
         return;
     }
     b -= p.s_tiles;
+    constexpr int JT = kWavesPerBlock * (kWave / LPRH);
+    const int sub = lane / LPRH, li = lane % LPRH;
     const int k = b / p.a_tiles;
     const int tile = b - k * p.a_tiles;
     const int s = p.idx[k];
     const int plan = p.route_plan ? p.route_plan[k] : -1;
     if ((s < 0) | (s >= p.slots.num_rows) | (plan >= 0)) return;
-    up_rows<LPRH, NCHH>(p.slots, s, tile * JT + wave * (kWave / LPRH) + sub, li, p.x,
-                        p.h + (int64_t)k * F);
+    up_rows<FMT, LPRH, NCHH>(p.slots, s, tile * JT + wave * (kWave / LPRH) + sub, li, p.x,
+                             p.h + (int64_t)k * F);
 }
 
-// h chunks of a fetched route, from its gate/up dots.
-template <int NCH>
-__device__ __forceinline__ void h_from_gu(const float *gu, int F, int li, int lpr,
-                                          XSeg<MOE_FMT_BF16, NCH> &hs) {
+// h chunks of a fetched route, from its gate/up dots and the w13 global
+// scale (as up_rows scales them).
+template <int FMT, int NCH>
+__device__ __forceinline__ void h_from_gu(const float *gu, int F, int li, int lpr, float glob,
+                                          XSeg<FMT, NCH> &hs) {
+    constexpr int V = XSeg<FMT, NCH>::kVecs;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int j0 = (li + c * lpr) * 8;
-        const u32x4 *g4 = reinterpret_cast<const u32x4 *>(gu + j0);
-        const u32x4 *u4 = reinterpret_cast<const u32x4 *>(gu + F + j0);
-        const u32x4 ga = g4[0], gb = g4[1], ua = u4[0], ub = u4[1];
-        float gv[8], uv[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            gv[q] = __uint_as_float(ga[q]);
-            gv[4 + q] = __uint_as_float(gb[q]);
-            uv[q] = __uint_as_float(ua[q]);
-            uv[4 + q] = __uint_as_float(ub[q]);
-        }
-        u32x4 v;
+        for (int vv = 0; vv < V; ++vv) {
+            const int j0 = (li + c * lpr) * Epc<FMT>::v + 8 * vv;
+            const u32x4 *g4 = reinterpret_cast<const u32x4 *>(gu + j0);
+            const u32x4 *u4 = reinterpret_cast<const u32x4 *>(gu + F + j0);
+            const u32x4 ga = g4[0], gb = g4[1], ua = u4[0], ub = u4[1];
+            float gv[8], uv[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = f32_to_bf16(silu_mul(gv[2 * q], uv[2 * q]));
-            const uint32_t hi = f32_to_bf16(silu_mul(gv[2 * q + 1], uv[2 * q + 1]));
-            v[q] = lo | (hi << 16);
+            for (int q = 0; q < 4; ++q) {
+                gv[q] = __uint_as_float(ga[q]) * glob;
+                gv[4 + q] = __uint_as_float(gb[q]) * glob;
+                uv[q] = __uint_as_float(ua[q]) * glob;
+                uv[4 + q] = __uint_as_float(ub[q]) * glob;
+            }
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = f32_to_bf16(silu_mul(gv[2 * q], uv[2 * q]));
+                const uint32_t hi = f32_to_bf16(silu_mul(gv[2 * q + 1], uv[2 * q + 1]));
+                o[q] = lo | (hi << 16);
+            }
+            hs.x[c][vv] = o;
         }
-        hs.x[c][0] = v;
     }
 }
 
 // One batch of up to kDownBatch routes of stage 2, loads first, math after:
 // the routes' slot ids and plan entries (scalar loads, issued together),
-// then every W2 row and activation chunk, and with the first batch the
-// shared expert's.  Routes that contribute nothing read row 0 and route 0
-// as in-range stand-ins, and without a shared expert the shared view points
-// at valid memory too (set by the launcher), so every load is
+// then every W2 row and activation chunk.  Routes that contribute nothing
+// read row 0 and route 0 as in-range stand-ins, so every load is
 // unconditional and none waits for another.
-template <int LPRF, int NCHF, bool FIRST>
-__device__ __forceinline__ void stage2_batch(const Stage2Params &p, int k0, int ii, int li,
-                                             float &acc, float &vs) {
+template <int FMT, int LPRF, int NCHF>
+__device__ __forceinline__ void stage2_batch(const Stage2Params &p, int k0, int ii, int li, float &acc) {
     const int F = p.slots.F;
     int sl[kDownBatch], pe[kDownBatch];
 #pragma unroll
@@ -227,52 +290,78 @@ __device__ __forceinline__ void stage2_batch(const Stage2Params &p, int k0, int 
         pe[q] = p.route_plan ? p.route_plan[kk] : -1;
     }
     __builtin_amdgcn_sched_barrier(0);
-    WSeg<MOE_FMT_BF16, NCHF> w2[kDownBatch];
-    XSeg<MOE_FMT_BF16, NCHF> hs[kDownBatch];
+    WSeg<FMT, NCHF> w2[kDownBatch];
+    XSeg<FMT, NCHF> hs[kDownBatch];
     int rows[kDownBatch];
+    float g13[kDownBatch], g2[kDownBatch];   // global scales (1 unless E2M1)
 #pragma unroll
     for (int q = 0; q < kDownBatch; ++q) {
         const int k = k0 + q;
         const bool ok = k < p.K && sl[q] >= 0 && sl[q] < p.slots.num_rows;
         rows[q] = ok ? sl[q] : -1;
-        w2[q].load(p.slots, ok ? sl[q] : 0, 1, ii, li, LPRF);
+        const int r = ok ? sl[q] : 0;
+        w2[q].load(p.slots, r, 1, ii, li, LPRF);
         hs[q].load(p.h + (int64_t)min(k, p.K - 1) * F, li, LPRF);
-    }
-    WSeg<MOE_FMT_BF16, NCHF> w2s;
-    XSeg<MOE_FMT_BF16, NCHF> hss;
-    if constexpr (FIRST) {
-        w2s.load(p.shared, 0, 1, ii, li, LPRF);
-        hss.load(p.hs, li, LPRF);
+        g13[q] = w2[q].glob(p.slots, r, 0);
+        g2[q] = w2[q].glob(p.slots, r, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < kDownBatch; ++q) {
         if (rows[q] < 0) continue;
-        if (pe[q] >= 0) h_from_gu<NCHF>(p.gu + (int64_t)pe[q] * 2 * F, F, li, LPRF, hs[q]);
-        const float v = group_total<LPRF>(seg_dot(w2[q], hs[q])) * w2[q].glob(p.slots, rows[q], 1);
+        if (pe[q] >= 0) h_from_gu<FMT, NCHF>(p.gu + (int64_t)pe[q] * 2 * F, F, li, LPRF, g13[q], hs[q]);
+        const float v = group_total<LPRF>(seg_dot(w2[q], hs[q])) * g2[q];
         acc = fmaf(p.w[k0 + q], v, acc);
     }
-    if constexpr (FIRST) vs = group_total<LPRF>(seg_dot(w2s, hss)) * w2s.glob(p.shared, 0, 1);
 }
 
-template <int LPRF, int NCHF>
+// Stage 2.  The routed W2 rows take LPRF x NCHF chunks, the shared
+// expert's bf16 rows SLPRF x SNCHF (SLPRF >= LPRF: a bf16 row has four
+// times the chunks of a 4-bit one).  A wave owns RPW = 64 / LPRF output
+// rows; the shared rows of those are taken SLPRF / LPRF passes of 64 / SLPRF
+// rows each, and each value is moved to the lane group of its row.
+template <int FMT, int LPRF, int NCHF, int SLPRF, int SNCHF>
 __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
     constexpr int RPW = kWave / LPRF;
     constexpr int IT = kWavesPerBlock * RPW;
+    constexpr int SRPW = kWave / SLPRF;
+    constexpr int PASSES = SLPRF / LPRF;
+    static_assert(SLPRF >= LPRF && PASSES * SRPW == RPW, "shared and routed row mapping");
     const int H = p.slots.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int sub = lane / LPRF, li = lane % LPRF;
-    const int i = blockIdx.x * IT + wave * RPW + sub;
+    const int row0 = blockIdx.x * IT + wave * RPW;
+    const int i = row0 + sub;
     const bool iok = i < H;
     const int ii = iok ? i : H - 1;
 
-    float acc = 0.f, vs = 0.f;
-    stage2_batch<LPRF, NCHF, true>(p, 0, ii, li, acc, vs);
-    for (int k0 = kDownBatch; k0 < p.K; k0 += kDownBatch)
-        stage2_batch<LPRF, NCHF, false>(p, k0, ii, li, acc, vs);
+    // the shared expert's rows, loaded with the first batch of routes
+    WSeg<MOE_FMT_BF16, SNCHF> w2s[PASSES];
+    XSeg<MOE_FMT_BF16, SNCHF> hss;
+    const int ssub = lane / SLPRF, sli = lane % SLPRF;
+    if (p.has_shared) {
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp)
+            w2s[pp].load(p.shared, 0, 1, min(row0 + pp * SRPW + ssub, H - 1), sli, SLPRF);
+        hss.load(p.hs, sli, SLPRF);
+    }
+    float acc = 0.f;
+    for (int k0 = 0; k0 < p.K; k0 += kDownBatch) stage2_batch<FMT, LPRF, NCHF>(p, k0, ii, li, acc);
     float res = acc;
     if (p.addend) res = acc + p.addend[ii];
     if (p.has_shared) {
+        float vs = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < PASSES; ++pp) {
+            const float v = group_total<SLPRF>(seg_dot(w2s[pp], hss));
+            if constexpr (PASSES == 1) {
+                vs = v;          // the same lane group holds the row
+            } else {
+                // row sub lives in pass sub / SRPW, lane group sub % SRPW
+                const float moved = __shfl(v, (sub % SRPW) * SLPRF + SLPRF - 1, kWave);
+                if (sub / SRPW == pp) vs = moved;
+            }
+        }
         // gamma * vs is rounded on its own (the library builds without fp
         // contraction), as the serial path rounds it when storing it
         res = acc + p.gamma[0] * vs;
@@ -280,21 +369,23 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
     if (iok && li == LPRF - 1) p.out[i] = f32_to_bf16(res);
 }
 
-template <int LPRH, int NCHH, int LPRF, int NCHF>
+template <int FMT, int LPRH, int NCHH, int SLPRH, int SNCHH, int LPRF, int NCHF, int SLPRF, int SNCHF>
 hipError_t launch_shape(const Stage1Params &a, const Stage2Params &b, int which, hipStream_t s) {
     constexpr int JT = kWavesPerBlock * (kWave / LPRH);
+    constexpr int SJT = kWavesPerBlock * (kWave / SLPRH);
     constexpr int IT = kWavesPerBlock * (kWave / LPRF);
     Stage1Params p1 = a;
     p1.a_tiles = (p1.slots.F + JT - 1) / JT;
-    p1.s_tiles = p1.s_tiles ? (p1.slots.F + JT - 1) / JT : 0;
+    p1.s_tiles = p1.s_tiles ? (p1.slots.F + SJT - 1) / SJT : 0;
     const int blocks1 = p1.gather_blocks + p1.s_tiles + p1.K * p1.a_tiles;
     if (which & 1) {
-        hipLaunchKernelGGL((stage1_kernel<LPRH, NCHH>), dim3(blocks1), dim3(kThreads), 0, s, p1);
+        hipLaunchKernelGGL((stage1_kernel<FMT, LPRH, NCHH, SLPRH, SNCHH>), dim3(blocks1), dim3(kThreads),
+                           0, s, p1);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (which & 2) {
-        hipLaunchKernelGGL((stage2_kernel<LPRF, NCHF>), dim3((b.slots.H + IT - 1) / IT),
+        hipLaunchKernelGGL((stage2_kernel<FMT, LPRF, NCHF, SLPRF, SNCHF>), dim3((b.slots.H + IT - 1) / IT),
                            dim3(kThreads), 0, s, b);
         return hipGetLastError();
     }
@@ -303,22 +394,26 @@ hipError_t launch_shape(const Stage1Params &a, const Stage2Params &b, int which,
 
 }  // namespace stage_detail
 
-// (H chunks, F chunks) with instantiated stage kernels.
-#define MOE_STAGE_SHAPES(X)                                                                  \
-    X(8, 8, 1, 16, 16, 1)       /* H 64,   F 128  */                                         \
-    X(128, 64, 2, 32, 32, 1)    /* H 1024, F 256  */                                         \
-    X(128, 64, 2, 64, 64, 1)    /* H 1024, F 512  */                                         \
-    X(256, 64, 4, 32, 32, 1)    /* H 2048, F 256  */                                         \
-    X(256, 64, 4, 64, 64, 1)    /* H 2048, F 512  */                                         \
-    X(256, 64, 4, 128, 64, 2)   /* H 2048, F 1024 */                                         \
-    X(512, 64, 8, 64, 64, 1)    /* H 4096, F 512  */                                         \
-    X(512, 64, 8, 128, 64, 2)   /* H 4096, F 1024 */
+// (H, F) with instantiated stage kernels, and the lanes per row (LPR) and
+// chunks per lane (NCH) of each row kind: LPR = min(chunks, 64), as the
+// serial kernels choose them (MOE_ROW_SWITCH), so that every dot product
+// reduces through the same trees.  Columns: H, F, then for bf16 rows
+// (16-byte chunks of 8 elements) gate/up (LPR, NCH) and down (LPR, NCH),
+// then for 4-bit rows (chunks of 32 elements) the same.
+#define MOE_STAGE_SHAPES(X)                           \
+    X(64, 128, 8, 1, 16, 1, 2, 1, 4, 1)               \
+    X(1024, 256, 64, 2, 32, 1, 32, 1, 8, 1)           \
+    X(1024, 512, 64, 2, 64, 1, 32, 1, 16, 1)          \
+    X(2048, 256, 64, 4, 32, 1, 64, 1, 8, 1)           \
+    X(2048, 512, 64, 4, 64, 1, 64, 1, 16, 1)          \
+    X(2048, 1024, 64, 4, 64, 2, 64, 1, 32, 1)         \
+    X(4096, 512, 64, 8, 64, 1, 64, 2, 16, 1)          \
+    X(4096, 1024, 64, 8, 64, 2, 64, 2, 32, 1)
 
 bool stage_supported(int fmt, int H, int F) {
-    if (fmt != MOE_FMT_BF16) return false;
-    const int ch = H / 8, cf = F / 8;
-#define MOE_STAGE_HAS(CH, LH, NH, CF, LF, NF) \
-    if (ch == CH && cf == CF) return true;
+    if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_E2M1 && fmt != MOE_FMT_MXFP4) return false;
+#define MOE_STAGE_HAS(SH, SF, A, B, C, D, E_, F_, G, H_) \
+    if (H == SH && F == SF) return true;
     MOE_STAGE_SHAPES(MOE_STAGE_HAS)
 #undef MOE_STAGE_HAS
     return false;
@@ -394,9 +489,16 @@ hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, co
                              {shared ? gamma : nullptr, rec::kRead}, {addend, rec::kRead}, {out, rec::kWrite}});
         return e;
     }
-    const int ch = slots.H / 8, cf = slots.F / 8;
-#define MOE_STAGE_CALL(CH, LH, NH, CF, LF, NF) \
-    if (ch == CH && cf == CF) return launch_shape<LH, NH, LF, NF>(a, b, which, s);
+    const int H = slots.H, F = slots.F;
+#define MOE_STAGE_CALL(SH, SF, BLH, BNH, BLF, BNF, QLH, QNH, QLF, QNF)                                   \
+    if (H == SH && F == SF) {                                                                        \
+        if (slots.fmt == MOE_FMT_BF16)                                                               \
+            return launch_shape<MOE_FMT_BF16, BLH, BNH, BLH, BNH, BLF, BNF, BLF, BNF>(a, b, which, s); \
+        if (slots.fmt == MOE_FMT_E2M1)                                                               \
+            return launch_shape<MOE_FMT_E2M1, QLH, QNH, BLH, BNH, QLF, QNF, BLF, BNF>(a, b, which, s); \
+        if (slots.fmt == MOE_FMT_MXFP4)                                                              \
+            return launch_shape<MOE_FMT_MXFP4, QLH, QNH, BLH, BNH, QLF, QNF, BLF, BNF>(a, b, which, s); \
+    }
     MOE_STAGE_SHAPES(MOE_STAGE_CALL)
 #undef MOE_STAGE_CALL
     return hipErrorNotSupported;

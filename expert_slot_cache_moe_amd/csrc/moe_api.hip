@@ -340,6 +340,23 @@ GatherParams gather_params(const moe_cache *c) {
     return gather_params(c, c->last_layer, c->n_miss, c->plan_slot, c->plan_expert);
 }
 
+// The same plan for stage 1's gather role: with 4-bit weights the gate/up
+// scale bank travels with the units of the codes it scales.
+GatherParams gather_params_staged(const moe_cache *c) {
+    GatherParams g = gather_params(c);
+    if (c->d.weight_format == MOE_FMT_BF16 || c->nb < 2) return g;
+    const int unit = gather_unit_bytes();
+    int units = 0;
+    for (int b = 0; b < c->nb; ++b) {
+        g.unit_start[b] = units;
+        if (b != 1) units += (int)((c->rb[b] + unit - 1) / unit);
+    }
+    g.unit_start[c->nb] = units;
+    g.units_per_entry = units;
+    g.carry_scales = c->d.weight_format == MOE_FMT_E2M1 ? 2 : 1;
+    return g;
+}
+
 moe_status_t launch_gather_checked(moe_cache *c, hipStream_t s) {
     if (c->nb == 0) return MOE_OK;
     HIP_TRY(launch_gather(gather_params(c), c->gather_wg, s), "gather launch");

@@ -135,6 +135,7 @@ moe_status_t launch_admit_checked(moe_cache *c, int layer, int32_t *ids, int R, 
 GatherParams gather_params(const moe_cache *c, int layer, const int32_t *n, const int32_t *ps,
                            const int32_t *pe);
 GatherParams gather_params(const moe_cache *c);
+GatherParams gather_params_staged(const moe_cache *c);
 moe_status_t launch_gather_checked(moe_cache *c, hipStream_t s);
 
 }  // namespace api

@@ -242,6 +242,11 @@ struct GatherParams {
     const uint8_t *host[MOE_MAX_BANKS];    // layer's rows [E][rb], device-visible
     uint8_t *slot[MOE_MAX_BANKS];          // [S][rb]
     int64_t rb[MOE_MAX_BANKS];
+    // Staged one-token step, 4-bit formats: bank 1 (the gate/up scales)
+    // has no units of its own; each bank-0 unit copies the scales of its
+    // chunks, carry_scales bytes per 16-byte chunk (2: E4M3 pair, 1: E8M0).
+    // 0 everywhere else.
+    int32_t carry_scales;
 };
 
 // Work items of the expert kernels.
@@ -315,7 +320,7 @@ hipError_t launch_down_fused(const PoolView &pool, const int32_t *idx, const flo
 hipError_t launch_combine(const int32_t *idx, const float *w, int T, int K, int H, int num_rows,
                           const float *d, const float *addend, uint16_t *out, hipStream_t s);
 
-// The single-token layer step in two launches (bf16): stage 1 = miss gather
+// The single-token layer step in two launches: stage 1 = miss gather
 // (+ the fetched experts' gate/up dots into gu [plan][2F]) | shared gate/up
 // | resident routes' gate/up; stage 2 = all down projections + combine.
 bool stage_supported(int fmt, int H, int F);

@@ -107,7 +107,7 @@ moe_status_t moe_layer_decode(moe_cache_t *c, int32_t layer, const void *x, cons
         }
         for (int which = 1; which <= 2; ++which) {
             if (timing) HIP_TRY(record_timing(tev[2 * which], s), "timing");
-            HIP_TRY(launch_stages(gather_params(c), c->gather_wg, c->ws_gu, pv, ids, w,
+            HIP_TRY(launch_stages(gather_params_staged(c), c->gather_wg, c->ws_gu, pv, ids, w,
                                   c->ws_route_plan, K, static_cast<const uint16_t *>(x),
                                   reinterpret_cast<uint16_t *>(c->ws_routed + rw.h),
                                   shared ? &spv : nullptr, hs,

@@ -120,8 +120,8 @@ typedef struct {
                                     shared expert and the resident routes run
                                     as disjoint workgroups of one kernel, the
                                     down projections and combine in a second
-                                    (single-token bf16 steps; other steps run
-                                    as 0);
+                                    (single-token steps of any format at the
+                                    supported widths; other steps run as 0);
                                  3: the split of the #678 variant [P2 "What we
                                     changed", difference from #678]: the
                                     shared expert and its gate on the side

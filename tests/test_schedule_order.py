@@ -32,7 +32,7 @@ LAYERS, TOKENS = 3, 3
 
 
 def _trace(overlap, T, fmt, shared, prefetch):
-    H, F = (64, 128) if fmt == 0 else (64, 64)
+    H, F = 64, 128          # a shape with staged kernels in every format
     return m.moe_trace_layer_steps(num_layers=LAYERS, num_experts=16, num_slots=8, hidden=H, ffn=F,
                                    T=T, K=2, overlap=overlap, weight_format=fmt, with_shared=shared,
                                    prefetch_width=4 if prefetch else 0, tokens=TOKENS)
@@ -182,3 +182,19 @@ def test_trace_rejects_bad_arguments():
     with pytest.raises(m.MoeError):
         m.moe_trace_layer_steps(num_layers=1, num_experts=8, num_slots=4, hidden=64, ffn=128, T=1, K=9,
                                 overlap=0)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_staged_schedule_covers_single_token_steps_of_every_format(fmt):
+    """Schedule 2 runs a one-token step as admission + two stage launches
+    in bf16, E2M1 and MXFP4 alike; wider steps and other schedules keep the
+    separate gather."""
+    for H, F in ((64, 128), (2048, 512), (1024, 256)):
+        ops = _parse(m.moe_trace_layer_steps(num_layers=1, num_experts=32, num_slots=12, hidden=H, ffn=F,
+                                             T=1, K=8, overlap=2, weight_format=fmt, tokens=1))
+        assert [op["name"] for op in ops if op["kind"] == "L"] == ["admit_kernel", "stage1_kernel",
+                                                                  "stage2_kernel"]
+    ops = _parse(m.moe_trace_layer_steps(num_layers=1, num_experts=32, num_slots=12, hidden=64, ffn=128,
+                                         T=3, K=2, overlap=2, weight_format=fmt, tokens=1))
+    assert "gather_kernel" in [op["name"] for op in ops]
+
