@@ -128,28 +128,56 @@ def traffic_ratios():
     return {k: float(v) for k, v in vals.items() if k.endswith("_ratio")}
 
 
-def build_stack(torch, m, W, seed=0, gather_workgroups=0, overlap=1):
-    """Pinned host store for 40 x 256 experts, shared experts, the cache."""
-    from expert_slot_cache_moe_amd.layer import SlotCacheLayers
+_SHARED = {}
 
+
+def shared_experts(W, seed=0):
+    """The 40 layers' gated shared experts (bf16 N(0, 0.02)), drawn once."""
+    if seed not in _SHARED:
+        gs = W.rng(seed, "bench", "shared")
+        _SHARED[seed] = [(W.normal_bf16(gs, 2 * F * H, 0.02), W.normal_bf16(gs, H * F, 0.02),
+                          W.normal_bf16(gs, H, 0.02)) for _ in range(L)]
+    return _SHARED[seed]
+
+
+def host_store(torch, W, fmt=0, seed=0):
+    """Pinned host rows of 40 x 256 experts in format fmt: every expert of
+    every layer drawn afresh on the device (N(0, 0.02), stored as bf16 or
+    quantized to 4 bits), then copied into the layer's pinned host rows."""
     t0 = time.time()
     host = []
     for l in range(L):
-        # every expert of every layer drawn afresh (N(0, 0.02) as bf16), on the
-        # device, then copied into the layer's pinned host rows
-        dev = W.device_expert_rows(0, (seed, "bench", l), E, H, F)
+        dev = W.device_expert_rows(fmt, (seed, "bench", l) if fmt == 0 else (seed, "bench", fmt, l), E, H, F)
         host.append([W.pinned_copy(b) for b in dev])
         del dev
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    log(f"[bench] pinned host store {L * E * ROW_BYTES / 1e9:.1f} GB in {time.time() - t0:.1f}s")
-    gs = W.rng(seed, "bench", "shared")
-    shared = [(W.normal_bf16(gs, 2 * F * H, 0.02), W.normal_bf16(gs, H * F, 0.02),
-               W.normal_bf16(gs, H, 0.02)) for _ in range(L)]
-    lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, host_rows=host,
-                          shared=shared, max_tokens=1, max_top_k=K, overlap=overlap,
+    nbytes = sum(b.numel() for hl in host for b in hl)
+    log(f"[bench] pinned host store, format {fmt}: {nbytes / 1e9:.1f} GB in {time.time() - t0:.1f}s")
+    return host
+
+
+def build_stack(torch, m, W, seed=0, gather_workgroups=0, overlap=1, fmt=0, host=None):
+    """Pinned host store for 40 x 256 experts, shared experts, the cache."""
+    from expert_slot_cache_moe_amd.layer import SlotCacheLayers
+
+    if host is None:
+        host = host_store(torch, W, fmt, seed)
+    lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, fmt=fmt, host_rows=host,
+                          shared=shared_experts(W, seed), max_tokens=1, max_top_k=K, overlap=overlap,
                           gather_workgroups=gather_workgroups)
     return lay
+
+
+def release_pinned(torch):
+    """Hands torch's cached pinned host blocks back (a leg's store is freed)."""
+    import gc
+
+    gc.collect()
+    torch.cuda.synchronize()
+    if hasattr(torch._C, "_host_emptyCache"):
+        torch._C._host_emptyCache()
+    torch.cuda.empty_cache()
 
 
 def make_trace(torch, W, n, seed=0):
@@ -456,6 +484,165 @@ def hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok):
     return {"threads": HYBRID_THREADS, "tokens": n, "runs": res}
 
 
+# The same decode trace over 4-bit experts: E2M1 codes with one E4M3 scale
+# per 16 elements and an fp32 global per matrix (the pages' decode model is
+# NVFP4): 1.77 MB per expert, an 18.1 GB pinned host store, 5.6 GB of slots.
+DECODE_4BIT_SCHEDULES = (2, 0)
+
+
+def decode_4bit_benchmark(torch, m, W, x_all, lg_all, n_warm, n_tok, fmt=1, seed=0):
+    """The timed tokens of the trace (after the same cache warm-up) over a
+    40 x 256 stack of 4-bit experts, each token one graph, under the staged
+    schedule (2) and the serial one (0)."""
+    host = host_store(torch, W, fmt, seed)
+    rb = m.moe_bank_row_bytes(fmt, H, F)
+    runs = []
+    try:
+        for ov in DECODE_4BIT_SCHEDULES:
+            lay = build_stack(torch, m, W, seed, overlap=ov, fmt=fmt, host=host)
+            try:
+                x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+                lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
+                out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+                tok = torch.zeros(1, dtype=torch.int64, device="cuda")
+                graph = capture(torch, lay, x_st, lg_st, out, (x_all, lg_all, tok))
+                for _ in range(n_warm):
+                    graph.replay()
+                torch.cuda.synchronize()
+                st0 = m.moe_cache_stats(lay.cache)
+                t0 = time.perf_counter()
+                toks = leg_tokens(n_warm, n_tok)
+                for _ in toks:
+                    graph.replay()
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
+                d = m.moe_cache_stats(lay.cache) - st0
+                n = len(toks)
+                fetched = float(d[m.MOE_STAT_MISSED] - d[m.MOE_STAT_OVERFLOW]) / n
+                runs.append({"overlap": ov, "value": round(L * n / dt, 1), "ms_per_step": round(dt / n * 1000.0, 4),
+                             "misses_per_token": round(fetched, 2),
+                             "gathered_gb_per_s": round(fetched * sum(rb) / (dt / n) / 1e9, 2)})
+                log(f"[bench] 4-bit decode, schedule {ov}: {runs[-1]}")
+                del graph
+            finally:
+                lay.close()
+    finally:
+        del host
+        release_pinned(torch)
+    return {"workload": "the shared-expert decode trace over E2M1 experts (E4M3 per-16 scales, fp32 "
+                        "globals): 40 x 256, top-8 + bf16 gated shared expert, H 2048, F 512, 3164 slots",
+            "expert_bytes": int(sum(rb)), "tokens": len(leg_tokens(n_warm, n_tok)), "runs": runs}
+
+
+# The other configurations as whole layer steps (admission, miss gather
+# from pinned host memory, routed experts, combine), each step captured as
+# a graph: (name, format, layers, experts, slots, H, F, top-k, token rows,
+# widths (one-call, query), shared expert, residents before each step).
+CONFIG_STEPS = (
+    ("tiny decode: 1 layer, 8 experts, top-2, H 64, F 128, 4 slots, 32 steps", 0, 8, 4, 64, 128, 2, 1,
+     (256, 128), False, None),
+    ("tiny decode + gated shared expert (F 128)", 0, 8, 4, 64, 128, 2, 1, (256, 128), True, None),
+    ("wide decode bf16: 150 rows x top-2 over 160 experts, 7 resident, 160 slots, H 1024, F 256", 0, 160,
+     160, 1024, 256, 2, 150, (256, 128), False, 7),
+    ("wide decode e2m1: 600 rows x top-2 over 160 experts, cold 1100 slots, H 1024, F 256", 1, 160, 1100,
+     1024, 256, 2, 600, (256, 128), False, 0),
+    ("prefill chunk bf16: 42 rows x top-6 over 256 experts, cold 256 slots, H 4096, F 1024", 0, 256, 256,
+     4096, 1024, 6, 42, (256, 128), False, 0),
+    ("prefill chunk bf16: 50 rows x top-6 over 640 experts, cold 640 slots, H 4096, F 1024", 0, 640, 640,
+     4096, 1024, 6, 50, (256, 128), False, 0),
+)
+CONFIG_REPLAYS = 3
+TINY_STEPS = 32
+
+
+def config_steps_benchmark(torch, m, W, seed=0):
+    """Each configuration's layer step.  Tiny: 32 decode steps of the Tiny
+    trace (Zipf(1.1) router logits) in one graph, replayed; layer-steps/s.
+    Wide and prefill: the step from its stated cache state (restored before
+    each replay), one graph per step, HIP events around it; microseconds
+    per step and the rate of the miss gather inside it."""
+    from expert_slot_cache_moe_amd.layer import SlotCacheLayers
+
+    res = []
+    for name, fmt, Ec, Sc, Hc, Fc, Kc, T, (one, qw), shared, residents in CONFIG_STEPS:
+        g = W.rng(seed, "bench", "config", name)
+        host = [[W.pinned_copy(b) for b in W.device_expert_rows(fmt, (seed, "config", name), Ec, Hc, Fc)]]
+        sh = None
+        if shared:
+            sh = [(W.normal_bf16(g, 2 * Fc * Hc, 0.02), W.normal_bf16(g, Hc * Fc, 0.02),
+                   W.normal_bf16(g, Hc, 0.02))]
+        lay = SlotCacheLayers(layers=1, experts=Ec, slots=Sc, hidden=Hc, ffn=Fc, fmt=fmt, host_rows=host,
+                              shared=sh, max_tokens=T, max_top_k=Kc, overlap=2, one_call_width=one,
+                              query_width=qw, max_routes=max(T * Kc, 1))
+        try:
+            stream = torch.cuda.Stream()
+            rb = m.moe_bank_row_bytes(fmt, Hc, Fc)
+            if T == 1:
+                lgs = torch.from_numpy(W.tiny_logits(seed, TINY_STEPS)).cuda()
+                xs = torch.from_numpy(W.normal_bf16(g, (TINY_STEPS, 1, Hc)).view(np.int16)).cuda()
+                out = torch.empty((TINY_STEPS, 1, Hc), dtype=torch.int16, device="cuda")
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    for t in range(TINY_STEPS):
+                        lay.decode(0, xs[t], lgs[t], Kc, out[t])
+                for _ in range(3):
+                    graph.replay()
+                torch.cuda.synchronize()
+                st0 = m.moe_cache_stats(lay.cache)
+                reps = 20
+                t0 = time.perf_counter()
+                for _ in range(reps):
+                    graph.replay()
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
+                d = m.moe_cache_stats(lay.cache) - st0
+                n = reps * TINY_STEPS
+                res.append({"workload": name, "value": round(n / dt, 1), "unit": "layer-steps/s",
+                            "us_per_step": round(dt / n * 1e6, 2),
+                            "misses_per_step": round(float(d[m.MOE_STAT_MISSED]) / n, 3)})
+            else:
+                if fmt == 0 and residents:
+                    chosen = W.wide_bf16_routes(seed)
+                else:
+                    chosen = np.stack([g.choice(Ec, Kc, replace=False) for _ in range(T)])
+                lg = torch.from_numpy(W.forced_logits(g, chosen, Ec)).cuda()
+                x = torch.from_numpy(W.normal_bf16(g, (T, Hc)).view(np.int16)).cuda()
+                out = torch.empty((T, Hc), dtype=torch.int16, device="cuda")
+                if residents:
+                    pre = torch.from_numpy(g.permutation(Ec)[:residents].astype(np.int32)).cuda()
+                    m.moe_admit(lay.cache, 0, pre)
+                    m.moe_gather_misses(lay.cache)
+                torch.cuda.synchronize()
+                snap = m.moe_cache_read_state(lay.cache)
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    lay.decode(0, x, lg, Kc, out, stream=stream)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                us = []
+                for r in range(1 + CONFIG_REPLAYS):
+                    m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"])
+                    st0 = m.moe_cache_stats(lay.cache)
+                    # the replay runs on the current stream: the events bracket it there
+                    e0.record()
+                    graph.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    if r:
+                        us.append(e0.elapsed_time(e1) * 1000.0)
+                    fetched = int((m.moe_cache_stats(lay.cache) - st0)[m.MOE_STAT_MISSED])
+                u = float(np.median(us))
+                gathered = fetched * sum(rb)
+                res.append({"workload": name, "us_per_step": round(u, 1), "value": round(1e6 / u, 2),
+                            "unit": "layer-steps/s", "routes": T * Kc, "fetched_experts": fetched,
+                            "gathered_bytes": gathered, "gather_inclusive_gb_per_s": round(gathered / u / 1e3, 2)})
+            log(f"[bench] config step: {res[-1]}")
+        finally:
+            lay.close()
+            del host
+            release_pinned(torch)
+    return res
+
+
 # Oracle admission timing: the admission-only workload's one-layer cache
 # (512 experts pre-filled into 2100 slots), single-threaded, µs per
 # admission at these batches (10, 480 and 1280 routes).
@@ -494,13 +681,13 @@ def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
     gathers (no math) to reach the same cache state."""
     import oracle
 
+    # the oracle's own host store (timing only): 64 distinct bf16 rows, expert
+    # (l, e) holding row (l E + e) 7919 mod 64
     g = W.rng(seed, "bench", "experts")
     distinct = 64
     base = W.bf16_expert_rows(g, distinct, H, F)
     host_idx = lambda l: ((np.arange(l * E, (l + 1) * E) * 7919) % distinct)
-    gs = W.rng(seed, "bench", "shared")
-    shared = [(W.normal_bf16(gs, 2 * F * H, 0.02), W.normal_bf16(gs, H * F, 0.02),
-               W.normal_bf16(gs, H, 0.02)) for _ in range(L)]
+    shared = shared_experts(W, seed)
     slots = [np.zeros((S, 4 * F * H), np.uint8), np.zeros((S, 2 * F * H), np.uint8)]
     tr = W.DecodeTrace(seed, L, E, K)
     gx = W.rng(seed, "bench", "hidden")
@@ -518,6 +705,7 @@ def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
                 slots[1][s] = base[1][r]
     pool = oracle.Pool(0, H, F, slots)
     n = 0
+    steps = []
     t0 = time.perf_counter()
     for t in range(sample_tokens):
         sets = tr.step_sets()
@@ -530,12 +718,62 @@ def cpu_baseline(W, warm_tokens, sample_tokens, seed=0):
             oracle.gather(base, slots, oc.plan_slot, host_idx(l)[oc.plan_expert].astype(np.int32))
             _, add = oracle.shared(H, F, *shared[l], xs[l])
             oracle.routed(pool, sl, w, xs[l], addend=add)
+            steps.append((l, lg[l:l + 1].copy(), xs[l].copy()))
             n += 1
     dt = time.perf_counter() - t0
+
+    # The layer math of the same layer-steps (top-k, shared expert, routed
+    # experts over the host store: the same bytes the slots hold) on every
+    # host core: one layer-step per task, the oracle's calls release the
+    # interpreter lock; each dot product stays sequential.
+    from concurrent.futures import ThreadPoolExecutor
+
+    hpool = oracle.Pool(0, H, F, base)
+
+    def layer_math(st):
+        l, lgl, x = st
+        ids, w = oracle.topk(lgl, K)
+        _, add = oracle.shared(H, F, *shared[l], x)
+        return oracle.routed(hpool, host_idx(l)[ids].astype(np.int32), w, x, addend=add)
+
+    cores = len(os.sched_getaffinity(0))
+    t1 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(layer_math, steps))
+    dt_all = time.perf_counter() - t1
     return {"value": round(n / dt, 3), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} layer-steps ({sample_tokens} tokens x {L} layers) of the shared-expert "
                       f"decode trace after {warm_tokens} tokens of admission+gather warm-up; "
-                      f"single-threaded C oracle (double precision), {dt:.1f} s"}
+                      f"single-threaded C oracle (double precision), {dt:.1f} s",
+            "all_cores": {"value": round(n / dt_all, 3), "unit": "layer-steps/s", "cores": cores,
+                          "kind": "oracle",
+                          "sample": f"the layer math of the same {n} layer-steps (top-k, shared expert, "
+                                    f"routed experts; no admission or gather), one layer-step per "
+                                    f"thread task, {dt_all:.1f} s"},
+            "host": host_description()}
+
+
+def host_description() -> dict:
+    """CPU model, logical CPUs (and those this process may use) and RAM of
+    the machine the baseline ran on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    mem = 0
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                mem = int(line.split()[1]) * 1024
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)),
+            "ram_gb": round(mem / 2 ** 30, 1)}
 
 
 DECODE_KERNELS = ("admit_fast_kernel", "admit_kernel", "topk_kernel", "stage1_kernel", "stage2_kernel",
@@ -845,6 +1083,8 @@ def main():
     ap.add_argument("--no-lookahead", action="store_true", help="skip the look-ahead prefetch runs")
     ap.add_argument("--no-schedules", action="store_true", help="skip the other layer-step schedules")
     ap.add_argument("--no-hybrid", action="store_true", help="skip the hybrid CPU/GPU runs")
+    ap.add_argument("--no-4bit", action="store_true", help="skip the 4-bit decode runs")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other configurations' layer steps")
     ap.add_argument("--only-wide", action="store_true",
                     help="run only the wide-step routed GEMV shapes (one JSON line each)")
     ap.add_argument("--summarize-counters", nargs="+", default=None, metavar="COUNTER_CSV",
@@ -1056,6 +1296,10 @@ def main():
         "hybrid", hybrid_benchmark, torch, m, lay, snap, x_all, lg_all, first, n_tok)
     lay.close()
     del lay
+    release_pinned(torch)
+    dec4 = None if args.no_4bit else run_leg(
+        "4-bit decode", decode_4bit_benchmark, torch, m, W, x_all, lg_all, n_warm, n_tok)
+    steps_cfg = None if args.no_configs else run_leg("config steps", config_steps_benchmark, torch, m, W)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_leg("cpu baseline", cpu_baseline, W, n_warm, args.cpu_sample_tokens)
@@ -1110,6 +1354,8 @@ def main():
         "lookahead": look,
         "schedules": sched,
         "hybrid": hyb,
+        "decode_4bit": dec4,
+        "config_steps": steps_cfg,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
