@@ -971,6 +971,29 @@ def summarize_trace(csv_path, log_path):
     p(f"| stage1 + stage2, all-hit layer steps (8 routed + shared expert) | {int(hit.sum())} | "
       f"{(dur(timed, 1) + dur(timed, 2))[hit].mean():.2f} |")
     p("")
+    d4 = line.get("decode_4bit") if line else None
+    if d4 and "runs" in d4:
+        # the 4-bit leg runs schedule 2 first (warm-up tokens, then the timed
+        # ones; its token graphs hold admission, stage 1 and stage 2 of the
+        # E2M1 kernels), then schedule 0
+        Lx = log["layers"]
+        n = d4["tokens"] * Lx
+        w0 = log.get("warm_tokens", log["warmup"]) * Lx
+        st = {k: [d["us"] for d in disp if d["k"] == k and "<1," in d["name"]]
+              for k in ("stage1_kernel", "stage2_kernel")}
+        if len(st["stage1_kernel"]) >= w0 + n:
+            s1 = np.asarray(st["stage1_kernel"][w0:w0 + n])
+            s2 = np.asarray(st["stage2_kernel"][w0:w0 + n])
+            fetch = s1 > 15.0
+            p("## 4-bit decode (E2M1 experts, schedule 2), its timed tokens\n")
+            p("| launch | launches | rocprofv3 mean µs |")
+            p("|---|---|---|")
+            p(f"| stage1_kernel<E2M1>, layer steps that fetched (above 15 µs) | {int(fetch.sum())} | "
+              f"{s1[fetch].mean() if fetch.any() else 0:.2f} |")
+            p(f"| stage1_kernel<E2M1>, all-hit layer steps | {int((~fetch).sum())} | "
+              f"{s1[~fetch].mean() if (~fetch).any() else 0:.2f} |")
+            p(f"| stage2_kernel<E2M1>, all layer steps | {len(s2)} | {s2.mean():.2f} |")
+            p("")
     if line:
         p("## bench.py line of the same run\n")
         p("    " + json.dumps(line))
@@ -1147,6 +1170,7 @@ def main():
     for t in range(n_warm):                # cache warm-up (and graph warm-up): untimed
         step(t)
     torch.cuda.synchronize()
+    log(f"[bench] cache warm-up: {n_warm} tokens")
     snap = m.moe_cache_read_state(lay.cache)
     st0 = m.moe_cache_stats(lay.cache)
     t0 = time.perf_counter()
@@ -1191,6 +1215,7 @@ def main():
         k1_ms.append(ms[:, 1])
         pair_ms.append([pairs[0][l].elapsed_time(pairs[1][l]) for l in range(L)])
     m.moe_cache_set_timing(lay.cache, False)
+    log("[bench] instrumented pass done")
     fetch_l = np.concatenate(fetch_l)
     k1_raw = np.concatenate(k1_ms)
     pair_us = float(np.mean(pair_ms)) * 1000.0
@@ -1236,6 +1261,7 @@ def main():
         if r > 0:
             per_call.append(g0.elapsed_time(g1) * 1000.0 / (GEMV_PASSES * L))
     rout_us = float(np.mean(per_call))
+    log(f"[bench] routed-GEMV phase: {rout_us:.2f} us per call")
     assert (ids_l >= 0).all(), "the GEMV phase reads resident slots only"
     gemv_bytes = K * ROW_BYTES + 2 * H * 2 + K * 8     # 8 experts' rows, x and out, ids and weights
     gemv_gbs = gemv_bytes / (rout_us * 1e-6) / 1e9
