@@ -146,6 +146,72 @@ __device__ __forceinline__ float matrix_glob(const PoolView &p, int64_t prow, in
     }
 }
 
+// A lane's codes of one 4-bit weight row for the LDS-staged kernels, from
+// slab 0, so slab s is a constant offset away (one address per row instead
+// of one per slab in flight).
+struct QRow {
+    const uint8_t *codes;
+    __device__ __forceinline__ void at(const PoolView &p, int fmt, int64_t prow, int m, int r, int q) {
+        const int ncols = m == 0 ? p.H : p.F;
+        const int b = (fmt == MOE_FMT_E2M1 ? 3 : 2) * m;
+        codes = p.bank[b] + prow * p.rb[b] + (int64_t)r * (ncols / 2) + 16 * q;
+    }
+    __device__ __forceinline__ u32x4 load(int s) const {
+        return *reinterpret_cast<const u32x4 *>(codes + s * (kSlab / 2));
+    }
+};
+
+// The scales of 4-bit weight rows pass through LDS.  A slab's scales for a
+// lane are 2 bytes (E2M1) or 1 byte (MXFP4) of its row, a few bytes apart
+// from the next lane's: loaded straight from HBM, every slab costs a load
+// instruction that touches 16 rows for a few bytes each, and those small
+// requests, not the bytes, bounded the kernels (measured on MI355X: the
+// gate/up kernel's loads took 22.7 us with them, 13.3 us without).  Each
+// row's scale bytes are instead loaded in 4-16 byte vectors, written to
+// LDS rows of SB + 4 bytes (bank spread), and read back per slab.
+template <int FMT, int COLS> struct QScales {
+    static constexpr int SB = COLS / (FMT == MOE_FMT_E2M1 ? 16 : 32);   // scale bytes per row
+    static constexpr int PITCH = SB + 4;
+    // scale byte offset of lane q's elements of slab s within a row
+    __device__ static constexpr int offset(int s, int q) {
+        return FMT == MOE_FMT_E2M1 ? 8 * s + 2 * q : 4 * s + q;
+    }
+    __device__ static const uint8_t *row_ptr(const PoolView &p, int64_t prow, int m, int r) {
+        const int b = (FMT == MOE_FMT_E2M1 ? 3 : 2) * m + 1;
+        return p.bank[b] + prow * p.rb[b] + (int64_t)r * SB;
+    }
+    // N bytes (a multiple of 4, 4-byte aligned) of scales in registers:
+    // loaded from HBM, later written to LDS (after the code loads issue).
+    template <int N> struct Chunk {
+        static_assert(N % 4 == 0, "whole dwords");
+        uint32_t v[N / 4];
+        __device__ void load(const uint8_t *src) {
+            if constexpr (N % 16 == 0) {
+#pragma unroll
+                for (int i = 0; i < N / 16; ++i) {
+                    const u32x4 t = reinterpret_cast<const u32x4 *>(src)[i];
+                    v[4 * i] = t[0], v[4 * i + 1] = t[1], v[4 * i + 2] = t[2], v[4 * i + 3] = t[3];
+                }
+            } else if constexpr (N == 8) {
+                const uint2 t = *reinterpret_cast<const uint2 *>(src);
+                v[0] = t.x, v[1] = t.y;
+            } else {
+                v[0] = *reinterpret_cast<const uint32_t *>(src);
+            }
+        }
+        __device__ void store(uint8_t *dst) const {
+#pragma unroll
+            for (int i = 0; i < N / 4; ++i) reinterpret_cast<uint32_t *>(dst)[i] = v[i];
+        }
+    };
+    __device__ static uint32_t read(const uint8_t *lds_row, int s, int q) {
+        if constexpr (FMT == MOE_FMT_E2M1)
+            return *reinterpret_cast<const uint16_t *>(lds_row + offset(s, q));
+        else
+            return lds_row[offset(s, q)];
+    }
+};
+
 // 32 bf16 activations of one token row for one slab.
 __device__ __forceinline__ void load_b(const uint16_t *row, int e0, u32x4 (&b)[4]) {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(row + e0);
@@ -352,6 +418,250 @@ __global__ __launch_bounds__(kMThreads, 2) void down_mfma_kernel(PoolView pool, 
     }
 }
 
+// ------------------------------------------------------------------ 4-bit weights, activations in LDS
+
+// For 4-bit weights the activations are the larger operand: a 16-token
+// batch of bf16 rows is four times the codes of a 16-row weight tile.  The
+// kernels above hold a wave's own copy of them in registers, which leaves
+// room for few weight slabs in flight at two waves per SIMD.  The kernels
+// below stage a batch's 16 activation rows once per workgroup of four
+// waves in LDS, and the scales of every wave's rows too (QScales); a wave
+// keeps kXAhead slabs of codes in flight and three or four waves share a
+// SIMD.  Measured on MI355X at the wide E2M1 step (H 1024, F 256, 160
+// groups): gate/up 23.6 -> 18.2 us, down 12.7 -> 12.6 us; MXFP4 19.3 ->
+// 14.1 and 11.1 -> 9.7 us.  Slab order, contraction permutation and MFMA
+// sequence are those of the kernels above (with one row tile per gate/up
+// wave), so both compute the same values.
+constexpr int kXWaves = 4;
+constexpr int kXThreads = kXWaves * kWave;
+constexpr int kXPad = 8;          // bf16 elements of padding per staged row (bank spread)
+constexpr int kXAhead = 4;        // slabs a gate/up wave keeps in flight
+constexpr int kXDownAhead = 8;    // (row tile, slab) pairs a down wave keeps in flight
+
+__host__ __device__ constexpr size_t x_rows_lds_bytes(int cols) { return (size_t)kTile * (cols + kXPad) * 2; }
+
+// LDS of the staged kernels: the batch's rows, then the scales of every
+// wave's weight rows (`scale_rows` rows of `scale_pitch` bytes per wave).
+__host__ __device__ constexpr size_t x_lds_bytes(int cols, int scale_rows, int scale_pitch) {
+    return x_rows_lds_bytes(cols) + (size_t)kXWaves * scale_rows * scale_pitch;
+}
+
+// Stages the batch's 16 rows of COLS bf16 elements (row `src_row` for this
+// thread's token column threadIdx.x / (THREADS / 16), chosen by the caller)
+// into LDS rows of COLS + kXPad.  The THREADS / 16 threads of a row copy
+// its 16-byte vectors round-robin, so each load instruction reads whole
+// runs of a row.  All threads of the workgroup take part; the caller
+// places the barriers.
+template <int COLS, int THREADS = kXThreads>
+__device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ src_row, uint16_t *__restrict__ xs) {
+    constexpr int TPR = THREADS / kTile;     // threads per row
+    constexpr int NV = COLS / 8 / TPR;       // vectors per thread
+    static_assert(NV * TPR * 8 == COLS, "whole vectors per thread");
+    const int t = threadIdx.x / TPR, part = threadIdx.x % TPR;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(src_row) + part;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(xs + t * (COLS + kXPad)) + part;
+#pragma unroll
+    for (int v0 = 0; v0 < NV; v0 += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (v0 + i < NV) v[i] = src[(v0 + i) * TPR];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (v0 + i < NV) dst[(v0 + i) * TPR] = v[i];
+    }
+}
+
+// gate/up + SwiGLU as up_mfma_kernel (one row tile per wave, 64 gate and 64
+// up rows per workgroup), the batch's activations from LDS; the hidden
+// width is NS slabs (pool.H == NS * kSlab, launcher).
+template <int FMT, int NS>
+__global__ __launch_bounds__(kXThreads, 3) void up_x_kernel(PoolView pool, Items items,
+                                                            const uint16_t *__restrict__ x,
+                                                            uint16_t *__restrict__ h) {
+    extern __shared__ __align__(16) uint16_t xs[];   // [kTile][H + kXPad], then scales
+    constexpr int H = NS * kSlab, nslab = NS;
+    constexpr int AHEAD = NS < kXAhead ? NS : kXAhead;
+    using QS = QScales<FMT, H>;
+    const int F = pool.F, K = items.K;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int c = lane & (kTile - 1), q = lane / kTile;
+    const int j0 = (blockIdx.x * kXWaves + wave) * kTile;   // < F: F % 64 == 0 (launcher)
+    const int gmax = min(items.n, pool.num_rows);
+    const uint16_t *xc = xs + c * (H + kXPad) + 32 * q;
+    // this wave's scale rows: gate rows 0-15, up rows 16-31
+    uint8_t *qs = reinterpret_cast<uint8_t *>(xs + kTile * (H + kXPad)) + wave * 2 * kTile * QS::PITCH;
+    GroupEntry cur;
+    cur.load(items, blockIdx.y, gmax);
+    for (int gi = blockIdx.y; gi < gmax && cur.valid(pool.num_rows); gi += gridDim.y) {
+        GroupEntry nxt;
+        nxt.load(items, gi + gridDim.y, gmax);
+        const int64_t row = cur.row;
+        const int32_t *list = items.grp_routes + cur.start;
+        for (int base = 0; base < cur.count; base += kTile) {
+            // scales first (lane (c, q) loads quarter q of row c's bytes)
+            constexpr int QB = QS::SB / 4;
+            typename QS::template Chunk<QB> sg, su;
+            sg.load(QS::row_ptr(pool, row, 0, j0 + c) + q * QB);
+            su.load(QS::row_ptr(pool, row, 0, F + j0 + c) + q * QB);
+            ASlab<FMT> wg[AHEAD], wu[AHEAD];
+            QRow rg, ru;
+            rg.at(pool, FMT, row, 0, j0 + c, q);
+            ru.at(pool, FMT, row, 0, F + j0 + c, q);
+#pragma unroll
+            for (int bfr = 0; bfr < AHEAD; ++bfr) {
+                wg[bfr].codes = rg.load(bfr);
+                wu[bfr].codes = ru.load(bfr);
+            }
+            const float glob = matrix_glob<FMT>(pool, row, 0);
+            const int n = min(base + (int)threadIdx.x / kTile, cur.count - 1);
+            const uint16_t *src = x + (int64_t)(list[n] / K) * H;
+            sg.store(qs + c * QS::PITCH + q * QB);      // this wave's own rows: no barrier
+            su.store(qs + (kTile + c) * QS::PITCH + q * QB);
+            __syncthreads();   // the previous batch's rows are consumed
+            stage_rows<H>(src, xs);
+            __syncthreads();
+            f32x4 ag = f32x4{0.f, 0.f, 0.f, 0.f}, au = ag;
+#pragma unroll
+            for (int s0 = 0; s0 < nslab; s0 += AHEAD) {
+#pragma unroll
+                for (int bfr = 0; bfr < AHEAD; ++bfr) {
+                    const int s = s0 + bfr;
+                    if (s < nslab) {
+                        u32x4 ga[4], ua[4], xb[4];
+                        const u32x4 *xp = reinterpret_cast<const u32x4 *>(xc + s * kSlab);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) xb[i] = xp[i];
+                        wg[bfr].sc = QS::read(qs + c * QS::PITCH, s, q);
+                        wu[bfr].sc = QS::read(qs + (kTile + c) * QS::PITCH, s, q);
+                        wg[bfr].expand(ga);
+                        wu[bfr].expand(ua);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            ag = mfma(ga[i], xb[i], ag);
+                            au = mfma(ua[i], xb[i], au);
+                        }
+                        if (s + AHEAD < nslab) {
+                            wg[bfr].codes = rg.load(s + AHEAD);
+                            wu[bfr].codes = ru.load(s + AHEAD);
+                        }
+                    }
+                    // one slab's LDS reads and expansion at a time (hoisting
+                    // them all ahead would spill)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // lane holds rows j0 + 4q + i (i < 4) of token column c: four
+            // consecutive h elements, one 8-byte store
+            if (base + c < cur.count) {
+                const int64_t r = list[base + c];
+                uint32_t hv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16(silu_mul(ag[i] * glob, au[i] * glob));
+                *reinterpret_cast<uint2 *>(h + r * F + j0 + 4 * q) = make_uint2(hv[0] | (hv[1] << 16),
+                                                                                hv[2] | (hv[3] << 16));
+            }
+        }
+        cur = nxt;
+    }
+}
+
+// down projection as down_mfma_kernel (RT row tiles per wave, 64 RT rows
+// per workgroup), the batch's activations h from LDS; the FFN width is NS
+// slabs (pool.F == NS * kSlab, launcher).
+template <int FMT, int RT, int NS>
+__global__ __launch_bounds__(kXThreads, 3) void down_x_kernel(PoolView pool, Items items,
+                                                              const uint16_t *__restrict__ h,
+                                                              float *__restrict__ d) {
+    extern __shared__ __align__(16) uint16_t hs[];   // [kTile][F + kXPad], then scales
+    constexpr int F = NS * kSlab, nslab = NS;
+    constexpr int NB0 = kXDownAhead / RT > 0 ? kXDownAhead / RT : 1;
+    constexpr int NB = NS < NB0 ? NS : NB0;
+    using QS = QScales<FMT, F>;
+    const int H = pool.H;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int c = lane & (kTile - 1), q = lane / kTile;
+    const int i0 = (blockIdx.x * kXWaves + wave) * RT * kTile;   // may pass H: such a wave only stages
+    const int gmax = min(items.n, pool.num_rows);
+    const uint16_t *hc = hs + c * (F + kXPad) + 32 * q;
+    // this wave's RT * 16 scale rows; lane l loads all of row l's bytes
+    static_assert(RT * kTile == kWave, "one scale row per lane");
+    uint8_t *qs = reinterpret_cast<uint8_t *>(hs + kTile * (F + kXPad)) + wave * RT * kTile * QS::PITCH;
+    const int srow = min(i0 + (lane / kTile) * kTile, H - kTile) + c;
+    GroupEntry cur;
+    cur.load(items, blockIdx.y, gmax);
+    for (int gi = blockIdx.y; gi < gmax && cur.valid(pool.num_rows); gi += gridDim.y) {
+        GroupEntry nxt;
+        nxt.load(items, gi + gridDim.y, gmax);
+        const int64_t row = cur.row;
+        const int32_t *list = items.grp_routes + cur.start;
+        for (int base = 0; base < cur.count; base += kTile) {
+            typename QS::template Chunk<QS::SB> sc2;
+            sc2.load(QS::row_ptr(pool, row, 1, srow));
+            ASlab<FMT> w2[NB][RT];
+            QRow r2[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) r2[rt].at(pool, FMT, row, 1, min(i0 + rt * kTile, H - kTile) + c, q);
+#pragma unroll
+            for (int bfr = 0; bfr < NB; ++bfr)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) w2[bfr][rt].codes = r2[rt].load(bfr);
+            const float glob = matrix_glob<FMT>(pool, row, 1);
+            const int n = min(base + (int)threadIdx.x / kTile, cur.count - 1);
+            const uint16_t *src = h + (int64_t)list[n] * F;
+            sc2.store(qs + lane * QS::PITCH);        // this wave's own rows: no barrier
+            __syncthreads();
+            stage_rows<F>(src, hs);
+            __syncthreads();
+            f32x4 acc[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s0 = 0; s0 < nslab; s0 += NB) {
+#pragma unroll
+                for (int bfr = 0; bfr < NB; ++bfr) {
+                    const int s = s0 + bfr;
+                    if (s < nslab) {
+                        u32x4 hb[4];
+                        const u32x4 *hp = reinterpret_cast<const u32x4 *>(hc + s * kSlab);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hb[i] = hp[i];
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) {
+                            u32x4 wa[4];
+                            w2[bfr][rt].sc = QS::read(qs + (rt * kTile + c) * QS::PITCH, s, q);
+                            w2[bfr][rt].expand(wa);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[rt] = mfma(wa[i], hb[i], acc[rt]);
+                        }
+                        if (s + NB < nslab) {
+#pragma unroll
+                            for (int rt = 0; rt < RT; ++rt) w2[bfr][rt].codes = r2[rt].load(s + NB);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (base + c < cur.count) {
+                const int64_t r = list[base + c];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const int ib = i0 + rt * kTile;
+                    if (ib < H) {
+                        float4 v;
+                        v.x = acc[rt][0] * glob;
+                        v.y = acc[rt][1] * glob;
+                        v.z = acc[rt][2] * glob;
+                        v.w = acc[rt][3] * glob;
+                        *reinterpret_cast<float4 *>(d + r * H + ib + 4 * q) = v;
+                    }
+                }
+            }
+        }
+        cur = nxt;
+    }
+}
+
 // ------------------------------------------------------------------ grouping
 
 // Routes grouped by pool row with a counting sort in LDS: per-row counts
@@ -500,6 +810,111 @@ hipError_t launch_down_shape(const PoolView &pool, const Items &items, int max_i
 }
 }  // namespace
 
+namespace {
+// The LDS-staged 4-bit kernels are built for hidden widths of 4 and 8
+// slabs (512, 1024) and FFN widths of 2, 4 and 8 slabs (256 .. 1024); other
+// widths take the kernels above.  Their LDS: 16 activation rows of the
+// width plus padding, and every wave's scale rows (at most 49 KB).
+template <int FMT, int COLS> constexpr size_t up_x_lds() {
+    using namespace mfma_detail;
+    return x_lds_bytes(COLS, 2 * kTile, QScales<FMT, COLS>::PITCH);
+}
+template <int FMT, int COLS> constexpr size_t down_x_lds() {
+    using namespace mfma_detail;
+    return x_lds_bytes(COLS, kWave, QScales<FMT, COLS>::PITCH);
+}
+constexpr int kXMaxLds = 64 * 1024;
+static_assert(up_x_lds<MOE_FMT_E2M1, 1024>() <= kXMaxLds && down_x_lds<MOE_FMT_E2M1, 1024>() <= kXMaxLds,
+              "staged kernels' LDS");
+
+bool x_up_fits(int fmt, int H) { return fmt != MOE_FMT_BF16 && (H == 512 || H == 1024); }
+bool x_down_fits(int fmt, int F) { return fmt != MOE_FMT_BF16 && (F == 256 || F == 512 || F == 1024); }
+
+// resident() for the LDS-staged kernels, one cache per instantiation.
+template <typename KERN>
+int resident_x(KERN kern, int *cache, size_t lds) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+    if (cache[dev] == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, mfma_detail::kXThreads, lds) !=
+                hipSuccess)
+            return 0;
+        cache[dev] = std::max(1, cus * per_cu);
+    }
+    return cache[dev];
+}
+
+template <int FMT, int NS>
+hipError_t launch_up_x(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
+                       uint16_t *h, hipStream_t s) {
+    using namespace mfma_detail;
+    static int res[16];
+    constexpr size_t lds = up_x_lds<FMT, NS * kSlab>();
+    const int cols = pool.F / (kXWaves * kTile);
+    const dim3 grid(cols, group_rows(max_items, cols, resident_x(up_x_kernel<FMT, NS>, res, lds)));
+    hipLaunchKernelGGL((up_x_kernel<FMT, NS>), grid, dim3(kXThreads), lds, s, pool, items, x, h);
+    return hipGetLastError();
+}
+
+template <int FMT, int NS>
+hipError_t launch_down_x(const PoolView &pool, const Items &items, int max_items, const uint16_t *h,
+                         float *d, hipStream_t s) {
+    using namespace mfma_detail;
+    constexpr int RT = 4;
+    static int res[16];
+    constexpr size_t lds = down_x_lds<FMT, NS * kSlab>();
+    const int rows = kXWaves * kTile * RT;
+    const int cols = (pool.H + rows - 1) / rows;
+    const dim3 grid(cols, group_rows(max_items, cols, resident_x(down_x_kernel<FMT, RT, NS>, res, lds)));
+    hipLaunchKernelGGL((down_x_kernel<FMT, RT, NS>), grid, dim3(kXThreads), lds, s, pool, items, h, d);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_up_x_width(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
+                             uint16_t *h, hipStream_t s) {
+    switch (pool.H) {
+    case 512: return launch_up_x<FMT, 4>(pool, items, max_items, x, h, s);
+    default: return launch_up_x<FMT, 8>(pool, items, max_items, x, h, s);
+    }
+}
+
+template <int FMT>
+hipError_t launch_down_x_width(const PoolView &pool, const Items &items, int max_items, const uint16_t *h,
+                               float *d, hipStream_t s) {
+    switch (pool.F) {
+    case 256: return launch_down_x<FMT, 2>(pool, items, max_items, h, d, s);
+    case 512: return launch_down_x<FMT, 4>(pool, items, max_items, h, d, s);
+    default: return launch_down_x<FMT, 8>(pool, items, max_items, h, d, s);
+    }
+}
+
+template <int FMT>
+hipError_t x_kernels_prepare_fmt(int lds) {
+    using namespace mfma_detail;
+    const void *kernels[] = {
+        reinterpret_cast<const void *>(&up_x_kernel<FMT, 4>),
+        reinterpret_cast<const void *>(&up_x_kernel<FMT, 8>),
+        reinterpret_cast<const void *>(&down_x_kernel<FMT, 4, 2>),
+        reinterpret_cast<const void *>(&down_x_kernel<FMT, 4, 4>),
+        reinterpret_cast<const void *>(&down_x_kernel<FMT, 4, 8>),
+    };
+    for (const void *k : kernels) {
+        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t x_kernels_prepare() {
+    const int lds = kXMaxLds;
+    hipError_t e = x_kernels_prepare_fmt<MOE_FMT_E2M1>(lds);
+    return e == hipSuccess ? x_kernels_prepare_fmt<MOE_FMT_MXFP4>(lds) : e;
+}
+}  // namespace
+
 hipError_t launch_up_mfma(const PoolView &pool, const Items &items, int max_items, const uint16_t *x,
                           uint16_t *h, hipStream_t s) {
     using namespace mfma_detail;
@@ -509,6 +924,9 @@ hipError_t launch_up_mfma(const PoolView &pool, const Items &items, int max_item
                            {{x, rec::kRead}, {pool.bank[0], rec::kRead, rec::items_part(items.route_plan, items.want_fresh)},
                             {items.idx, rec::kRead}, {items.n_groups, rec::kRead}, {items.grp_row, rec::kRead},
                             {h, rec::kWrite}});
+    if (x_up_fits(pool.fmt, pool.H))
+        return pool.fmt == MOE_FMT_MXFP4 ? launch_up_x_width<MOE_FMT_MXFP4>(pool, items, max_items, x, h, s)
+                                         : launch_up_x_width<MOE_FMT_E2M1>(pool, items, max_items, x, h, s);
     if (pool.fmt == MOE_FMT_MXFP4) return launch_up_shape<MOE_FMT_MXFP4, 2, 2>(pool, items, max_items, x, h, s);
     if (pool.fmt == MOE_FMT_E2M1) return launch_up_shape<MOE_FMT_E2M1, 1, 3>(pool, items, max_items, x, h, s);
     if (pool.F >= 1024) return launch_up_shape<MOE_FMT_BF16, 2, 2>(pool, items, max_items, x, h, s);
@@ -528,6 +946,9 @@ hipError_t launch_down_mfma(const PoolView &pool, const Items &items, int max_it
     // (152 VGPRs for the 4-bit formats against 221 with two) lets three
     // waves share a SIMD, which beats a second buffer (E2M1 wide step 3%,
     // bf16 and MXFP4 1%); other tile counts were slower.
+    if (x_down_fits(pool.fmt, pool.F))
+        return pool.fmt == MOE_FMT_MXFP4 ? launch_down_x_width<MOE_FMT_MXFP4>(pool, items, max_items, h, d, s)
+                                         : launch_down_x_width<MOE_FMT_E2M1>(pool, items, max_items, h, d, s);
     if (pool.fmt == MOE_FMT_MXFP4) return launch_down_shape<MOE_FMT_MXFP4, 4, 1>(pool, items, max_items, h, d, s);
     if (pool.fmt == MOE_FMT_E2M1) return launch_down_shape<MOE_FMT_E2M1, 4, 1>(pool, items, max_items, h, d, s);
     return launch_down_shape<MOE_FMT_BF16, 2, 1>(pool, items, max_items, h, d, s);
@@ -541,8 +962,9 @@ bool group_count_supported(int num_rows, int routes) {
 }
 
 hipError_t group_count_prepare() {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_detail::group_count_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, kGroupCountMaxLds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_detail::group_count_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGroupCountMaxLds);
+    return e == hipSuccess ? x_kernels_prepare() : e;
 }
 
 hipError_t launch_group_count(const int32_t *idx, int routes, int num_rows, int32_t *n_groups,
