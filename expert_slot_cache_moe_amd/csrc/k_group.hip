@@ -319,16 +319,18 @@ __global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, It
                     }
                 }
             }
-            // lane holds rows j0 + 16t + 4q + i (i < 4) of token column c
+            // lane holds rows j0 + 16t + 4q + i (i < 4) of token column c:
+            // four consecutive h elements, one 8-byte store
             if (base + c < cur.count) {
                 const int64_t r = list[base + c];
 #pragma unroll
-                for (int t = 0; t < UT; ++t)
+                for (int t = 0; t < UT; ++t) {
+                    uint32_t hv[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float g = ag[t][i] * glob, u = au[t][i] * glob;
-                        h[r * F + j0 + kTile * t + 4 * q + i] = f32_to_bf16(silu_mul(g, u));
-                    }
+                    for (int i = 0; i < 4; ++i) hv[i] = f32_to_bf16(silu_mul(ag[t][i] * glob, au[t][i] * glob));
+                    *reinterpret_cast<uint2 *>(h + r * F + j0 + kTile * t + 4 * q) =
+                        make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+                }
             }
         }
         cur = nxt;

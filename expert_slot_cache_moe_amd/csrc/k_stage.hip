@@ -71,6 +71,7 @@ struct Stage2Params {
 };
 
 constexpr int kGatherUnit = kThreads * 16 * 4;  // 16 KiB, as the gather kernel
+constexpr int kMaxStageRoutes = 64;             // top-k of a single-token step (kMaxTopK)
 constexpr int kUnitChunks = kGatherUnit / 16;   // 1024 chunks of 16 bytes
 
 // gate/up rows jj and F + jj of one expert with x -> h[j] (bf16), the
@@ -274,98 +275,157 @@ __device__ __forceinline__ void h_from_gu(const float *gu, int F, int li, int lp
     }
 }
 
-// One batch of up to kDownBatch routes of stage 2, loads first, math after:
-// the routes' slot ids and plan entries (scalar loads, issued together),
-// then every W2 row and activation chunk.  Routes that contribute nothing
-// read row 0 and route 0 as in-range stand-ins, so every load is
-// unconditional and none waits for another.
-template <int FMT, int LPRF, int NCHF>
-__device__ __forceinline__ void stage2_batch(const Stage2Params &p, int k0, int ii, int li, float &acc) {
+// Stage 2 of bf16 rows gives each wave its own row group and all of the
+// step's routes (kDownBatch at a time, accumulated in registers).  4-bit
+// rows are a quarter of the bytes and their wave's dequantisation needs
+// more registers, so there the four waves of a workgroup share one row
+// group and split the routes, two at a time, with the per-route values
+// meeting in LDS (measured on MI355X at the 40 x 256 decode: the 4-bit
+// decode 19.8K -> 21.2K layer-steps/s; the same split made the bf16
+// single-token GEMV 5% slower).
+template <int FMT> struct Stage2Split {
+    static constexpr int ways = FMT == MOE_FMT_BF16 ? 1 : kWavesPerBlock;   // waves per row group
+    static constexpr int batch = FMT == MOE_FMT_BF16 ? kDownBatch : 2;      // routes in flight per wave
+};
+
+// One batch of up to B of a wave's routes [k0, khi) of stage 2, loads
+// first, math after: the routes' slot ids and plan entries (scalar loads,
+// issued together), then every W2 row and activation chunk.  Routes that
+// contribute nothing read row 0 and the last route as in-range stand-ins,
+// so every load is unconditional and none waits for another.  Each route's
+// down value of the lane group's row is accumulated (acc = fma(w, v, acc),
+// ascending k), or with TO_LDS stored to vals[k][sub] and whether it
+// counts to ok[k].
+template <int FMT, int LPRF, int NCHF, int B, bool TO_LDS>
+__device__ __forceinline__ void stage2_batch(const Stage2Params &p, int k0, int khi, int ii, int li, int sub,
+                                             float &acc, float (*vals)[kWave / LPRF], int *ok) {
     const int F = p.slots.F;
-    int sl[kDownBatch], pe[kDownBatch];
+    int sl[B], pe[B];
 #pragma unroll
-    for (int q = 0; q < kDownBatch; ++q) {
-        const int kk = min(k0 + q, p.K - 1);
+    for (int q = 0; q < B; ++q) {
+        const int kk = min(k0 + q, khi - 1);
         sl[q] = p.idx[kk];
         pe[q] = p.route_plan ? p.route_plan[kk] : -1;
     }
     __builtin_amdgcn_sched_barrier(0);
-    WSeg<FMT, NCHF> w2[kDownBatch];
-    XSeg<FMT, NCHF> hs[kDownBatch];
-    int rows[kDownBatch];
-    float g13[kDownBatch], g2[kDownBatch];   // global scales (1 unless E2M1)
+    WSeg<FMT, NCHF> w2[B];
+    XSeg<FMT, NCHF> hs[B];
+    int rows[B];
+    float g13[B], g2[B];   // global scales (1 unless E2M1)
 #pragma unroll
-    for (int q = 0; q < kDownBatch; ++q) {
+    for (int q = 0; q < B; ++q) {
         const int k = k0 + q;
-        const bool ok = k < p.K && sl[q] >= 0 && sl[q] < p.slots.num_rows;
-        rows[q] = ok ? sl[q] : -1;
-        const int r = ok ? sl[q] : 0;
+        const bool use = k < khi && sl[q] >= 0 && sl[q] < p.slots.num_rows;
+        rows[q] = use ? sl[q] : -1;
+        const int r = use ? sl[q] : 0;
         w2[q].load(p.slots, r, 1, ii, li, LPRF);
-        hs[q].load(p.h + (int64_t)min(k, p.K - 1) * F, li, LPRF);
+        hs[q].load(p.h + (int64_t)min(k, khi - 1) * F, li, LPRF);
         g13[q] = w2[q].glob(p.slots, r, 0);
         g2[q] = w2[q].glob(p.slots, r, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
+    const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int q = 0; q < kDownBatch; ++q) {
+    for (int q = 0; q < B; ++q) {
+        const int k = k0 + q;
+        if (k >= khi) continue;
+        if constexpr (TO_LDS) {
+            if (lane == 0) ok[k] = rows[q] >= 0;
+        }
         if (rows[q] < 0) continue;
         if (pe[q] >= 0) h_from_gu<FMT, NCHF>(p.gu + (int64_t)pe[q] * 2 * F, F, li, LPRF, g13[q], hs[q]);
         const float v = group_total<LPRF>(seg_dot(w2[q], hs[q])) * g2[q];
-        acc = fmaf(p.w[k0 + q], v, acc);
+        if constexpr (TO_LDS) {
+            if (li == LPRF - 1) vals[k][sub] = v;
+        } else {
+            acc = fmaf(p.w[k], v, acc);
+        }
     }
 }
 
 // Stage 2.  The routed W2 rows take LPRF x NCHF chunks, the shared
 // expert's bf16 rows SLPRF x SNCHF (SLPRF >= LPRF: a bf16 row has four
-// times the chunks of a 4-bit one).  A wave owns RPW = 64 / LPRF output
-// rows; the shared rows of those are taken SLPRF / LPRF passes of 64 / SLPRF
-// rows each, and each value is moved to the lane group of its row.
+// times the chunks of a 4-bit one).  A row group is RPW = 64 / LPRF output
+// rows (one lane group per row) and WAYS waves (Stage2Split): wave way w
+// takes routes [w KW, (w + 1) KW), KW = ceil(K / WAYS), and the shared
+// expert's passes of 64 / SLPRF rows numbered WAYS - 1 - w, 2 WAYS - 1 -
+// w, ...  With one way the wave sums its routes itself; with several they
+// meet in LDS and the row group's first wave sums them in ascending k with
+// the same fma chain.  Either way the gated shared term is added last.
 template <int FMT, int LPRF, int NCHF, int SLPRF, int SNCHF>
 __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
     constexpr int RPW = kWave / LPRF;
-    constexpr int IT = kWavesPerBlock * RPW;
     constexpr int SRPW = kWave / SLPRF;
     constexpr int PASSES = SLPRF / LPRF;
+    constexpr int WAYS = Stage2Split<FMT>::ways, BATCH = Stage2Split<FMT>::batch;
+    constexpr int GROUPS = kWavesPerBlock / WAYS;       // row groups per workgroup
+    constexpr bool SPLIT = WAYS > 1;
     static_assert(SLPRF >= LPRF && PASSES * SRPW == RPW, "shared and routed row mapping");
+    __shared__ float vals[SPLIT ? GROUPS * kMaxStageRoutes : 1][RPW];
+    __shared__ int ok[SPLIT ? GROUPS * kMaxStageRoutes : 1];
+    __shared__ float svals[SPLIT ? GROUPS : 1][RPW];
     const int H = p.slots.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int grp = wave / WAYS, way = wave % WAYS;
     const int sub = lane / LPRF, li = lane % LPRF;
-    const int row0 = blockIdx.x * IT + wave * RPW;
+    const int row0 = (blockIdx.x * GROUPS + grp) * RPW;
     const int i = row0 + sub;
     const bool iok = i < H;
     const int ii = iok ? i : H - 1;
+    const int kw = (p.K + WAYS - 1) / WAYS;
+    const int klo = way * kw, khi = min(p.K, klo + kw);
+    float(*gvals)[RPW] = vals + (SPLIT ? grp * kMaxStageRoutes : 0);
+    int *gok = ok + (SPLIT ? grp * kMaxStageRoutes : 0);
 
-    // the shared expert's rows, loaded with the first batch of routes
-    WSeg<MOE_FMT_BF16, SNCHF> w2s[PASSES];
+    // this wave's passes of the shared expert's rows, loaded with its
+    // first batch of routes
+    constexpr int MYP = (PASSES + WAYS - 1) / WAYS;
+    WSeg<MOE_FMT_BF16, SNCHF> w2s[MYP];
     XSeg<MOE_FMT_BF16, SNCHF> hss;
     const int ssub = lane / SLPRF, sli = lane % SLPRF;
+    const int p0 = WAYS - 1 - way;   // first pass of this wave
     if (p.has_shared) {
 #pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp)
-            w2s[pp].load(p.shared, 0, 1, min(row0 + pp * SRPW + ssub, H - 1), sli, SLPRF);
-        hss.load(p.hs, sli, SLPRF);
+        for (int m = 0; m < MYP; ++m) {
+            const int pp = p0 + m * WAYS;
+            if (pp < PASSES) w2s[m].load(p.shared, 0, 1, min(row0 + pp * SRPW + ssub, H - 1), sli, SLPRF);
+        }
+        if (p0 < PASSES) hss.load(p.hs, sli, SLPRF);
     }
     float acc = 0.f;
-    for (int k0 = 0; k0 < p.K; k0 += kDownBatch) stage2_batch<FMT, LPRF, NCHF>(p, k0, ii, li, acc);
-    float res = acc;
-    if (p.addend) res = acc + p.addend[ii];
+    for (int k0 = klo; k0 < khi; k0 += BATCH)
+        stage2_batch<FMT, LPRF, NCHF, BATCH, SPLIT>(p, k0, khi, ii, li, sub, acc, gvals, gok);
+    float vs = 0.f;
     if (p.has_shared) {
-        float vs = 0.f;
 #pragma unroll
-        for (int pp = 0; pp < PASSES; ++pp) {
-            const float v = group_total<SLPRF>(seg_dot(w2s[pp], hss));
-            if constexpr (PASSES == 1) {
-                vs = v;          // the same lane group holds the row
-            } else {
-                // row sub lives in pass sub / SRPW, lane group sub % SRPW
-                const float moved = __shfl(v, (sub % SRPW) * SLPRF + SLPRF - 1, kWave);
-                if (sub / SRPW == pp) vs = moved;
+        for (int m = 0; m < MYP; ++m) {
+            const int pp = p0 + m * WAYS;
+            if (pp < PASSES) {
+                const float v = group_total<SLPRF>(seg_dot(w2s[m], hss));
+                if constexpr (SPLIT) {
+                    if (sli == SLPRF - 1) svals[grp][pp * SRPW + ssub] = v;
+                } else if constexpr (PASSES == 1) {
+                    vs = v;          // the same lane group holds the row
+                } else {
+                    // row sub lives in pass sub / SRPW, lane group sub % SRPW
+                    const float moved = __shfl(v, (sub % SRPW) * SLPRF + SLPRF - 1, kWave);
+                    if (sub / SRPW == pp) vs = moved;
+                }
             }
         }
-        // gamma * vs is rounded on its own (the library builds without fp
-        // contraction), as the serial path rounds it when storing it
-        res = acc + p.gamma[0] * vs;
     }
+    if constexpr (SPLIT) {
+        __syncthreads();
+        if (way != 0) return;
+        for (int k = 0; k < p.K; ++k)
+            if (gok[k]) acc = fmaf(p.w[k], gvals[k][sub], acc);
+        if (p.has_shared) vs = svals[grp][sub];
+    }
+    float res = acc;
+    if (p.addend) res = acc + p.addend[ii];
+    // gamma * vs is rounded on its own (the library builds without fp
+    // contraction), as the serial path rounds it when storing it
+    if (p.has_shared) res = acc + p.gamma[0] * vs;
     if (iok && li == LPRF - 1) p.out[i] = f32_to_bf16(res);
 }
 
@@ -373,7 +433,7 @@ template <int FMT, int LPRH, int NCHH, int SLPRH, int SNCHH, int LPRF, int NCHF,
 hipError_t launch_shape(const Stage1Params &a, const Stage2Params &b, int which, hipStream_t s) {
     constexpr int JT = kWavesPerBlock * (kWave / LPRH);
     constexpr int SJT = kWavesPerBlock * (kWave / SLPRH);
-    constexpr int IT = kWavesPerBlock * (kWave / LPRF);
+    constexpr int IT = kWavesPerBlock / Stage2Split<FMT>::ways * (kWave / LPRF);   // stage 2 rows per workgroup
     Stage1Params p1 = a;
     p1.a_tiles = (p1.slots.F + JT - 1) / JT;
     p1.s_tiles = p1.s_tiles ? (p1.slots.F + SJT - 1) / SJT : 0;
@@ -425,6 +485,7 @@ hipError_t launch_stages(const GatherParams &g, int gather_blocks, float *gu, co
                          const uint16_t *gate_vec, float *gamma, const float *addend, uint16_t *out,
                          int which, hipStream_t s) {
     using namespace stage_detail;
+    if (K > kMaxStageRoutes) return hipErrorInvalidValue;
     Stage1Params a{};
     a.g = g;
     a.gather_blocks = gather_blocks;
