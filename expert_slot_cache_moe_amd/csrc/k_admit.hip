@@ -280,14 +280,14 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 // value, then id among the lanes holding that value), and only the lane
 // that held it looks for its next best.
 template <int NC>
-__device__ __forceinline__ void wave_topk_nc(const float *__restrict__ row, const float *pre, int E,
-                                             int K, int32_t *ids_lds, float *w_out) {
+__device__ __forceinline__ void wave_topk_nc(const float *__restrict__ row, int E, int K, int32_t *ids_lds,
+                                             float *w_out) {
     const int lane = threadIdx.x & (kWave - 1);
-    // the row's logits, loaded by the caller (pre) or here, all loads in
-    // flight together (clamped in-range indices)
+    // the row's logits, all loads in flight together (clamped in-range
+    // indices)
     float lv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) lv[c] = pre ? pre[c] : row[min(lane + kWave * c, E - 1)];
+    for (int c = 0; c < NC; ++c) lv[c] = row[min(lane + kWave * c, E - 1)];
     uint64_t keys[NC];
     uint64_t lb = 0ull;
 #pragma unroll
@@ -322,14 +322,14 @@ __device__ __forceinline__ void wave_topk_nc(const float *__restrict__ row, cons
     }
 }
 
-__device__ __forceinline__ void wave_topk(const float *__restrict__ row, const float *pre, int E, int K,
-                                          int32_t *ids_lds, float *w_out) {
+__device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int K, int32_t *ids_lds,
+                                          float *w_out) {
     const int nc = (E + kWave - 1) / kWave;
-    if (nc <= 1) wave_topk_nc<1>(row, pre, E, K, ids_lds, w_out);
-    else if (nc <= 2) wave_topk_nc<2>(row, pre, E, K, ids_lds, w_out);
-    else if (nc <= 4) wave_topk_nc<4>(row, pre, E, K, ids_lds, w_out);
-    else if (nc <= 8) wave_topk_nc<8>(row, pre, E, K, ids_lds, w_out);
-    else wave_topk_nc<16>(row, pre, E, K, ids_lds, w_out);
+    if (nc <= 1) wave_topk_nc<1>(row, E, K, ids_lds, w_out);
+    else if (nc <= 2) wave_topk_nc<2>(row, E, K, ids_lds, w_out);
+    else if (nc <= 4) wave_topk_nc<4>(row, E, K, ids_lds, w_out);
+    else if (nc <= 8) wave_topk_nc<8>(row, E, K, ids_lds, w_out);
+    else wave_topk_nc<16>(row, E, K, ids_lds, w_out);
 }
 
 // Register-resident admission.  p.order holds (slot, owner) pairs here, so
@@ -338,6 +338,17 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ row, const f
 // waits for a wave's outstanding memory operations, so stores issued
 // between barriers would each cost a memory round trip.
 constexpr int kNarrowWindow = 4 * kWave;
+
+// The admission's statistics are the first five (calls, met, missed,
+// overflow, invalid); stat_delta gives statistic k's increment of a step.
+constexpr int kAdmitStats = 5;
+static_assert(MOE_STAT_CALLS == 0 && MOE_STAT_MET == 1 && MOE_STAT_MISSED == 2 && MOE_STAT_OVERFLOW == 3 &&
+                  MOE_STAT_INVALID == 4,
+              "admission statistics are indices 0-4");
+__device__ __forceinline__ int64_t stat_delta(int k, int met, int missed, int overflow, int invalid) {
+    return k == MOE_STAT_CALLS ? 1 : k == MOE_STAT_MET ? met : k == MOE_STAT_MISSED ? missed
+                                                     : k == MOE_STAT_OVERFLOW ? overflow : invalid;
+}
 
 // Orders LDS accesses of one wave: a compiler fence (a wave's LDS
 // instructions execute in issue order).
@@ -363,7 +374,7 @@ struct lds_view {
 //   (slots used so far this step) + (misses) <= 2 * 64 + 64
 // entries of the order, inside the 256-entry window the wave holds.
 __device__ __forceinline__ void narrow_step(const AdmitParams &p, lds_view v, const int (&wslot)[4],
-                                         const int (&wown)[4], uint32_t now, const int64_t (&st0)[5]) {
+                                         const int (&wown)[4], uint32_t now, int64_t st_lane) {
     const int lane = threadIdx.x;
     const int E = p.E, R = p.R;
     const int64_t lbase = (int64_t)p.layer * E;
@@ -486,13 +497,10 @@ __device__ __forceinline__ void narrow_step(const AdmitParams &p, lds_view v, co
         p.freq[lbase + e] = v.freq_l[e] + v.cnt[e];
         p.dlast[lbase + e] = now;
     }
+    if (lane < kAdmitStats)
+        p.stats[(int64_t)p.layer * MOE_NUM_STATS + lane] =
+            st_lane + stat_delta(lane, nD, nmissed, noverflow, ninvalid);
     if (lane == 0) {
-        int64_t *st = p.stats + (int64_t)p.layer * MOE_NUM_STATS;
-        st[MOE_STAT_CALLS] = st0[MOE_STAT_CALLS] + 1;
-        st[MOE_STAT_MET] = st0[MOE_STAT_MET] + nD;
-        st[MOE_STAT_MISSED] = st0[MOE_STAT_MISSED] + nmissed;
-        st[MOE_STAT_OVERFLOW] = st0[MOE_STAT_OVERFLOW] + noverflow;
-        st[MOE_STAT_INVALID] = st0[MOE_STAT_INVALID] + ninvalid;
         p.clock[0] = now;
         p.clock[1] = now;
         p.n_miss[0] = nplan;
@@ -523,76 +531,60 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     const int64_t lbase = (int64_t)p.layer * E;
 
     // Every load of the prologue is issued before any result is used: the
-    // first logits row of each wave (fused top-k), the LRU order, the slot
-    // map and histogram rows, the statistics and the clock.  This kernel is
-    // the only writer of the layer's statistics and histogram during the
-    // step, so they are updated with plain stores of the values read here.
-    float lgv[kTopkMaxPerLane];
-    const bool pre_row = p.logits != nullptr && wave < p.T;
-    if (pre_row) {
-        const float *row = p.logits + (int64_t)wave * E;
-        const int lane = tid & (kWave - 1);
-#pragma unroll
-        for (int c = 0; c < kTopkMaxPerLane; ++c)
-            if (c * kWave < E) lgv[c] = row[min(lane + kWave * c, E - 1)];
-    }
-    int64_t st0[5];
-    if (tid == 0) {
-        const int64_t *st = p.stats + (int64_t)p.layer * MOE_NUM_STATS;
-#pragma unroll
-        for (int k = 0; k < 5; ++k) st0[k] = st[k];
-    }
+    // clock, the statistics, the LRU order (and, for a narrow step, its
+    // head again as wave 0's victim window), the slot map and histogram
+    // rows, and last the logits of the fused top-k, which runs as soon as
+    // they land, while the rows still wait for LDS.  Measured on MI355X at
+    // the 40 x 256 decode: with the clock read after the rows reached LDS
+    // (a second round trip) and the preloaded logits kept in scratch (one
+    // round trip per 64 of them), prologue and top-k took 6.7 us.  This
+    // kernel is the only writer of the layer's statistics and histogram
+    // during the step, so they are updated with plain stores of the values
+    // read here.
+    // The clock and the admission statistics (one per lane of the first
+    // threads) are read with vector loads: as scalar loads they shared a
+    // counter with the kernel arguments read later, and waiting for those
+    // waited for them.  mbcnt_lo(0, 0) is 0 in every lane, but lane-varying
+    // to the compiler.
+    const uint32_t clk = p.clock[__builtin_amdgcn_mbcnt_lo(0u, 0u)];
+    const int64_t st_lane = tid < kAdmitStats ? p.stats[(int64_t)p.layer * MOE_NUM_STATS + tid] : 0;
 
     // This thread's run of the LRU order: (slot, owner) pairs.  The order
     // buffer holds kThreads * P pairs (admit_order_bytes), so the loads are
     // unconditional 16-byte ones, all in flight together; positions past S
-    // are masked afterwards.
-    int ord[P], owner[P];
+    // are masked once the top-k is done.
+    int4 ov[P / 2 > 0 ? P / 2 : 1];
+    int2 ov1;
     if constexpr (P == 1) {
-        const int2 v = reinterpret_cast<const int2 *>(p.order)[tid];
-        ord[0] = v.x;
-        owner[0] = v.y;
+        ov1 = reinterpret_cast<const int2 *>(p.order)[tid];
     } else {
         const int4 *q4 = reinterpret_cast<const int4 *>(p.order) + tid * (P / 2);
-        int4 v[P / 2];
 #pragma unroll
-        for (int q = 0; q < P / 2; ++q) v[q] = q4[q];
-#pragma unroll
-        for (int q = 0; q < P / 2; ++q) {
-            ord[2 * q] = v[q].x;
-            owner[2 * q] = v[q].y;
-            ord[2 * q + 1] = v[q].z;
-            owner[2 * q + 1] = v[q].w;
-        }
+        for (int q = 0; q < P / 2; ++q) ov[q] = q4[q];
     }
-#pragma unroll
-    for (int q = 0; q < P; ++q)
-        if (tid * P + q >= S) ord[q] = owner[q] = -1;
     // A narrow step (at most one route per lane of wave 0) is admitted by
     // wave 0 alone; its victims come from the head of the LRU order, of
     // which the wave holds the first kNarrowWindow entries (four per lane).
     const bool narrow = R <= kWave;
-    int wslot[4], wown[4];
-    if (narrow && wave == 0) {
+    const bool window = narrow && wave == 0;
+    int4 wa, wb;   // read only where window holds (selected after the top-k, so no early wait)
+    if (window) {
         const int4 *q4 = reinterpret_cast<const int4 *>(p.order) + tid * 2;
-        const int4 a = q4[0], b = q4[1];
-        wslot[0] = a.x; wown[0] = a.y; wslot[1] = a.z; wown[1] = a.w;
-        wslot[2] = b.x; wown[2] = b.y; wslot[3] = b.z; wown[3] = b.w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tid * 4 + i >= S) wslot[i] = wown[i] = -1;
+        wa = q4[0];
+        wb = q4[1];
     }
-    // The layer's slot map row into LDS: loads of a batch issued together
-    // (clamped in-range indices), stores after.
-    for (int e0 = 0; e0 < E; e0 += 4 * kThreads) {
-        int32_t v[4];
-        int64_t fv[4];
+    // The layer's slot map and histogram rows into LDS, 4 * kThreads
+    // entries a batch (clamped in-range indices): the first batch's loads
+    // are issued here, their LDS stores follow the top-k.
+    auto load_rows = [&](int e0, int32_t (&v)[4], int64_t (&fv)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t e = lbase + min(e0 + tid + j * kThreads, E - 1);
             v[j] = p.res[e];
             fv[j] = p.freq[e];
         }
+    };
+    auto store_rows = [&](int e0, const int32_t (&v)[4], const int64_t (&fv)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = e0 + tid + j * kThreads;
@@ -603,25 +595,57 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
                 filled[e] = 0;
             }
         }
-    }
-    for (int i = tid; i < S; i += kThreads) touched[i] = 0;
-    if (tid < 16) misc[tid] = 0;
-    const uint32_t now = p.clock[0] + 1u;
+    };
+    int32_t rv[4];
+    int64_t rfv[4];
+    load_rows(0, rv, rfv);
 
     if (p.logits != nullptr) {
         for (int t = wave; t < p.T; t += kWaves)
-            wave_topk(p.logits + (int64_t)t * E, t == wave ? lgv : nullptr, E, p.K, ids_l + t * p.K,
-                      p.w_out + (int64_t)t * p.K);
+            wave_topk(p.logits + (int64_t)t * E, E, p.K, ids_l + t * p.K, p.w_out + (int64_t)t * p.K);
     } else {
         for (int i = tid; i < R; i += kThreads) ids_l[i] = p.ids[i];
     }
+
+    int ord[P], owner[P];
+    if constexpr (P == 1) {
+        ord[0] = ov1.x;
+        owner[0] = ov1.y;
+    } else {
+#pragma unroll
+        for (int q = 0; q < P / 2; ++q) {
+            ord[2 * q] = ov[q].x;
+            owner[2 * q] = ov[q].y;
+            ord[2 * q + 1] = ov[q].z;
+            owner[2 * q + 1] = ov[q].w;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+        if (tid * P + q >= S) ord[q] = owner[q] = -1;
+    int wslot[4] = {-1, -1, -1, -1}, wown[4] = {-1, -1, -1, -1};
+    if (window) {
+        wslot[0] = wa.x; wown[0] = wa.y; wslot[1] = wa.z; wown[1] = wa.w;
+        wslot[2] = wb.x; wown[2] = wb.y; wslot[3] = wb.z; wown[3] = wb.w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (tid * 4 + i >= S) wslot[i] = wown[i] = -1;
+    }
+    store_rows(0, rv, rfv);
+    for (int e0 = 4 * kThreads; e0 < E; e0 += 4 * kThreads) {
+        load_rows(e0, rv, rfv);
+        store_rows(e0, rv, rfv);
+    }
+    for (int i = tid; i < S; i += kThreads) touched[i] = 0;
+    if (tid < 16) misc[tid] = 0;
+    const uint32_t now = clk + 1u;
     __syncthreads();
 
     int nD;
     if (narrow) {
         if (wave == 0) narrow_step(p, lds_view{freq_l, cnt, resl, dlist, missl, pslot, pold, pexp, ids_l,
                                                 slot_e, touched, filled, misc},
-                                   wslot, wown, now, st0);
+                                   wslot, wown, now, st_lane);
         __syncthreads();
         nD = misc[1];
     } else {
@@ -760,13 +784,10 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
         p.freq[lbase + e] = freq_l[e] + cnt[e];
         p.dlast[lbase + e] = now;
     }
+    if (tid < kAdmitStats)
+        p.stats[(int64_t)p.layer * MOE_NUM_STATS + tid] =
+            st_lane + stat_delta(tid, nD, nmissed, noverflow, misc[0]);
     if (tid == 0) {
-        int64_t *st = p.stats + (int64_t)p.layer * MOE_NUM_STATS;
-        st[MOE_STAT_CALLS] = st0[MOE_STAT_CALLS] + 1;
-        st[MOE_STAT_MET] = st0[MOE_STAT_MET] + nD;
-        st[MOE_STAT_MISSED] = st0[MOE_STAT_MISSED] + nmissed;
-        st[MOE_STAT_OVERFLOW] = st0[MOE_STAT_OVERFLOW] + noverflow;
-        st[MOE_STAT_INVALID] = st0[MOE_STAT_INVALID] + misc[0];
         p.clock[0] = now;
         p.clock[1] = now;
         p.n_miss[0] = nplan;
