@@ -778,8 +778,8 @@ def host_description() -> dict:
 
 DECODE_KERNELS = ("admit_fast_kernel", "admit_kernel", "topk_kernel", "stage1_kernel", "stage2_kernel",
                   "gather_kernel", "up_kernel", "down_d_kernel", "down_fused_kernel",
-                  "group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "combine_kernel",
-                  "prefetch_kernel")
+                  "group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "up_x_kernel",
+                  "down_x_kernel", "combine_kernel", "prefetch_kernel")
 
 
 def _short(name: str) -> str:
@@ -835,12 +835,14 @@ def _wide_calls(log, moe):
     L, W_, K_ = log["layers"], log.get("warm_tokens", log["warmup"]), log["steps"]
     pos = 3 * (W_ + 2 * K_) * L + 2 * log["gemv_calls"]
     out = []
-    kinds = ["group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "combine_kernel"]
+    # grouping, gate/up (bf16, or the LDS-staged 4-bit kernel), down, combine
+    kinds = [("group_count_kernel",), ("up_mfma_kernel", "up_x_kernel"), ("down_mfma_kernel", "down_x_kernel"),
+             ("combine_kernel",)]
     for wcfg in log.get("wide") or []:
         seq = moe[pos:pos + 4 * wcfg["calls"]]
         pos += 4 * wcfg["calls"]
         calls = [seq[i:i + 4] for i in range(0, len(seq), 4)]
-        if len(calls) != wcfg["calls"] or any([d["k"] for d in c] != kinds for c in calls):
+        if len(calls) != wcfg["calls"] or any(not all(d["k"] in ks for d, ks in zip(c, kinds)) for c in calls):
             raise SystemExit("trace does not hold the wide-step launches the run made")
         out.append((wcfg["workload"], calls[-wcfg["timed_calls"]:]))
     return out
@@ -909,7 +911,8 @@ def summarize_trace(csv_path, log_path):
     for name, wc in _wide_calls(log, [d for d in disp if d["k"]]):
         tot = np.asarray([sum(d["us"] for d in c) for c in wc])
         parts = " + ".join(f"{np.mean([c[i]['us'] for c in wc]):.2f}" for i in range(4))
-        p(f"| routed GEMV, {name}: group_count + up_mfma + down_mfma + combine ({parts}) | {len(wc)} | "
+        names = " + ".join(d["k"].replace("_kernel", "") for d in wc[0])
+        p(f"| routed GEMV, {name}: {names} ({parts}) | {len(wc)} | "
           f"{tot.mean():.2f} | {wl.get(name, {}).get('us_per_call')} |")
     p("")
     pfd = [d for d in disp if d["k"] == "prefetch_kernel"]
@@ -1083,7 +1086,7 @@ def summarize_counters(csv_paths):
     rows = []
     for key in sorted(acc):
         c = {n: np.mean(v) for n, v in acc[key].items()}
-        if "mfma" not in key or any(n not in c for n in need) or c["SQ_WAVES"] <= 0:
+        if ("mfma" not in key and "_x_kernel" not in key) or any(n not in c for n in need) or c["SQ_WAVES"] <= 0:
             continue
         rows.append(f"#   {key}: {c['SQ_WAVES']:.0f} waves a dispatch; stalled on outstanding loads "
                     f"{100 * c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.0f}% of wave cycles, VALU issuing "
