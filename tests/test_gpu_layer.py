@@ -92,6 +92,8 @@ def _routed_gpu(pool, x, idx, w, H, addend=None):
     (2, 2048, 512, 12, 1, 8),       # mxfp4, shared-expert decode shape
     (2, 1024, 256, 40, 33, 2),      # mxfp4, grouped path (matrix cores)
     (2, 64, 64, 6, 3, 3),           # mxfp4, smallest rows (vector path)
+    (1, 512, 512, 6, 40, 2),        # e2m1 grouped at H 512 / F 512 (LDS-staged kernels), several batches a group
+    (2, 512, 512, 6, 40, 2),        # the same as mxfp4
 ])
 def test_routed_matches_oracle(fmt, H, F, rows, T, K):
     g = W.rng(4, "routed", fmt, H, T)
