@@ -63,81 +63,143 @@ __global__ __launch_bounds__(kThreads) void prefetch_kernel(PrefetchParams p) {
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int64_t lbase = (int64_t)p.layer * E;
-    const uint32_t now = p.clock[0] + 1u;
-    const uint32_t latest_demand = p.clock[1];
+
+    // ---- every load the call can issue before any result is used, in one
+    // round trip (then one more for what depends on the order's entries):
+    // the clock (vector loads: mbcnt_lo(0, 0) is 0 but lane-varying to the
+    // compiler, so they do not share a counter with later kernel-argument
+    // loads), the first predictions, the layer's slot-map entries and demand
+    // heat, this thread's entries of the LRU order, and for its first entry
+    // the slot's stamp and the owner's heat.  Measured on MI355X in the
+    // decode graph, the same work with each load issued where it is used
+    // took about seven dependent round trips (11 us a call).
+    const int z = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
+    const uint32_t now = p.clock[z] + 1u;
+    const uint32_t latest_demand = p.clock[z + 1];
+    const int id0 = tid < p.n ? p.ids[tid] : -1;
+    const int e0 = min(tid, E - 1);
+    const int res0 = p.res[lbase + e0];
+    const int64_t freq0 = p.freq[lbase + e0];
+    const uint32_t dlast0 = p.dlast[lbase + e0];
+    constexpr int kHeld = 4;                 // order entries a thread holds (S <= 4096)
+    // (slot, owner) pairs or bare slots: the same two dword loads either
+    // way (a bare slot read twice), so no branch sits between the loads
+    int ord[kHeld], oown[kHeld];
+    const int step = p.pairs ? 2 : 1;
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k) {
+        const int i = min(tid + k * kThreads, S - 1);
+        ord[k] = p.order[(int64_t)i * step];
+        oown[k] = p.order[(int64_t)i * step + (step - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < kHeld; ++k)
+        if (!p.pairs) oown[k] = -1;
+    const int s00 = ord[0] >= 0 && ord[0] < S ? ord[0] : 0;
+    // the first entry's owner and its heat, then its slot's stamp: with
+    // pairs the owner came with the order (so both are a second round
+    // trip), else it comes from the owner map first
+    int o00;
+    int64_t ofreq0;
+    uint32_t odlast0, stamp0;
+    if (p.pairs) {
+        o00 = oown[0];
+        const int oi = o00 >= 0 ? o00 : 0;
+        ofreq0 = p.freq[oi];
+        odlast0 = p.dlast[oi];
+        stamp0 = p.stamp[s00];
+    } else {
+        stamp0 = p.stamp[s00];
+        o00 = p.own[s00];
+        const int oi = o00 >= 0 ? o00 : 0;
+        ofreq0 = p.freq[oi];
+        odlast0 = p.dlast[oi];
+    }
+    // entry i of the order (held for i < kHeld * kThreads)
+    auto order_at = [&](int base, int i, int &sl, int &ow) {
+        const int k = base / kThreads;
+        if (k < kHeld) {
+            sl = k == 0 ? ord[0] : k == 1 ? ord[1] : k == 2 ? ord[2] : ord[3];
+            ow = k == 0 ? oown[0] : k == 1 ? oown[1] : k == 2 ? oown[2] : oown[3];
+        } else if (p.pairs) {
+            const int2 v = reinterpret_cast<const int2 *>(p.order)[i];
+            sl = v.x;
+            ow = v.y;
+        } else {
+            sl = p.order[i];
+            ow = -1;
+        }
+    };
 
     for (int e = tid; e < E; e += kThreads) want[e] = 0;
-    for (int s = tid; s < S; s += kThreads) touched[s] = 0;
+    for (int sl = tid; sl < S; sl += kThreads) touched[sl] = 0;
     __syncthreads();
     for (int i = tid; i < p.n; i += kThreads) {
-        const int e = p.ids[i];
+        const int e = i == tid ? id0 : p.ids[i];
         if (e >= 0 && e < E) want[e] = 1;
     }
     __syncthreads();
 
-    // Hits (used now) and missing predictions, both ascending.
+    // Hits (used now) and missing predictions, both ascending, with the
+    // missing predictions' scores.
     int nh = 0, nm = 0;
     for (int base = 0; base < E; base += kThreads) {
         const int e = base + tid;
         const bool w = e < E && want[e] != 0;
-        const int s = w ? p.res[lbase + e] : -1;
-        const bool hit = w && s >= 0, miss = w && s < 0;
+        const int sl = w ? (base == 0 ? res0 : p.res[lbase + e]) : -1;
+        const bool hit = w && sl >= 0, miss = w && sl < 0;
         int th, tm;
         const int rh = block_scan(hit, wsum, th);
         const int rm = block_scan(miss, wsum, tm);
         if (hit) {
-            touched[s] = 1;
-            tslot[nh + rh] = s;
+            touched[sl] = 1;
+            tslot[nh + rh] = sl;
             town[nh + rh] = (int32_t)(lbase + e);
         }
-        if (miss) missl[nm + rm] = e;
+        if (miss) {
+            missl[nm + rm] = e;
+            score_p[nm + rm] = base == 0 ? lfru_score(freq0, dlast0, now)
+                                         : lfru_score(p.freq[lbase + e], p.dlast[lbase + e], now);
+        }
         nh += th;
         nm += tm;
     }
     __syncthreads();
 
     // Candidates: the first nm entries of the LRU order that this call has
-    // not used and that are not pinned.
+    // not used and that are not pinned, with their owners' scores (-1: the
+    // owner is never protected).
     int nv = 0;
     for (int base = 0; nv < nm && base < S; base += kThreads) {
         const int i = base + tid;
-        int s = -1, o = -1;
+        int sl = -1, o = -1;
         bool f = false;
+        int64_t sc = -1;
         if (i < S) {
-            if (p.pairs) {
-                const int2 v = reinterpret_cast<const int2 *>(p.order)[i];
-                s = v.x;
-                o = v.y;
-            } else {
-                s = p.order[i];
+            order_at(base, i, sl, o);
+            const uint32_t st = base == 0 ? stamp0 : p.stamp[sl];
+            f = touched[sl] == 0 && !(st != 0u && st >= latest_demand);
+            if (f) {
+                if (base == 0) {
+                    o = o00;
+                    if (o >= 0 && ofreq0 >= 2) sc = lfru_score(ofreq0, odlast0, now);
+                } else {
+                    if (!p.pairs) o = p.own[sl];
+                    if (o >= 0) {
+                        const int64_t fq = p.freq[o];
+                        if (fq >= 2) sc = lfru_score(fq, p.dlast[o], now);
+                    }
+                }
             }
-            const uint32_t st = p.stamp[s];
-            f = touched[s] == 0 && !(st != 0u && st >= latest_demand);
-            if (f && !p.pairs) o = p.own[s];
         }
         int tot;
         const int r = block_scan(f, wsum, tot);
         if (f && nv + r < nm) {
-            vslot[nv + r] = s;
+            vslot[nv + r] = sl;
             vown[nv + r] = o;
+            score_v[nv + r] = sc;
         }
         nv = min(nm, nv + tot);
-    }
-    __syncthreads();
-
-    // Heat of the candidates' owners and of the missing predictions.
-    for (int j = tid; j < nv; j += kThreads) {
-        const int o = vown[j];
-        int64_t sc = -1;
-        if (o >= 0) {
-            const int64_t f = p.freq[o];
-            if (f >= 2) sc = lfru_score(f, p.dlast[o], now);
-        }
-        score_v[j] = sc;
-    }
-    for (int k = tid; k < nm; k += kThreads) {
-        const int64_t x = lbase + missl[k];
-        score_p[k] = lfru_score(p.freq[x], p.dlast[x], now);
     }
     __syncthreads();
 
@@ -204,15 +266,7 @@ __global__ __launch_bounds__(kThreads) void prefetch_kernel(PrefetchParams p) {
         for (int base = 0; base < S; base += kThreads) {
             const int i = base + tid;
             int s = -1, o = -1;
-            if (i < S) {
-                if (p.pairs) {
-                    const int2 v = reinterpret_cast<const int2 *>(p.order)[i];
-                    s = v.x;
-                    o = v.y;
-                } else {
-                    s = p.order[i];
-                }
-            }
+            if (i < S) order_at(base, i, s, o);
             const bool f = i < S && touched[s] == 0;
             int tot;
             const int r = block_scan(f, wsum, tot);
