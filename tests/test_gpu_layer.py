@@ -445,6 +445,34 @@ def test_all_schedules_are_bit_identical():
             lay.close()
 
 
+@pytest.mark.parametrize("fmt,K", [(1, 1), (1, 3), (1, 6), (2, 5), (2, 7), (0, 3)])
+def test_staged_steps_split_any_top_k_like_the_serial_path(fmt, K):
+    """Stage 2 of 4-bit rows splits a step's routes over four waves (the
+    last ones may get none): any top-k gives the serial schedule's bytes
+    and the oracle's values."""
+    L, E, S, H, F = 2, 32, 12, 1024, 256
+    lays = [_tiny_layers(ov, True, seed=41, fmt=fmt, L=L, E=E, S=S, H=H, F=F, K=K) for ov in (0, 2)]
+    g = W.rng(41, "split", fmt, K)
+    outs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in lays]
+    host, sh = lays[0][1], lays[0][2]
+    oc = oracle.OracleCache(L, E, S)
+    try:
+        for t in range(6):
+            for l in range(L):
+                xn = W.normal_bf16(g, (1, H))
+                lg = W.zipf_logits(g, 1, E, 0.5)
+                for (lay, _, _), o in zip(lays, outs):
+                    lay.decode(l, _dev_u16(xn), torch.from_numpy(lg).cuda(), K, o)
+                torch.cuda.synchronize()
+                assert torch.equal(outs[0], outs[1]), (t, l)
+                ref, _, _ = _oracle_layer(oc, host, sh, l, xn, lg, K, fmt, H, F)
+                _close(_bf16_to_f64(outs[1]), ref, f"fmt{fmt} K{K} t{t} l{l}")
+        assert m.moe_cache_stats(lays[1][0].cache)[2] > 0
+    finally:
+        for lay, _, _ in lays:
+            lay.close()
+
+
 def test_shared_expert_decode_shape_staged():
     """H 2048, F 512, top-8 of 256 + gated shared expert, 2 layers over a
     small cache (many misses): the staged schedule equals the serial one bit
