@@ -128,6 +128,36 @@ def test_grouped_routes_do_not_depend_on_their_place_in_the_group(fmt, rows):
     _close(_bf16_to_f64(a), ref, f"fmt{fmt} rows{rows}")
 
 
+@pytest.mark.parametrize("fmt,H,T,K", [(1, 1024, 33, 2), (0, 64, 5, 3)])
+def test_wide_combine_takes_unaligned_outputs_and_addends(fmt, H, T, K):
+    """The combine of a grouped step writes 8 outputs per thread when the
+    output and the addend are 16-byte aligned, one otherwise: the same
+    bytes either way, and within tolerance of the oracle."""
+    F, rows = 256 if H > 64 else 128, 12
+    g = W.rng(12, "unaligned", fmt, H)
+    _, pool, opool = _pool_pair(fmt, rows, H, F, 13)
+    x = W.normal_bf16(g, (T, H))
+    idx = np.stack([g.choice(rows, K, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[g.random((T, K)) < 0.15] = -1
+    wts = g.random((T, K)).astype(np.float32)
+    add = (g.standard_normal((T, H)) * 0.01).astype(np.float32)
+    ws = torch.empty(m.moe_routed_workspace_bytes(fmt, H, F, T, K), dtype=torch.uint8, device="cuda")
+    args = (_dev_u16(x), torch.from_numpy(idx).cuda(), torch.from_numpy(wts).cuda())
+    outs = []
+    for shift in (0, 1):
+        ob = torch.empty(T * H + 8, dtype=torch.int16, device="cuda")
+        ab = torch.zeros(T * H + 4, dtype=torch.float32, device="cuda")
+        out = ob[shift:shift + T * H].view(T, H)
+        a = ab[shift:shift + T * H].view(T, H)
+        a.copy_(torch.from_numpy(add))
+        m.moe_routed_decode(pool, *args, out, ws, addend=a)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    assert torch.equal(outs[0], outs[1])
+    ref = oracle.routed(opool, idx, wts.astype(np.float64), x, addend=add.astype(np.float64))
+    _close(_bf16_to_f64(outs[0]), ref, f"fmt{fmt} H{H}")
+
+
 def test_routed_skips_minus_one_and_rows_outside_the_pool():
     """[P1 section 5] a -1 route adds nothing; rows >= num_rows are treated
     the same way."""
