@@ -164,6 +164,20 @@ def test_large_cache_uses_the_general_kernel():
     _run(L, E, S, steps, check_every=10)
 
 
+@pytest.mark.parametrize("S", [5000, 12000])
+def test_register_order_of_8_and_16_slots_per_thread(S):
+    """Caches of 4097-16384 slots keep 8 or 16 (slot, owner) order entries
+    per thread of the register-resident kernel; wide and narrow steps with
+    evictions across layers (20 x 640 experts > S)."""
+    g = np.random.default_rng(S)
+    L, E = 20, 640
+    steps = []
+    for i in range(80):
+        R = int(g.integers(1, 64)) if i % 2 else int(g.integers(64, 1300))
+        steps.append((int(g.integers(0, L)), g.integers(-1, E + 1, R), int(g.choice([-1, -1, 3]))))
+    _run(L, E, S, steps, check_every=4)
+
+
 @pytest.mark.parametrize("one,qw", [(256, 128), (20, 8), (1, 1)])
 def test_narrow_steps_with_caps_and_invalid_ids(one, qw):
     """Steps of at most 64 routes (one route per lane of a wave), over a

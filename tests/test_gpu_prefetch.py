@@ -148,6 +148,7 @@ def _ops(g, L, E, n_ops, max_r, hot_frac, cap_choices=(-1,)):
     (3, 64, 40, 256, 128, 64),       # narrow steps up to one wave
     (2, 96, 70, 40, 16, 300),        # wide chunked steps
     (1, 300, 500, 256, 128, 250),    # many predictions per call
+    (2, 64, 6000, 256, 128, 64),     # (slot, owner) order longer than the entries a thread holds
 ])
 def test_mixed_traces_match_the_oracle(L, E, S, one, qw, max_r):
     g = np.random.default_rng(100 + E)
