@@ -685,13 +685,18 @@ __global__ __launch_bounds__(kCountThreads) void group_count_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
 
-    for (int r = tid; r < num_rows; r += kCountThreads) cnt[r] = 0;
-    __syncthreads();
+    // the routes' rows first (in flight while the counts are cleared)
     int row[kCountRoutesPerThread], pos[kCountRoutesPerThread];
 #pragma unroll
     for (int k = 0; k < kCountRoutesPerThread; ++k) {
         const int i = tid + k * kCountThreads;
-        const int r = i < n ? idx[i] : -1;
+        row[k] = i < n ? idx[i] : -1;
+    }
+    for (int r = tid; r < num_rows; r += kCountThreads) cnt[r] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kCountRoutesPerThread; ++k) {
+        const int r = row[k];
         row[k] = (r >= 0 && r < num_rows) ? r : -1;
         pos[k] = row[k] >= 0 ? atomicAdd(&cnt[row[k]], 1) : 0;
     }
