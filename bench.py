@@ -779,7 +779,7 @@ def host_description() -> dict:
 DECODE_KERNELS = ("admit_fast_kernel", "admit_kernel", "topk_kernel", "stage1_kernel", "stage2_kernel",
                   "gather_kernel", "up_kernel", "down_d_kernel", "down_fused_kernel",
                   "group_count_kernel", "up_mfma_kernel", "down_mfma_kernel", "up_x_kernel",
-                  "down_x_kernel", "combine_kernel", "prefetch_kernel")
+                  "down_x_kernel", "combine_kernel", "combine8_kernel", "prefetch_kernel")
 
 
 def _short(name: str) -> str:
@@ -836,8 +836,9 @@ def _wide_calls(log, moe):
     pos = 3 * (W_ + 2 * K_) * L + 2 * log["gemv_calls"]
     out = []
     # grouping, gate/up (bf16, or the LDS-staged 4-bit kernel), down, combine
+    # (one output per thread, or eight for aligned outputs)
     kinds = [("group_count_kernel",), ("up_mfma_kernel", "up_x_kernel"), ("down_mfma_kernel", "down_x_kernel"),
-             ("combine_kernel",)]
+             ("combine_kernel", "combine8_kernel")]
     for wcfg in log.get("wide") or []:
         seq = moe[pos:pos + 4 * wcfg["calls"]]
         pos += 4 * wcfg["calls"]
