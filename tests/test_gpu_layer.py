@@ -158,6 +158,48 @@ def test_wide_combine_takes_unaligned_outputs_and_addends(fmt, H, T, K):
     _close(_bf16_to_f64(outs[0]), ref, f"fmt{fmt} H{H}")
 
 
+@pytest.mark.parametrize("fmt,T,K", [(0, 50, 3), (2, 40, 2)])
+def test_routed_over_a_pool_of_more_than_32768_rows(fmt, T, K):
+    """Pools past 32768 rows group their routes with the rank-sort kernel
+    instead of the counting one (whose LDS holds one count per row); rows
+    on both sides of 32768, against the oracle over host copies of the rows
+    the step reads."""
+    H, F, rows = 64, 128, 40000
+    banks = W.device_expert_rows(fmt, (18, fmt), rows, H, F)
+    pool = m.make_pool(fmt, H, F, rows, banks)
+    g = W.rng(18, "big-pool", fmt)
+    x = W.normal_bf16(g, (T, H))
+    idx = np.stack([g.choice(rows, K, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[:4, 0] = [0, 32767, 32768, rows - 1]
+    idx[g.random((T, K)) < 0.1] = -1
+    w = g.random((T, K))
+    out = _routed_gpu(pool, x, idx, w, H)
+    used = np.unique(idx[idx >= 0])
+    sel = torch.from_numpy(used.astype(np.int64)).cuda()
+    opool = oracle.Pool(fmt, H, F, [b.index_select(0, sel).cpu().numpy() for b in banks])
+    local = np.where(idx >= 0, np.searchsorted(used, idx), -1).astype(np.int32)
+    ref = oracle.routed(opool, local, w.astype(np.float32).astype(np.float64), x)
+    _close(_bf16_to_f64(out), ref, f"fmt{fmt} rows{rows}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_routed_at_the_route_limits(fmt):
+    """The largest steps the routed call takes: one token with top-64 (the
+    stage kernels' route limit) and 8192 routes (the counting grouping's
+    limit, 8 per thread)."""
+    H, F, rows = 64, 128, 300
+    _, pool, opool = _pool_pair(fmt, rows, H, F, 19)
+    g = W.rng(19, "limits", fmt)
+    for T, K in ((1, 64), (4096, 2)):
+        x = W.normal_bf16(g, (T, H))
+        idx = np.stack([g.choice(rows, K, replace=False) for _ in range(T)]).astype(np.int32)
+        idx[g.random((T, K)) < 0.05] = -1
+        w = g.random((T, K))
+        out = _routed_gpu(pool, x, idx, w, H)
+        ref = oracle.routed(opool, idx, w.astype(np.float32).astype(np.float64), x)
+        _close(_bf16_to_f64(out), ref, f"fmt{fmt} T{T} K{K}")
+
+
 def test_routed_skips_minus_one_and_rows_outside_the_pool():
     """[P1 section 5] a -1 route adds nothing; rows >= num_rows are treated
     the same way."""
