@@ -545,6 +545,38 @@ def test_staged_steps_split_any_top_k_like_the_serial_path(fmt, K):
             lay.close()
 
 
+@pytest.mark.parametrize("fmt,E,S,K", [(0, 128, 100, 64), (1, 128, 90, 64), (2, 1500, 40, 8), (0, 1025, 30, 6)])
+def test_single_token_layer_steps_at_the_top_k_and_expert_limits(fmt, E, S, K):
+    """Top-64 (the largest a single-token step takes: the admission's fused
+    top-k and the stage kernels' route limit) and more than 1024 experts
+    (the fused top-k's limit: a separate top-k launch first), with the
+    shared expert and misses every step: slot ids exact, staged == serial
+    bit for bit, outputs within tolerance of the oracle."""
+    L, H, F = 2, 64, 128
+    lays = [_tiny_layers(ov, True, seed=43, fmt=fmt, L=L, E=E, S=S, H=H, F=F, K=K) for ov in (2, 0)]
+    host, sh = lays[0][1], lays[0][2]
+    oc = oracle.OracleCache(L, E, S)
+    g = W.rng(43, "limits", fmt, E, K)
+    outs = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in lays]
+    ids = [torch.empty((1, K), dtype=torch.int32, device="cuda") for _ in lays]
+    try:
+        for t in range(5):
+            for l in range(L):
+                x = W.normal_bf16(g, (1, H))
+                lg = W.zipf_logits(g, 1, E, 0.5)
+                for (lay, _, _), o, i in zip(lays, outs, ids):
+                    lay.decode(l, _dev_u16(x), torch.from_numpy(lg).cuda(), K, o, ids_out=i)
+                torch.cuda.synchronize()
+                assert torch.equal(outs[0], outs[1]) and torch.equal(ids[0], ids[1]), (t, l)
+                ref, slots, _ = _oracle_layer(oc, host, sh, l, x, lg, K, fmt, H, F)
+                np.testing.assert_array_equal(ids[0].cpu().numpy(), slots, err_msg=f"token {t} layer {l}")
+                _close(_bf16_to_f64(outs[0]), ref, f"fmt{fmt} E{E} K{K} t{t} l{l}")
+        assert m.moe_cache_stats(lays[0][0].cache)[2] > 0
+    finally:
+        for lay, _, _ in lays:
+            lay.close()
+
+
 def test_shared_expert_decode_shape_staged():
     """H 2048, F 512, top-8 of 256 + gated shared expert, 2 layers over a
     small cache (many misses): the staged schedule equals the serial one bit
