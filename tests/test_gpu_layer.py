@@ -158,6 +158,33 @@ def test_wide_combine_takes_unaligned_outputs_and_addends(fmt, H, T, K):
     _close(_bf16_to_f64(outs[0]), ref, f"fmt{fmt} H{H}")
 
 
+STAGE_SHAPES = [(64, 128), (1024, 256), (1024, 512), (2048, 256), (2048, 512), (2048, 1024), (4096, 512),
+                (4096, 1024)]
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("H,F", STAGE_SHAPES)
+def test_single_token_routed_at_every_stage_shape(H, F, fmt):
+    """Every (hidden, FFN) width the one-token stage kernels are built for,
+    in every format, against the oracle (device-drawn experts, all
+    distinct; a -1 route and a weight of zero included)."""
+    rows, K = 6, 5
+    banks = W.device_expert_rows(fmt, (20, fmt, H, F), rows, H, F)
+    pool = m.make_pool(fmt, H, F, rows, banks)
+    opool = oracle.Pool(fmt, H, F, [b.cpu().numpy() for b in banks])
+    g = W.rng(20, "stage-shapes", fmt, H, F)
+    x = W.normal_bf16(g, (1, H))
+    idx = g.choice(rows, K, replace=False).astype(np.int32)[None, :]
+    idx[0, 2] = -1
+    w = g.random((1, K))
+    w[0, 4] = 0.0
+    add = g.standard_normal((1, H)) * 0.01
+    out = _routed_gpu(pool, x, idx, w, H, addend=add)
+    ref = oracle.routed(opool, idx, w.astype(np.float32).astype(np.float64), x,
+                        addend=add.astype(np.float32).astype(np.float64))
+    _close(_bf16_to_f64(out), ref, f"fmt{fmt} H{H} F{F}")
+
+
 @pytest.mark.parametrize("fmt,T,K", [(0, 50, 3), (2, 40, 2)])
 def test_routed_over_a_pool_of_more_than_32768_rows(fmt, T, K):
     """Pools past 32768 rows group their routes with the rank-sort kernel
