@@ -185,6 +185,28 @@ def test_single_token_routed_at_every_stage_shape(H, F, fmt):
     _close(_bf16_to_f64(out), ref, f"fmt{fmt} H{H} F{F}")
 
 
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("H,F", [(128, 256), (512, 256), (512, 1024), (1024, 512), (1024, 1024), (2048, 512),
+                                 (4096, 1024)])
+def test_grouped_routed_across_widths(H, F, fmt):
+    """Grouped steps (T > 1) across the widths that pick different kernels:
+    matrix-core gate/up and down (bf16 at every width, 4-bit outside the
+    LDS-staged widths), the LDS-staged 4-bit kernels (hidden 512 / 1024,
+    FFN 256 / 512 / 1024); against the oracle, device-drawn experts."""
+    rows, T, K = 8, 24, 2
+    banks = W.device_expert_rows(fmt, (21, fmt, H, F), rows, H, F)
+    pool = m.make_pool(fmt, H, F, rows, banks)
+    opool = oracle.Pool(fmt, H, F, [b.cpu().numpy() for b in banks])
+    g = W.rng(21, "grouped-widths", fmt, H, F)
+    x = W.normal_bf16(g, (T, H))
+    idx = np.stack([g.choice(rows, K, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[g.random((T, K)) < 0.1] = -1
+    w = g.random((T, K))
+    out = _routed_gpu(pool, x, idx, w, H)
+    ref = oracle.routed(opool, idx, w.astype(np.float32).astype(np.float64), x)
+    _close(_bf16_to_f64(out), ref, f"fmt{fmt} H{H} F{F}")
+
+
 @pytest.mark.parametrize("fmt,T,K", [(0, 50, 3), (2, 40, 2)])
 def test_routed_over_a_pool_of_more_than_32768_rows(fmt, T, K):
     """Pools past 32768 rows group their routes with the rank-sort kernel
