@@ -441,12 +441,13 @@ def test_wide_step_cached_equals_streamed_bit_for_bit(fmt, H, F, E, S, T, K, one
         lay.close()
 
 
-@pytest.mark.parametrize("overlap", [1, 2, 3])
-def test_graph_replay_matches_eager_over_changing_routes(overlap):
+@pytest.mark.parametrize("overlap,fmt", [(1, 0), (2, 0), (3, 0), (2, 1), (2, 2), (3, 1)])
+def test_graph_replay_matches_eager_over_changing_routes(overlap, fmt):
     """A whole token (3 layers) captured as one graph and replayed over 40
-    steps with changing routes equals the same steps run eagerly."""
+    steps with changing routes equals the same steps run eagerly (bf16 and
+    the 4-bit formats)."""
     L, E, S, H, F, K = 3, 16, 10, 64, 128, 2
-    mk = lambda: _tiny_layers(overlap, True, seed=3, L=L, E=E, S=S)[0]
+    mk = lambda: _tiny_layers(overlap, True, seed=3, fmt=fmt, L=L, E=E, S=S)[0]
     graph_l, eager_l = mk(), mk()
     g = W.rng(3, "graph")
     steps = 40
