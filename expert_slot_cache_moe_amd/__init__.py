@@ -93,7 +93,7 @@ def lib():
             "moe_cache_stats": (st, [P, i32, P, P]),
             "moe_prefetch": (st, [P, i32, P, i32, P]),
             "moe_cache_set_cpu_threads": (st, [P, i32]),
-            "moe_cpu_experts": (st, [i32, i32, i32, i32, i32, P, P, P, P, P, P]),
+            "moe_cpu_experts": (st, [i32, i32, i32, i32, i32, i32, P, P, P, P, P]),
             "moe_layer_decode_hybrid": (st, [P, i32, P, P, i32, i32, P, i32, P, P, P, P]),
             "moe_prefetch_join": (st, [P, P]),
             "moe_cache_read_state": (st, [P, P, P, P, P, P, P, P, P, P]),
@@ -349,19 +349,20 @@ def moe_layer_decode(cache: Cache, layer: int, x, logits, K: int, out, shared=No
         _dev_ptr(ids_out), _dev_ptr(w_out), _stream(stream)))
 
 
-def moe_cpu_experts(threads: int, experts, w, x, w13_rows, w2_rows, H: int, F: int) -> np.ndarray:
+def moe_cpu_experts(threads: int, experts, w, x, banks, H: int, F: int, fmt: int = MOE_FMT_BF16) -> np.ndarray:
     """The hybrid step's CPU half on host arrays: experts int32 [T,K] (-1 =
-    not a CPU route), w fp32 [T,K], x bf16 bits uint16 [T,H], w13_rows /
-    w2_rows the layer's bf16 banks as uint8 [E, bytes].  Returns fp32 [T,H]."""
+    not a CPU route), w fp32 [T,K], x bf16 bits uint16 [T,H], banks the
+    layer's banks of the format in bank order, each uint8 [E, bytes].
+    Returns fp32 [T,H]."""
     experts = np.ascontiguousarray(experts, np.int32)
     w = np.ascontiguousarray(w, np.float32)
     x = np.ascontiguousarray(x, np.uint16)
-    w13 = np.ascontiguousarray(w13_rows, np.uint8)
-    w2 = np.ascontiguousarray(w2_rows, np.uint8)
+    banks = [np.ascontiguousarray(b, np.uint8) for b in banks]
     T, K = experts.shape
     out = np.zeros((T, H), np.float32)
-    _check(lib().moe_cpu_experts(threads, T, K, H, F, _np_ptr(experts), _np_ptr(w), _np_ptr(x),
-                                 _np_ptr(w13), _np_ptr(w2), _np_ptr(out)))
+    ptrs = (C.c_void_p * len(banks))(*[b.ctypes.data for b in banks])
+    _check(lib().moe_cpu_experts(threads, fmt, T, K, H, F, _np_ptr(experts), _np_ptr(w), _np_ptr(x),
+                                 ptrs, _np_ptr(out)))
     return out
 
 

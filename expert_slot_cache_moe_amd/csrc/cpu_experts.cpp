@@ -12,6 +12,8 @@
 // partial sums (two 8-wide FMA chains once vectorised) added pairwise.
 #include "cpu_experts.h"
 
+#include "moe_cache.h"
+
 #include <atomic>
 #include <cmath>
 #include <condition_variable>
@@ -53,6 +55,67 @@ inline float dot_bf16(const uint16_t *__restrict a, const float *__restrict b, i
     for (int s = 8; s >= 1; s >>= 1)
         for (int j = 0; j < s; ++j) acc[j] += acc[j + s];
     return acc[0];
+}
+
+inline float dot_f32(const float *__restrict a, const float *__restrict b, int n) {
+    float acc[16] = {};
+    for (int i = 0; i < n; i += 16)
+        for (int j = 0; j < 16; ++j) acc[j] += a[i + j] * b[i + j];
+    for (int s = 8; s >= 1; s >>= 1)
+        for (int j = 0; j < s; ++j) acc[j] += acc[j + s];
+    return acc[0];
+}
+
+// The OCP microscaling element and scale encodings, decoded once into
+// tables: E2M1 (sign, 2-bit exponent with bias 1, 1-bit mantissa), E4M3
+// "fn" (bias 7, subnormals, 0x7f / 0xff NaN, no infinities), E8M0 (2^(v -
+// 127), 0xff NaN).
+struct Tables {
+    float e2m1[16], e4m3[256], e8m0[256];
+    Tables() {
+        static const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+        for (int v = 0; v < 16; ++v) e2m1[v] = (v & 8) ? -mag[v & 7] : mag[v & 7];
+        for (int v = 0; v < 256; ++v) {
+            const int ex = (v >> 3) & 15, mt = v & 7;
+            float f;
+            if (ex == 15 && mt == 7) f = std::nanf("");
+            else if (ex == 0) f = std::ldexp((float)mt, -9);
+            else f = std::ldexp(1.f + mt / 8.f, ex - 7);
+            e4m3[v] = (v & 0x80) ? -f : f;
+            e8m0[v] = v == 255 ? std::nanf("") : std::ldexp(1.f, v - 127);
+        }
+    }
+};
+const Tables &tables() {
+    static const Tables t;
+    return t;
+}
+
+// Row `row` of matrix m (0: w13 [2F][H], 1: w2 [H][F]) of expert e, dotted
+// with xf (n floats, n the row length); wv: n floats of scratch.  4-bit
+// rows are expanded to fp32 (code times its block's scale) first; the
+// E2M1 global scale multiplies the dot product.
+float row_dot(const CpuRoutes &r, int m, int e, int row, const float *xf, int n, float *wv) {
+    if (r.fmt == MOE_FMT_BF16) {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(r.bank[m] + (size_t)e * r.rb[m]) + (size_t)row * n;
+        return dot_bf16(p, xf, n);
+    }
+    const Tables &tb = tables();
+    const bool e2m1 = r.fmt == MOE_FMT_E2M1;
+    const int b0 = (e2m1 ? 3 : 2) * m, block = e2m1 ? 16 : 32;
+    const uint8_t *codes = r.bank[b0] + (size_t)e * r.rb[b0] + (size_t)row * (n / 2);
+    const uint8_t *sc = r.bank[b0 + 1] + (size_t)e * r.rb[b0 + 1] + (size_t)row * (n / block);
+    for (int i = 0; i < n; i += block) {
+        const float s = e2m1 ? tb.e4m3[sc[i / block]] : tb.e8m0[sc[i / block]];
+        for (int j = 0; j < block; j += 2) {
+            const uint8_t c = codes[(i + j) / 2];
+            wv[i + j] = tb.e2m1[c & 15] * s;
+            wv[i + j + 1] = tb.e2m1[c >> 4] * s;
+        }
+    }
+    float glob = 1.f;
+    if (e2m1) std::memcpy(&glob, r.bank[b0 + 2] + (size_t)e * r.rb[b0 + 2], 4);
+    return dot_f32(wv, xf, n) * glob;
 }
 
 }  // namespace
@@ -132,14 +195,13 @@ private:
         const int64_t lo = items_ * id / n_, hi = items_ * (id + 1) / n_;
         const CpuRoutes &r = *r_;
         const int H = r.H, F = r.F;
+        std::vector<float> wv(r.fmt == MOE_FMT_BF16 ? 0 : (size_t)(H > F ? H : F));
         if (phase_ == 0) {
             for (int64_t it = lo; it < hi; ++it) {
                 const int q = (int)(it / (2 * F)), f = (int)(it % (2 * F));
                 const int route = routes_[q];
-                const int e = r.expert[route];
-                const uint16_t *row =
-                    reinterpret_cast<const uint16_t *>(r.w13 + (size_t)e * 4 * F * H) + (size_t)f * H;
-                gu_[(size_t)q * 2 * F + f] = dot_bf16(row, &xf_[(size_t)(route / r.K) * H], H);
+                gu_[(size_t)q * 2 * F + f] =
+                    row_dot(r, 0, r.expert[route], f, &xf_[(size_t)(route / r.K) * H], H, wv.data());
             }
         } else if (phase_ == 1) {
             for (int64_t it = lo; it < hi; ++it) {
@@ -154,10 +216,7 @@ private:
                     float acc = 0.f;
                     while (q < (int)routes_.size() && routes_[q] / r.K == t) {
                         const int route = routes_[q];
-                        const uint16_t *row = reinterpret_cast<const uint16_t *>(
-                                                  r.w2 + (size_t)r.expert[route] * 2 * F * H) +
-                                              (size_t)i * F;
-                        acc += r.w[route] * dot_bf16(row, &h_[(size_t)q * F], F);
+                        acc += r.w[route] * row_dot(r, 1, r.expert[route], (int)i, &h_[(size_t)q * F], F, wv.data());
                         ++q;
                     }
                     r.partial[(size_t)t * H + i] = acc;

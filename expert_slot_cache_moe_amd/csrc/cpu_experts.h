@@ -5,8 +5,11 @@
 //
 // Plain C++ (no HIP): a fixed pool of worker threads, created once, that
 // computes the partial sum of a step's CPU routes from the pinned host
-// store.  The rows are the bf16 layout of the slot banks: w13 [2F][H]
-// (gate rows, then up rows) and w2 [H][F].
+// store.  The rows have the slot banks' layout in every weight format:
+// w13 [2F][H] (gate rows, then up rows) and w2 [H][F], as bf16, or as
+// E2M1 codes (two per byte, the even element in the low nibble) with one
+// E4M3 scale per 16 elements and an fp32 global scale per matrix (six
+// banks), or with one E8M0 scale per 32 elements (MXFP4, four banks).
 #pragma once
 
 #include <cstdint>
@@ -15,11 +18,12 @@ namespace moe {
 
 struct CpuRoutes {
     int T, K, H, F;
+    int fmt;                      // MOE_FMT_BF16 / _E2M1 / _MXFP4
     const int32_t *expert;        // [T][K] expert id of each CPU route, -1 = not a CPU route
     const float *w;               // [T][K] route weights
     const uint16_t *x;            // [T][H] bf16 hidden states
-    const uint8_t *w13;           // the layer's w13 rows [E][4FH bytes]
-    const uint8_t *w2;            // the layer's w2 rows [E][2FH bytes]
+    const uint8_t *bank[6];       // the layer's rows of each bank, [E][rb[b] bytes]
+    int64_t rb[6];
     float *partial;               // [T][H] out: sum over CPU routes, ascending k
 };
 

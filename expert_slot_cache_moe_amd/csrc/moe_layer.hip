@@ -189,8 +189,9 @@ moe_status_t moe_cache_set_cpu_threads(moe_cache_t *c, int32_t threads) {
     if (threads > 0) {
         if (c->nb == 0 || c->d.max_tokens < 1)
             return fail(MOE_INVALID_ARG, "the hybrid step needs weight banks and max_tokens > 0");
-        if (c->d.weight_format != MOE_FMT_BF16 || c->d.hidden % 16 || c->d.ffn % 16)
-            return fail(MOE_UNSUPPORTED, "the CPU experts take bf16 rows with hidden and ffn multiples of 16");
+        const int blk = c->d.weight_format == MOE_FMT_MXFP4 ? 32 : 16;
+        if (c->d.hidden % blk || c->d.ffn % blk)
+            return fail(MOE_UNSUPPORTED, "the CPU experts take hidden and ffn multiples of %d in this format", blk);
     }
     HIP_TRY(hipDeviceSynchronize(), "sync");
     if (c->cpu) {
@@ -225,25 +226,32 @@ moe_status_t moe_cache_set_cpu_threads(moe_cache_t *c, int32_t threads) {
     return MOE_OK;
 }
 
-moe_status_t moe_cpu_experts(int32_t threads, int32_t T, int32_t K, int32_t H, int32_t F,
-                             const int32_t *experts, const float *w, const void *x,
-                             const void *w13_rows, const void *w2_rows, float *partial) {
-    if (threads < 1 || threads > 1024 || T < 0 || K < 1 || H < 16 || F < 16 || H % 16 || F % 16)
+moe_status_t moe_cpu_experts(int32_t threads, int32_t weight_format, int32_t T, int32_t K, int32_t H,
+                             int32_t F, const int32_t *experts, const float *w, const void *x,
+                             const void *const *banks, float *partial) {
+    if (weight_format != MOE_FMT_BF16 && weight_format != MOE_FMT_E2M1 && weight_format != MOE_FMT_MXFP4)
+        return fail(MOE_INVALID_ARG, "weight_format %d", weight_format);
+    const int blk = weight_format == MOE_FMT_MXFP4 ? 32 : 16;
+    if (threads < 1 || threads > 1024 || T < 0 || K < 1 || H < blk || F < blk || H % blk || F % blk)
         return fail(MOE_INVALID_ARG, "bad CPU expert sizes (threads %d, T %d, K %d, H %d, F %d)", threads,
                     T, K, H, F);
     if (T == 0) return MOE_OK;
-    if (!experts || !w || !x || !w13_rows || !w2_rows || !partial)
-        return fail(MOE_INVALID_ARG, "NULL CPU expert buffer");
+    if (!experts || !w || !x || !banks || !partial) return fail(MOE_INVALID_ARG, "NULL CPU expert buffer");
     CpuRoutes r{};
+    int nb = 0;
+    row_bytes_of(weight_format, H, F, r.rb, &nb);
+    for (int b = 0; b < nb; ++b) {
+        if (!banks[b]) return fail(MOE_INVALID_ARG, "NULL CPU expert bank %d", b);
+        r.bank[b] = static_cast<const uint8_t *>(banks[b]);
+    }
     r.T = T;
     r.K = K;
     r.H = H;
     r.F = F;
+    r.fmt = weight_format;
     r.expert = experts;
     r.w = w;
     r.x = static_cast<const uint16_t *>(x);
-    r.w13 = static_cast<const uint8_t *>(w13_rows);
-    r.w2 = static_cast<const uint8_t *>(w2_rows);
     r.partial = partial;
     CpuExperts *p = cpu_experts_create(threads);
     cpu_experts_run(p, r);
@@ -312,8 +320,11 @@ moe_status_t moe_layer_decode_hybrid(moe_cache_t *c, int32_t layer, const void *
         r.expert = c->cpu_ids.data();
         r.w = c->h_w;
         r.x = c->h_x;
-        r.w13 = c->host_rows[lb + 0];
-        r.w2 = c->host_rows[lb + 1];
+        r.fmt = c->d.weight_format;
+        for (int b = 0; b < c->nb; ++b) {
+            r.bank[b] = c->host_rows[lb + b];
+            r.rb[b] = c->rb[b];
+        }
         r.partial = c->h_partial;
         cpu_experts_run(c->cpu, r);
         return hipSuccess;

@@ -329,7 +329,7 @@ moe_status_t moe_layer_decode(moe_cache_t *cache, int32_t layer, const void *x_d
  * thread of a hybrid step works too: threads - 1 workers are started.
  * Synchronises the device.  Errors: MOE_INVALID_ARG (threads outside
  * [0, 1024], a cache without banks or layer workspace), MOE_UNSUPPORTED
- * (the CPU experts take bf16 rows with hidden and ffn multiples of 16),
+ * (hidden and ffn not multiples of 16, or of 32 for MXFP4),
  * MOE_OUT_OF_MEMORY. */
 moe_status_t moe_cache_set_cpu_threads(moe_cache_t *cache, int32_t threads);
 
@@ -338,15 +338,18 @@ moe_status_t moe_cache_set_cpu_threads(moe_cache_t *cache, int32_t threads);
  * of w[t][k] * W2[e] (bf16(silu(W1[e] x_t) * (W3[e] x_t))), e =
  * experts[t][k], in fp32 with the activation rounded to bf16.  experts:
  * int32 [T][K] expert ids or -1; w: fp32 [T][K]; x: bf16 [T][H];
- * w13_rows: a layer's bf16 gate/up rows [E][2F][H]; w2_rows: its down rows
- * [E][H][F]; partial: fp32 [T][H] out.  Starts threads - 1 workers for
- * the call.  The result does not depend on the thread count.  Errors:
- * MOE_INVALID_ARG (threads outside [1, 1024], H or F not a multiple of
- * 16, null pointers). */
-moe_status_t moe_cpu_experts(int32_t threads, int32_t T, int32_t K, int32_t H, int32_t F,
-                             const int32_t *experts_host, const float *w_host, const void *x_host,
-                             const void *w13_rows_host, const void *w2_rows_host,
-                             float *partial_host);
+ * banks_host: the layer's host rows of each weight bank of the format, in
+ * bank order (moe_bank_row_bytes: 2 for bf16, 6 for E2M1, 4 for MXFP4),
+ * each [E][row bytes]; 4-bit weights are expanded to fp32 as code times
+ * its block's scale (E4M3 per 16, or E8M0 per 32) and the E2M1 global
+ * scale multiplies each dot product; partial: fp32 [T][H] out.  Starts
+ * threads - 1 workers for the call.  The result does not depend on the
+ * thread count.  Errors: MOE_INVALID_ARG (unknown format, threads
+ * outside [1, 1024], H or F not a multiple of the format's block -- 16,
+ * or 32 for MXFP4 -- null pointers). */
+moe_status_t moe_cpu_experts(int32_t threads, int32_t weight_format, int32_t T, int32_t K, int32_t H,
+                             int32_t F, const int32_t *experts_host, const float *w_host, const void *x_host,
+                             const void *const *banks_host, float *partial_host);
 
 /* The hybrid layer step [P1 sections 4-5]: routes the cache leaves at -1
  * (misses beyond max_fetch, or with no victim) run on host cores over the

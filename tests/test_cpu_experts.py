@@ -15,9 +15,9 @@ from parity import check_close
 
 
 
-def _case(seed, E, H, F, T, K, cpu_frac):
-    g = W.rng(seed, "cpu-experts", E, H, T)
-    banks = W.bf16_expert_rows(g, E, H, F)
+def _case(seed, E, H, F, T, K, cpu_frac, fmt=0):
+    g = W.rng(seed, "cpu-experts", E, H, T, fmt)
+    banks = W.expert_rows(fmt, g, E, H, F)
     x = W.normal_bf16(g, (T, H))
     ids = np.stack([g.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
     cpu = np.where(g.random((T, K)) < cpu_frac, ids, -1).astype(np.int32)
@@ -25,23 +25,25 @@ def _case(seed, E, H, F, T, K, cpu_frac):
     return banks, x, cpu, w
 
 
+@pytest.mark.parametrize("fmt", [0, 1, 2])
 @pytest.mark.parametrize("E,H,F,T,K,frac", [
     (8, 64, 128, 1, 2, 1.0),          # the tiny layer, every route on the CPU
     (8, 64, 128, 5, 2, 0.5),          # ragged: some tokens have no CPU route
     (16, 256, 64, 7, 4, 0.4),
     (32, 2048, 512, 1, 8, 0.3),       # the shared-expert decode shape, one token
 ])
-def test_cpu_routes_match_the_oracle(E, H, F, T, K, frac):
-    banks, x, cpu, w = _case(1, E, H, F, T, K, frac)
-    got = m.moe_cpu_experts(4, cpu, w, x, banks[0], banks[1], H, F)
-    ref = oracle.routed(oracle.Pool(0, H, F, banks), cpu, w.astype(np.float64), x)
+def test_cpu_routes_match_the_oracle(E, H, F, T, K, frac, fmt):
+    banks, x, cpu, w = _case(1, E, H, F, T, K, frac, fmt)
+    got = m.moe_cpu_experts(4, cpu, w, x, banks, H, F, fmt)
+    ref = oracle.routed(oracle.Pool(fmt, H, F, banks), cpu, w.astype(np.float64), x)
     assert (got[(cpu < 0).all(axis=1)] == 0).all()       # tokens with no CPU route add nothing
     check_close(got, ref, "CPU experts")
 
 
-def test_result_does_not_depend_on_the_thread_count():
-    banks, x, cpu, w = _case(2, 16, 256, 128, 6, 4, 0.7)
-    outs = [m.moe_cpu_experts(n, cpu, w, x, banks[0], banks[1], 256, 128) for n in (1, 2, 3, 8)]
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_result_does_not_depend_on_the_thread_count(fmt):
+    banks, x, cpu, w = _case(2, 16, 256, 128, 6, 4, 0.7, fmt)
+    outs = [m.moe_cpu_experts(n, cpu, w, x, banks, 256, 128, fmt) for n in (1, 2, 3, 8)]
     for o in outs[1:]:
         np.testing.assert_array_equal(o, outs[0])
 
@@ -49,13 +51,17 @@ def test_result_does_not_depend_on_the_thread_count():
 def test_no_cpu_route_gives_zeros():
     banks, x, cpu, w = _case(3, 8, 64, 128, 3, 2, 0.0)
     assert (cpu < 0).all()
-    got = m.moe_cpu_experts(2, cpu, w, x, banks[0], banks[1], 64, 128)
+    got = m.moe_cpu_experts(2, cpu, w, x, banks, 64, 128)
     assert (got == 0).all()
 
 
 def test_bad_sizes_are_rejected():
     banks, x, cpu, w = _case(4, 8, 64, 128, 1, 2, 1.0)
     with pytest.raises(m.MoeError):
-        m.moe_cpu_experts(0, cpu, w, x, banks[0], banks[1], 64, 128)
+        m.moe_cpu_experts(0, cpu, w, x, banks, 64, 128)
     with pytest.raises(m.MoeError):
-        m.moe_cpu_experts(2, cpu, w, x[:, :40], banks[0], banks[1], 40, 128)     # H % 16
+        m.moe_cpu_experts(2, cpu, w, x[:, :40], banks, 40, 128)     # H % 16
+    with pytest.raises(m.MoeError):
+        m.moe_cpu_experts(2, cpu, w, x[:, :48], banks, 48, 128, m.MOE_FMT_MXFP4)   # H % 32
+    with pytest.raises(m.MoeError):
+        m.moe_cpu_experts(2, cpu, w, x, banks, 64, 128, 7)          # no such format

@@ -25,29 +25,31 @@ def _dev_u16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
 
-def _layers(seed, L, E, S, H, F, T, K, overlap, shared=True):
-    g = W.rng(seed, "hybrid", L, E, H, T)
-    host = [W.bf16_expert_rows(g, E, H, F) for _ in range(L)]
+def _layers(seed, L, E, S, H, F, T, K, overlap, shared=True, fmt=0):
+    g = W.rng(seed, "hybrid", L, E, H, T, fmt)
+    host = [W.expert_rows(fmt, g, E, H, F) for _ in range(L)]
     sh = None
     if shared:
         sh = [(W.normal_bf16(g, 2 * F * H, 0.02), W.normal_bf16(g, H * F, 0.02), W.normal_bf16(g, H, 0.02))
               for _ in range(L)]
-    lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, host_rows=host, shared=sh,
+    lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, fmt=fmt, host_rows=host, shared=sh,
                           max_tokens=T, max_top_k=K, overlap=overlap)
     return lay, host, sh, g
 
 
-@pytest.mark.parametrize("overlap,T,max_fetch,shared", [
-    (2, 1, 0, True),       # every miss on the CPU, overlapped
-    (0, 1, 0, True),       # the serial debug order
-    (1, 1, 1, True),       # one fetch per step, the rest on the CPU
-    (2, 5, 1, True),       # a small batch (grouped GPU path)
-    (2, 3, 0, False),      # no shared expert: the CPU partial alone is the added term
-    (3, 1, 1, True),       # schedule 3 (the hybrid step overlaps the CPU half)
+@pytest.mark.parametrize("overlap,T,max_fetch,shared,fmt", [
+    (2, 1, 0, True, 0),       # every miss on the CPU, overlapped
+    (0, 1, 0, True, 0),       # the serial debug order
+    (1, 1, 1, True, 0),       # one fetch per step, the rest on the CPU
+    (2, 5, 1, True, 0),       # a small batch (grouped GPU path)
+    (2, 3, 0, False, 0),      # no shared expert: the CPU partial alone is the added term
+    (3, 1, 1, True, 0),       # schedule 3 (the hybrid step overlaps the CPU half)
+    (2, 1, 0, True, 1),       # E2M1 experts (E4M3 per-16 scales) on both halves
+    (2, 5, 1, True, 2),       # MXFP4 experts, a small batch
 ])
-def test_hybrid_steps_match_the_oracle(overlap, T, max_fetch, shared):
+def test_hybrid_steps_match_the_oracle(overlap, T, max_fetch, shared, fmt):
     L, E, S, H, F, K = 2, 16, 6, 64, 128, 2
-    lay, host, sh, g = _layers(51, L, E, S, H, F, T, K, overlap, shared)
+    lay, host, sh, g = _layers(51, L, E, S, H, F, T, K, overlap, shared, fmt)
     m.moe_cache_set_cpu_threads(lay.cache, 4)
     oc = oracle.OracleCache(L, E, S)
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
@@ -65,7 +67,7 @@ def test_hybrid_steps_match_the_oracle(overlap, T, max_fetch, shared):
                 add = None
                 if shared:
                     _, add = oracle.shared(H, F, sh[l][0], sh[l][1], sh[l][2], x)
-                ref = oracle.routed(oracle.Pool(0, H, F, host[l]), ids_e, w, x, addend=add)
+                ref = oracle.routed(oracle.Pool(fmt, H, F, host[l]), ids_e, w, x, addend=add)
                 torch.cuda.synchronize()
                 np.testing.assert_array_equal(ids.cpu().numpy(), slots, err_msg=f"step {step} layer {l}")
                 got = out.view(torch.bfloat16).double().cpu().numpy()

@@ -89,7 +89,8 @@ def test_random_layer_steps_match_the_oracle(i):
 @pytest.mark.parametrize("i", range(12))
 def test_random_hybrid_steps_match_the_oracle(i):
     """The hybrid step (routes left at -1 run on host threads) at random
-    bf16 widths, batch sizes, caps, schedules and thread counts."""
+    weight formats, widths, batch sizes, caps, schedules and thread
+    counts."""
     g0 = np.random.default_rng([79, i])
     H = int(g0.choice([64, 128, 256, 1024]))
     F = int(g0.choice([64, 128, 256]))
@@ -102,15 +103,16 @@ def test_random_hybrid_steps_match_the_oracle(i):
     shared = bool(g0.random() < 0.6)
     threads = int(g0.choice([1, 2, 5]))
     caps = [int(c) for c in g0.choice([0, 0, 1, 3, -1], 4)]
-    print(f"hybrid case {i}: H {H} F {F} E {E} S {S} K {K} T {T} L {L} overlap {overlap} shared {shared} "
-          f"threads {threads} caps {caps}", flush=True)
+    fmt = int(g0.choice([0, 1, 2]))
+    print(f"hybrid case {i}: fmt {fmt} H {H} F {F} E {E} S {S} K {K} T {T} L {L} overlap {overlap} "
+          f"shared {shared} threads {threads} caps {caps}", flush=True)
     g = W.rng(80, "random-hybrid", i)
-    host = [W.bf16_expert_rows(g, E, H, F) for _ in range(L)]
+    host = [W.expert_rows(fmt, g, E, H, F) for _ in range(L)]
     sh = None
     if shared:
         sh = [(W.normal_bf16(g, 2 * F * H, 0.02), W.normal_bf16(g, H * F, 0.02), W.normal_bf16(g, H, 0.02))
               for _ in range(L)]
-    lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, host_rows=host, shared=sh,
+    lay = SlotCacheLayers(layers=L, experts=E, slots=S, hidden=H, ffn=F, fmt=fmt, host_rows=host, shared=sh,
                           max_tokens=T, max_top_k=K, overlap=overlap)
     m.moe_cache_set_cpu_threads(lay.cache, threads)
     oc = oracle.OracleCache(L, E, S)
@@ -128,7 +130,7 @@ def test_random_hybrid_steps_match_the_oracle(i):
             add = None
             if sh is not None:
                 _, add = oracle.shared(H, F, sh[layer][0], sh[layer][1], sh[layer][2], x)
-            ref = oracle.routed(oracle.Pool(0, H, F, host[layer]), ids_e, w, x, addend=add)
+            ref = oracle.routed(oracle.Pool(fmt, H, F, host[layer]), ids_e, w, x, addend=add)
             torch.cuda.synchronize()
             np.testing.assert_array_equal(ids.cpu().numpy(), slots, err_msg=f"step {step}")
             got = out.view(torch.bfloat16).double().cpu().numpy()
