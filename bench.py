@@ -526,12 +526,31 @@ def decode_4bit_benchmark(torch, m, W, x_all, lg_all, n_warm, n_tok, fmt=1, seed
                 del graph
             finally:
                 lay.close()
+        # the hybrid step over the same 4-bit experts: the cache warmed by
+        # the same tokens (eager layer steps), then the timed tokens again
+        # per fetch cap, the CPU routes on host threads
+        try:
+            lay = build_stack(torch, m, W, seed, overlap=2, fmt=fmt, host=host)
+            try:
+                out = torch.empty((1, H), dtype=torch.int16, device="cuda")
+                for t in range(n_warm):
+                    for l in range(L):
+                        lay.decode(l, x_all[t, l], lg_all[t, l], K, out)
+                torch.cuda.synchronize()
+                snap = m.moe_cache_read_state(lay.cache)
+                hyb = hybrid_benchmark(torch, m, lay, snap, x_all, lg_all, n_warm, n_tok)
+            finally:
+                lay.close()
+        except Exception as e:   # the schedule runs above stand on their own
+            hyb = {"error": f"{type(e).__name__}: {e}"}
+            log(f"[bench] 4-bit hybrid: {hyb['error']}")
     finally:
         del host
         release_pinned(torch)
     return {"workload": "the shared-expert decode trace over E2M1 experts (E4M3 per-16 scales, fp32 "
                         "globals): 40 x 256, top-8 + bf16 gated shared expert, H 2048, F 512, 3164 slots",
-            "expert_bytes": int(sum(rb)), "tokens": len(leg_tokens(n_warm, n_tok)), "runs": runs}
+            "expert_bytes": int(sum(rb)), "tokens": len(leg_tokens(n_warm, n_tok)), "runs": runs,
+            "hybrid": hyb}
 
 
 # The other configurations as whole layer steps (admission, miss gather
