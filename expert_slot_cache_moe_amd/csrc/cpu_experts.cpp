@@ -14,6 +14,8 @@
 
 #include "moe_cache.h"
 
+#include <immintrin.h>
+
 #include <atomic>
 #include <cmath>
 #include <condition_variable>
@@ -57,24 +59,13 @@ inline float dot_bf16(const uint16_t *__restrict a, const float *__restrict b, i
     return acc[0];
 }
 
-inline float dot_f32(const float *__restrict a, const float *__restrict b, int n) {
-    float acc[16] = {};
-    for (int i = 0; i < n; i += 16)
-        for (int j = 0; j < 16; ++j) acc[j] += a[i + j] * b[i + j];
-    for (int s = 8; s >= 1; s >>= 1)
-        for (int j = 0; j < s; ++j) acc[j] += acc[j + s];
-    return acc[0];
-}
-
-// The OCP microscaling element and scale encodings, decoded once into
-// tables: E2M1 (sign, 2-bit exponent with bias 1, 1-bit mantissa), E4M3
-// "fn" (bias 7, subnormals, 0x7f / 0xff NaN, no infinities), E8M0 (2^(v -
-// 127), 0xff NaN).
+// The OCP microscaling scale encodings, decoded once into tables: E4M3
+// "fn" (bias 7, subnormals, 0x7f / 0xff NaN, no infinities) and E8M0
+// (2^(v - 127), 0xff NaN).  (E2M1 elements -- sign, 2-bit exponent with
+// bias 1, 1-bit mantissa -- are decoded by e2m1_x2_i8 below.)
 struct Tables {
-    float e2m1[16], e4m3[256], e8m0[256];
+    float e4m3[256], e8m0[256];
     Tables() {
-        static const float mag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
-        for (int v = 0; v < 16; ++v) e2m1[v] = (v & 8) ? -mag[v & 7] : mag[v & 7];
         for (int v = 0; v < 256; ++v) {
             const int ex = (v >> 3) & 15, mt = v & 7;
             float f;
@@ -91,11 +82,39 @@ const Tables &tables() {
     return t;
 }
 
+// 16 E2M1 codes (8 bytes, the even element in the low nibble) as twice
+// their values, exact small integers: sign bit 3, magnitudes 0, 1, 2, 3,
+// 4, 6, 8, 12 -- one byte shuffle of a 16-entry table.
+inline __m128i e2m1_x2_i8(const uint8_t *codes) {
+    const __m128i lut = _mm_setr_epi8(0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12);
+    const __m128i v = _mm_loadl_epi64(reinterpret_cast<const __m128i *>(codes));
+    const __m128i lo = _mm_and_si128(v, _mm_set1_epi8(0x0f));
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(v, 4), _mm_set1_epi8(0x0f));
+    return _mm_shuffle_epi8(lut, _mm_unpacklo_epi8(lo, hi));
+}
+
+// Sum over one block of 16 codes (times two) of code * x, in two 8-lane
+// halves.
+inline __m256 block16(const uint8_t *codes, const float *x) {
+    const __m128i q = e2m1_x2_i8(codes);
+    const __m256 a = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(q));
+    const __m256 b = _mm256_cvtepi32_ps(_mm256_cvtepi8_epi32(_mm_srli_si128(q, 8)));
+    return _mm256_fmadd_ps(b, _mm256_loadu_ps(x + 8), _mm256_mul_ps(a, _mm256_loadu_ps(x)));
+}
+
+inline float hsum(__m256 v) {
+    __m128 s = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));
+    s = _mm_add_ps(s, _mm_movehl_ps(s, s));
+    s = _mm_add_ss(s, _mm_movehdup_ps(s));
+    return _mm_cvtss_f32(s);
+}
+
 // Row `row` of matrix m (0: w13 [2F][H], 1: w2 [H][F]) of expert e, dotted
-// with xf (n floats, n the row length); wv: n floats of scratch.  4-bit
-// rows are expanded to fp32 (code times its block's scale) first; the
-// E2M1 global scale multiplies the dot product.
-float row_dot(const CpuRoutes &r, int m, int e, int row, const float *xf, int n, float *wv) {
+// with xf (n floats, n the row length).  A 4-bit row is taken a scale block
+// at a time: the block's codes (as twice their values) dotted with x, times
+// half the block's scale (E4M3 per 16 or E8M0 per 32), accumulated; the
+// E2M1 global scale multiplies the result.
+float row_dot(const CpuRoutes &r, int m, int e, int row, const float *xf, int n) {
     if (r.fmt == MOE_FMT_BF16) {
         const uint16_t *p = reinterpret_cast<const uint16_t *>(r.bank[m] + (size_t)e * r.rb[m]) + (size_t)row * n;
         return dot_bf16(p, xf, n);
@@ -105,17 +124,26 @@ float row_dot(const CpuRoutes &r, int m, int e, int row, const float *xf, int n,
     const int b0 = (e2m1 ? 3 : 2) * m, block = e2m1 ? 16 : 32;
     const uint8_t *codes = r.bank[b0] + (size_t)e * r.rb[b0] + (size_t)row * (n / 2);
     const uint8_t *sc = r.bank[b0 + 1] + (size_t)e * r.rb[b0 + 1] + (size_t)row * (n / block);
-    for (int i = 0; i < n; i += block) {
-        const float s = e2m1 ? tb.e4m3[sc[i / block]] : tb.e8m0[sc[i / block]];
-        for (int j = 0; j < block; j += 2) {
-            const uint8_t c = codes[(i + j) / 2];
-            wv[i + j] = tb.e2m1[c & 15] * s;
-            wv[i + j + 1] = tb.e2m1[c >> 4] * s;
+    __m256 acc0 = _mm256_setzero_ps(), acc1 = _mm256_setzero_ps();
+    if (e2m1) {
+        // n is a multiple of 16: blocks in pairs, then a last odd one
+        int i = 0;
+        for (; i + 32 <= n; i += 32) {
+            acc0 = _mm256_fmadd_ps(block16(codes + i / 2, xf + i), _mm256_set1_ps(0.5f * tb.e4m3[sc[i / 16]]), acc0);
+            acc1 = _mm256_fmadd_ps(block16(codes + i / 2 + 8, xf + i + 16),
+                                   _mm256_set1_ps(0.5f * tb.e4m3[sc[i / 16 + 1]]), acc1);
+        }
+        if (i < n)
+            acc0 = _mm256_fmadd_ps(block16(codes + i / 2, xf + i), _mm256_set1_ps(0.5f * tb.e4m3[sc[i / 16]]), acc0);
+    } else {
+        for (int i = 0; i < n; i += 32) {
+            const __m256 t = _mm256_add_ps(block16(codes + i / 2, xf + i), block16(codes + i / 2 + 8, xf + i + 16));
+            acc0 = _mm256_fmadd_ps(t, _mm256_set1_ps(0.5f * tb.e8m0[sc[i / 32]]), acc0);
         }
     }
     float glob = 1.f;
     if (e2m1) std::memcpy(&glob, r.bank[b0 + 2] + (size_t)e * r.rb[b0 + 2], 4);
-    return dot_f32(wv, xf, n) * glob;
+    return hsum(_mm256_add_ps(acc0, acc1)) * glob;
 }
 
 }  // namespace
@@ -195,13 +223,12 @@ private:
         const int64_t lo = items_ * id / n_, hi = items_ * (id + 1) / n_;
         const CpuRoutes &r = *r_;
         const int H = r.H, F = r.F;
-        std::vector<float> wv(r.fmt == MOE_FMT_BF16 ? 0 : (size_t)(H > F ? H : F));
         if (phase_ == 0) {
             for (int64_t it = lo; it < hi; ++it) {
                 const int q = (int)(it / (2 * F)), f = (int)(it % (2 * F));
                 const int route = routes_[q];
                 gu_[(size_t)q * 2 * F + f] =
-                    row_dot(r, 0, r.expert[route], f, &xf_[(size_t)(route / r.K) * H], H, wv.data());
+                    row_dot(r, 0, r.expert[route], f, &xf_[(size_t)(route / r.K) * H], H);
             }
         } else if (phase_ == 1) {
             for (int64_t it = lo; it < hi; ++it) {
@@ -216,7 +243,7 @@ private:
                     float acc = 0.f;
                     while (q < (int)routes_.size() && routes_[q] / r.K == t) {
                         const int route = routes_[q];
-                        acc += r.w[route] * row_dot(r, 1, r.expert[route], (int)i, &h_[(size_t)q * F], F, wv.data());
+                        acc += r.w[route] * row_dot(r, 1, r.expert[route], (int)i, &h_[(size_t)q * F], F);
                         ++q;
                     }
                     r.partial[(size_t)t * H + i] = acc;

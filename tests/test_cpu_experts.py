@@ -40,6 +40,16 @@ def test_cpu_routes_match_the_oracle(E, H, F, T, K, frac, fmt):
     check_close(got, ref, "CPU experts")
 
 
+def test_e2m1_rows_of_an_odd_number_of_scale_blocks():
+    """E2M1 rows need only whole 16-element blocks: widths of 80 and 48
+    leave an odd block after the pairs the vector loop takes."""
+    E, H, F, T, K = 8, 80, 48, 3, 2
+    banks, x, cpu, w = _case(5, E, H, F, T, K, 0.7, fmt=1)
+    got = m.moe_cpu_experts(3, cpu, w, x, banks, H, F, 1)
+    ref = oracle.routed(oracle.Pool(1, H, F, banks), cpu, w.astype(np.float64), x)
+    check_close(got, ref, "CPU experts, E2M1, odd blocks")
+
+
 @pytest.mark.parametrize("fmt", [0, 1, 2])
 def test_result_does_not_depend_on_the_thread_count(fmt):
     banks, x, cpu, w = _case(2, 16, 256, 128, 6, 4, 0.7, fmt)
