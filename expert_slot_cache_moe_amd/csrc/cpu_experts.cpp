@@ -1,15 +1,19 @@
 // Routed experts on host cores (the CPU half of the hybrid decode step;
 // FreeToken PR #491, sections 4-5).  See cpu_experts.h.
 //
-// A step's CPU routes run in three data-parallel phases over a fixed pool
-// of threads, each thread owning a contiguous share of the rows of a phase:
-//   A. gate and up rows of every CPU route: dot products with x_t;
-//   B. the SwiGLU activation, rounded to bf16 like the GPU path;
-//   C. the down rows: for each output element, the routes of its token in
+// A step's CPU routes run in two data-parallel phases over a fixed pool
+// of threads, each thread owning a contiguous share of the items of a
+// phase:
+//   A. gate row f and up row F + f of every CPU route: dot products with
+//      x_t, then the SwiGLU activation, rounded to bf16 like the GPU path;
+//   B. the down rows: for each output element, the routes of its token in
 //      ascending k, weighted and summed.
 // Every output element is computed by one thread in a fixed order, so the
-// result does not depend on the thread count.  Dot products keep 16
+// result does not depend on the thread count.  bf16 dot products keep 16
 // partial sums (two 8-wide FMA chains once vectorised) added pairwise.
+// Between phases and steps the workers busy-wait for kSpin, then sleep on
+// a condition variable: a hybrid step's next CPU half comes one GPU layer
+// step later, and a wake-up from sleep costs more than that wait.
 #include "cpu_experts.h"
 
 #include "moe_cache.h"
@@ -17,6 +21,7 @@
 #include <immintrin.h>
 
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <cstring>
@@ -27,6 +32,8 @@
 namespace moe {
 
 namespace {
+
+constexpr std::chrono::microseconds kSpin{200};   // a worker's busy wait before it sleeps
 
 inline float bf16_to_f32(uint16_t v) {
     const uint32_t u = (uint32_t)v << 16;
@@ -174,15 +181,13 @@ public:
         const int nr = (int)routes_.size();
         xf_.resize((size_t)r.T * H);
         for (size_t i = 0; i < xf_.size(); ++i) xf_[i] = bf16_to_f32(r.x[i]);
-        gu_.resize((size_t)nr * 2 * F);
         h_.resize((size_t)nr * F);
         if (nr == 0) {
             std::memset(r.partial, 0, sizeof(float) * (size_t)r.T * H);
             return 0;
         }
-        parallel(0, (int64_t)nr * 2 * F);
-        parallel(1, (int64_t)nr * F);
-        parallel(2, H);
+        parallel(0, (int64_t)nr * F);
+        parallel(1, H);
         return nr;
     }
 
@@ -204,9 +209,19 @@ private:
     void worker(int id) {
         uint64_t seen = 0;
         for (;;) {
-            // spin a little (phases follow each other closely), then sleep
+            // spin for a while (phases follow each other closely, and a
+            // hybrid step's next CPU half comes one GPU layer step later),
+            // then sleep
             uint64_t g = gen_.load(std::memory_order_acquire);
-            for (int spin = 0; g == seen && spin < 20000; ++spin) g = gen_.load(std::memory_order_acquire);
+            if (g == seen) {
+                const auto t0 = std::chrono::steady_clock::now();
+                while (g == seen && std::chrono::steady_clock::now() - t0 < kSpin) {
+                    for (int i = 0; i < 64 && g == seen; ++i) {
+                        _mm_pause();
+                        g = gen_.load(std::memory_order_acquire);
+                    }
+                }
+            }
             if (g == seen) {
                 std::unique_lock<std::mutex> lk(mu_);
                 cv_.wait(lk, [&] { return gen_.load() != seen; });
@@ -225,15 +240,11 @@ private:
         const int H = r.H, F = r.F;
         if (phase_ == 0) {
             for (int64_t it = lo; it < hi; ++it) {
-                const int q = (int)(it / (2 * F)), f = (int)(it % (2 * F));
-                const int route = routes_[q];
-                gu_[(size_t)q * 2 * F + f] =
-                    row_dot(r, 0, r.expert[route], f, &xf_[(size_t)(route / r.K) * H], H);
-            }
-        } else if (phase_ == 1) {
-            for (int64_t it = lo; it < hi; ++it) {
                 const int q = (int)(it / F), f = (int)(it % F);
-                const float g = gu_[(size_t)q * 2 * F + f], u = gu_[(size_t)q * 2 * F + F + f];
+                const int route = routes_[q];
+                const float *xt = &xf_[(size_t)(route / r.K) * H];
+                const float g = row_dot(r, 0, r.expert[route], f, xt, H);
+                const float u = row_dot(r, 0, r.expert[route], F + f, xt, H);
                 h_[(size_t)q * F + f] = round_bf16(g / (1.0f + std::exp(-g)) * u);
             }
         } else {
@@ -264,7 +275,7 @@ private:
     int phase_ = 0;
     int64_t items_ = 0;
     std::vector<int> routes_;      // flattened t*K + k of the CPU routes, ascending
-    std::vector<float> xf_, gu_, h_;
+    std::vector<float> xf_, h_;
 };
 
 CpuExperts *cpu_experts_create(int threads) { return new CpuExperts(threads); }
