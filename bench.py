@@ -401,6 +401,100 @@ def lookahead_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok, seed=0
     return res
 
 
+# The look-ahead where it is meant to pay: the pages' prefetch hides the
+# next layer's copies behind the rest of the current layer (attention and
+# the other layer work), which this workload does not have.  A kernel that
+# holds the compute stream for about LOOKAHEAD_REST_US without touching
+# memory stands in for that work before every layer step (an idealised
+# stand-in: real attention would also use HBM and compute units).
+LOOKAHEAD_REST_US = 150.0
+
+
+def rest_cycles(torch, us):
+    """Clock cycles of torch.cuda._sleep that take about `us` microseconds
+    on this device, measured."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe = 1_000_000
+    torch.cuda._sleep(probe)
+    torch.cuda.synchronize()
+    e0.record()
+    torch.cuda._sleep(probe)
+    e1.record()
+    torch.cuda.synchronize()
+    return max(1, int(probe * us / (e0.elapsed_time(e1) * 1000.0)))
+
+
+def lookahead_rest_benchmark(torch, m, lay, snap, x_all, lg_all, first, n_tok, seed=0):
+    """The timed tokens again with the stand-in for the rest of each layer
+    before every layer step: without look-ahead, and with it at each
+    predictor accuracy (as in lookahead_benchmark); the same cache state
+    each time.  Also the stand-in alone (40 of them per token)."""
+    cyc = rest_cycles(torch, LOOKAHEAD_REST_US)
+    stream = torch.cuda.Stream()
+    x_st = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    lg_st = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
+    pr_st = torch.empty((L, K), dtype=torch.int32, device="cuda")
+    pred = torch.empty((n_tok, L, K), dtype=torch.int32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+
+    def capture(prefetch, layers=True):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            stage_inputs(torch, ((x_all, x_st), (lg_all, lg_st), (pred, pr_st)), step)
+            for l in range(L):
+                torch.cuda._sleep(cyc)
+                if not layers:
+                    continue
+                lay.decode(l, x_st[l], lg_st[l], K, out[l], stream=stream)
+                if prefetch and l + 1 < L:
+                    m.moe_prefetch(lay.cache, l + 1, pr_st[l + 1], stream=stream)
+            if prefetch:
+                m.moe_prefetch_join(lay.cache, stream)
+        return graph
+
+    true_ids = torch.topk(lg_all[:, :, 0, :], K, dim=-1).indices.to(torch.int32)
+    toks = leg_tokens(first, n_tok)
+    n = len(toks)
+
+    def run(graph):
+        step.fill_(first)
+        m.moe_cache_write_state(lay.cache, snap["res"], snap["own"], snap["stamp"], snap["clock"],
+                                freq=snap["freq"], dlast=snap["dlast"], last_demand=snap["last_demand"])
+        st0 = m.moe_cache_stats(lay.cache)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in toks:
+            graph.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        d = m.moe_cache_stats(lay.cache) - st0
+        return {"value": round(L * n / dt, 1), "ms_per_step": round(dt / n * 1000.0, 4),
+                "demand_fetches_per_token": round(float(d[m.MOE_STAT_MISSED] - d[m.MOE_STAT_OVERFLOW]) / n, 2),
+                "prefetch_fills_per_token": round(float(d[m.MOE_STAT_PF_FILLED]) / n, 2)}
+
+    g = capture(False, layers=False)
+    rest = run(g)
+    del g
+    res = {"rest_us": LOOKAHEAD_REST_US, "rest_ms_per_token": rest["ms_per_step"], "tokens": n, "runs": []}
+    g = capture(False)
+    r = run(g)
+    del g
+    res["runs"].append({"prefetch": False, **r})
+    log(f"[bench] rest of the layer ({LOOKAHEAD_REST_US} us stand-in), no look-ahead: {r}")
+    g = capture(True)
+    for acc in LOOKAHEAD_ACCURACY:
+        rng = np.random.default_rng([seed, int(round(acc * 1000))])
+        keep = torch.from_numpy(rng.random((n_tok, L, K)) < acc).cuda()
+        rnd = torch.from_numpy(rng.integers(0, E, (n_tok, L, K)).astype(np.int32)).cuda()
+        pred.copy_(torch.where(keep, true_ids, rnd))
+        r = run(g)
+        res["runs"].append({"prefetch": True, "predictor_accuracy": acc, **r})
+        log(f"[bench] rest of the layer ({LOOKAHEAD_REST_US} us stand-in), look-ahead at accuracy {acc}: {r}")
+    del g
+    return res
+
+
 # The layer-step schedules timed beside the default one (overlap = 2).
 SCHEDULES = ((0, "serial: gather, shared expert and routed experts in order on one stream"),
              (1, "gather on the side stream, overlapping the shared expert and the resident routes"),
@@ -1339,6 +1433,9 @@ def main():
         batches=ADMISSION_CHUNKED_BATCHES)
     look = None if args.no_lookahead else run_leg(
         "look-ahead", lookahead_benchmark, torch, m, lay, snap, x_all, lg_all, first, n_tok)
+    look_rest = None if args.no_lookahead else run_leg(
+        "look-ahead with the rest of the layer", lookahead_rest_benchmark, torch, m, lay, snap, x_all, lg_all,
+        first, n_tok)
     sched = (None if args.no_schedules or args.overlap != 2
              else run_leg("schedules", schedule_benchmark, torch, m, lay, snap, x_all, lg_all, first, n_tok))
     hyb = None if args.no_hybrid else run_leg(
@@ -1401,6 +1498,7 @@ def main():
         "admission_us_one_call_width_128": adm_chunked,
         "routed_gemv_wide": wide,
         "lookahead": look,
+        "lookahead_with_rest": look_rest,
         "schedules": sched,
         "hybrid": hyb,
         "decode_4bit": dec4,
