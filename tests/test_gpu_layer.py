@@ -595,11 +595,12 @@ def test_staged_steps_split_any_top_k_like_the_serial_path(fmt, K):
             lay.close()
 
 
-@pytest.mark.parametrize("fmt,E,S,K", [(0, 128, 100, 64), (1, 128, 90, 64), (2, 1500, 40, 8), (0, 1025, 30, 6)])
+@pytest.mark.parametrize("fmt,E,S,K", [(0, 128, 100, 64), (1, 128, 90, 64), (2, 1500, 40, 8), (0, 1025, 30, 6),
+                                     (1, 1024, 30, 6)])
 def test_single_token_layer_steps_at_the_top_k_and_expert_limits(fmt, E, S, K):
     """Top-64 (the largest a single-token step takes: the admission's fused
-    top-k and the stage kernels' route limit) and more than 1024 experts
-    (the fused top-k's limit: a separate top-k launch first), with the
+    top-k and the stage kernels' route limit), 1024 experts (the most the
+    fused top-k takes) and more (a separate top-k launch first), with the
     shared expert and misses every step: slot ids exact, staged == serial
     bit for bit, outputs within tolerance of the oracle."""
     L, H, F = 2, 64, 128
