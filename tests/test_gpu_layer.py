@@ -661,10 +661,12 @@ def test_shared_expert_decode_shape_staged():
             lay.close()
 
 
-def test_fused_topk_in_the_layer_step_handles_ties_and_nan():
-    """Few rows: the layer step's top-k runs inside the admission kernel;
-    equal logits take the lower expert, NaN counts as -infinity."""
-    E, S, H, K, T = 64, 40, 64, 4, 5
+@pytest.mark.parametrize("T", [5, 32, 33])
+def test_fused_topk_in_the_layer_step_handles_ties_and_nan(T):
+    """Up to 32 rows the layer step's top-k runs inside the admission
+    kernel (33: a separate top-k launch); equal logits take the lower
+    expert, NaN counts as -infinity."""
+    E, S, H, K = 64, 40, 64, 4
     g = W.rng(14, "fused-topk")
     host = [W.bf16_expert_rows(g, E, H, 128)]
     lay = SlotCacheLayers(layers=1, experts=E, slots=S, hidden=H, ffn=128, host_rows=host,
