@@ -68,6 +68,16 @@ def test_admission_only_crossover_widths():
     _run(1, 512, 2100, steps, one=128, qw=128)
 
 
+@pytest.mark.parametrize("R", [255, 256, 257, 384])
+def test_one_call_width_boundary(R):
+    """At most 256 routes are one query over the raw route list; 257 and
+    more go through the distinct list in 128-expert chunks; with misses and
+    evictions (600 experts over 500 slots), states bit-exact each step."""
+    g = np.random.default_rng(30 + R)
+    steps = [(0, g.integers(0, 600, R), -1) for _ in range(12)]
+    _run(1, 600, 500, steps)
+
+
 def test_wide_step_counts_printed_on_the_pages():
     E = 160
     g = W.rng(0, "test", "wide")
