@@ -18,6 +18,10 @@ HIPCC_FLAGS = [
     # no implicit a*b+c fusion: kernels that must agree bit for bit round
     # alike wherever they are inlined (explicit fmaf still fuses)
     "-ffp-contract=off",
+    # gfx950 loads the leading kernel arguments into scalar registers at
+    # wave launch (up to 14 dwords), so kernels that put their hot scalar
+    # arguments first need no argument load before their first request
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

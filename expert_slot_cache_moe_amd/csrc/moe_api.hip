@@ -46,26 +46,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 void row_bytes_of(int fmt, int H, int F, int64_t rb[MOE_MAX_BANKS], int *nb) {
-    for (int b = 0; b < MOE_MAX_BANKS; ++b) rb[b] = 0;
-    if (fmt == MOE_FMT_BF16) {
-        rb[0] = (int64_t)2 * F * H * 2;
-        rb[1] = (int64_t)H * F * 2;
-        *nb = 2;
-    } else if (fmt == MOE_FMT_MXFP4) {
-        rb[0] = (int64_t)2 * F * H / 2;
-        rb[1] = (int64_t)2 * F * H / 32;
-        rb[2] = (int64_t)H * F / 2;
-        rb[3] = (int64_t)H * F / 32;
-        *nb = 4;
-    } else {
-        rb[0] = (int64_t)2 * F * H / 2;
-        rb[1] = (int64_t)2 * F * H / 16;
-        rb[2] = 4;
-        rb[3] = (int64_t)H * F / 2;
-        rb[4] = (int64_t)H * F / 16;
-        rb[5] = 4;
-        *nb = 6;
-    }
+    for (int b = 0; b < MOE_MAX_BANKS; ++b) rb[b] = bank_row_bytes(fmt, b, H, F);
+    *nb = bank_count(fmt);
 }
 
 RoutedWs routed_ws(int H, int F, int T, int K) {

@@ -277,6 +277,18 @@ struct PoolView {
     int64_t rb[MOE_MAX_BANKS];
 };
 
+// Bytes of one expert's row in bank b (0 past the format's last bank):
+// bf16 [gate|up][H] and down [H][F]; E2M1 gate/up codes, their E4M3 scales
+// (one per 16), the fp32 global scale, then the same three for down; MXFP4
+// gate/up codes, their E8M0 scales (one per 32), then down's two.
+constexpr int64_t bank_row_bytes(int fmt, int b, int H, int F) {
+    const int64_t up = (int64_t)2 * F * H, dn = (int64_t)H * F;
+    if (fmt == MOE_FMT_BF16) return b == 0 ? up * 2 : b == 1 ? dn * 2 : 0;
+    if (fmt == MOE_FMT_MXFP4) return b == 0 ? up / 2 : b == 1 ? up / 32 : b == 2 ? dn / 2 : b == 3 ? dn / 32 : 0;
+    return b == 0 ? up / 2 : b == 1 ? up / 16 : b == 2 ? 4 : b == 3 ? dn / 2 : b == 4 ? dn / 16 : b == 5 ? 4 : 0;
+}
+constexpr int bank_count(int fmt) { return fmt == MOE_FMT_BF16 ? 2 : fmt == MOE_FMT_MXFP4 ? 4 : 6; }
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_topk(const float *logits, int T, int E, int K, int32_t *ids, float *w,
