@@ -508,9 +508,25 @@ __device__ __forceinline__ void narrow_step(const AdmitParams &p, lds_view v, co
     }
 }
 
+// The arguments the prologue's loads need lead, as scalars: gfx950 preloads
+// the leading kernel arguments into scalar registers at wave launch, so the
+// clock, order, slot map, histogram and logits requests go out without
+// waiting for an argument load first.
 template <int P>
-__global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
+__global__ __launch_bounds__(kThreads) void admit_fast_kernel(uint32_t *clock, int32_t *order, int32_t *res,
+                                                              int64_t *freq, const float *logits, int layer,
+                                                              int E_, int R_, int S_, AdmitParams p_in) {
     extern __shared__ __align__(16) int32_t lds[];
+    AdmitParams p = p_in;
+    p.clock = clock;
+    p.order = order;
+    p.res = res;
+    p.freq = freq;
+    p.logits = logits;
+    p.layer = layer;
+    p.E = E_;
+    p.R = R_;
+    p.S = S_;
     const int E = p.E, S = p.S, R = p.R;
     int32_t *wsum = lds;            // [32]
     int32_t *misc = lds + 32;       // [16]: 0 invalid routes
@@ -547,7 +563,6 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     // waited for them.  mbcnt_lo(0, 0) is 0 in every lane, but lane-varying
     // to the compiler.
     const uint32_t clk = p.clock[__builtin_amdgcn_mbcnt_lo(0u, 0u)];
-    const int64_t st_lane = tid < kAdmitStats ? p.stats[(int64_t)p.layer * MOE_NUM_STATS + tid] : 0;
 
     // This thread's run of the LRU order: (slot, owner) pairs.  The order
     // buffer holds kThreads * P pairs (admit_order_bytes), so the loads are
@@ -599,6 +614,9 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     int32_t rv[4];
     int64_t rfv[4];
     load_rows(0, rv, rfv);
+    // (after the requests above: the statistics' address is a kernel
+    // argument that is not preloaded)
+    const int64_t st_lane = tid < kAdmitStats ? p.stats[(int64_t)p.layer * MOE_NUM_STATS + tid] : 0;
 
     if (p.logits != nullptr) {
         for (int t = wave; t < p.T; t += kWaves)
@@ -824,6 +842,8 @@ __global__ __launch_bounds__(kThreads) void admit_fast_kernel(AdmitParams p) {
     }
 }
 
+#define MOE_ADMIT_LEAD(p) (p).clock, (p).order, (p).res, (p).freq, (p).logits, (p).layer, (p).E, (p).R, (p).S
+
 int fast_p(int S) {
     int P = 1;
     while (P * kThreads < S) P *= 2;
@@ -877,11 +897,11 @@ hipError_t launch_admit(const AdmitParams &p, size_t lds_bytes, hipStream_t s) {
                             {p.res, rec::kReadWrite}, {p.plan_slot, rec::kWrite},
                             {p.route_plan, rec::kWrite}, {p.w_out, rec::kWrite}});
     switch (fast_p(p.S)) {
-    case 1: hipLaunchKernelGGL(admit_fast_kernel<1>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
-    case 2: hipLaunchKernelGGL(admit_fast_kernel<2>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
-    case 4: hipLaunchKernelGGL(admit_fast_kernel<4>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
-    case 8: hipLaunchKernelGGL(admit_fast_kernel<8>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
-    case 16: hipLaunchKernelGGL(admit_fast_kernel<16>, dim3(1), dim3(kThreads), lds_bytes, s, p); break;
+    case 1: hipLaunchKernelGGL(admit_fast_kernel<1>, dim3(1), dim3(kThreads), lds_bytes, s, MOE_ADMIT_LEAD(p), p); break;
+    case 2: hipLaunchKernelGGL(admit_fast_kernel<2>, dim3(1), dim3(kThreads), lds_bytes, s, MOE_ADMIT_LEAD(p), p); break;
+    case 4: hipLaunchKernelGGL(admit_fast_kernel<4>, dim3(1), dim3(kThreads), lds_bytes, s, MOE_ADMIT_LEAD(p), p); break;
+    case 8: hipLaunchKernelGGL(admit_fast_kernel<8>, dim3(1), dim3(kThreads), lds_bytes, s, MOE_ADMIT_LEAD(p), p); break;
+    case 16: hipLaunchKernelGGL(admit_fast_kernel<16>, dim3(1), dim3(kThreads), lds_bytes, s, MOE_ADMIT_LEAD(p), p); break;
     default:
         if (p.logits != nullptr) return hipErrorInvalidValue;
         hipLaunchKernelGGL(admit_kernel, dim3(1), dim3(kThreads), lds_bytes, s, p);

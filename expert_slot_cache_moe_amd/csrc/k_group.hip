@@ -246,6 +246,24 @@ struct GroupEntry {
     }
 };
 
+// The grouped kernels take what their first request needs -- the group
+// table and its bounds -- as leading scalar arguments, which gfx950
+// preloads into scalar registers at wave launch: the first group entry is
+// requested without waiting for an argument load.
+#define MOE_GROUP_LEAD_PARAMS                                                                       \
+    const int32_t *__restrict__ lead_row, const int32_t *__restrict__ lead_count,                \
+        const int32_t *__restrict__ lead_start, int lead_n, int lead_rows
+#define MOE_GROUP_LEAD_ARGS(pool, items) \
+    (items).grp_row, (items).grp_count, (items).grp_start, (items).n, (pool).num_rows
+#define MOE_GROUP_TAKE_LEAD()             \
+    PoolView pool = pool_in;              \
+    Items items = items_in;               \
+    pool.num_rows = lead_rows;            \
+    items.grp_row = lead_row;             \
+    items.grp_count = lead_count;         \
+    items.grp_start = lead_start;         \
+    items.n = lead_n
+
 // gate/up + SwiGLU, 16 * UT rows j per wave, for the groups blockIdx.y,
 // blockIdx.y + gridDim.y, ...: h[route][j] = bf16(silu(g) * u) for every
 // route of a group.  The grid holds about as many workgroups as the device
@@ -256,9 +274,10 @@ struct GroupEntry {
 // loads) are read.  Tokens go through the matrix cores 16 at a time; a
 // group of more than 16 routes streams its rows once per 16.
 template <int FMT, int UT, int NB>
-__global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, Items items,
-                                                               const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(MOE_GROUP_LEAD_PARAMS, PoolView pool_in,
+                                                               Items items_in, const uint16_t *__restrict__ x,
                                                                uint16_t *__restrict__ h) {
+    MOE_GROUP_TAKE_LEAD();
     const int H = pool.H, F = pool.F, K = items.K;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int c = lane & (kTile - 1), q = lane / kTile;
@@ -343,9 +362,10 @@ __global__ __launch_bounds__(kMThreads, 2) void up_mfma_kernel(PoolView pool, It
 // (F) is short, so a wave takes several row tiles to keep enough bytes in
 // flight; the activation operand is shared by all of them.
 template <int FMT, int RT, int NB>
-__global__ __launch_bounds__(kMThreads, 2) void down_mfma_kernel(PoolView pool, Items items,
-                                                              const uint16_t *__restrict__ h,
+__global__ __launch_bounds__(kMThreads, 2) void down_mfma_kernel(MOE_GROUP_LEAD_PARAMS, PoolView pool_in,
+                                                              Items items_in, const uint16_t *__restrict__ h,
                                                               float *__restrict__ d) {
+    MOE_GROUP_TAKE_LEAD();
     const int H = pool.H, F = pool.F;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
     const int c = lane & (kTile - 1), q = lane / kTile;
@@ -478,10 +498,11 @@ __device__ __forceinline__ void stage_rows(const uint16_t *__restrict__ src_row,
 // up rows per workgroup), the batch's activations from LDS; the hidden
 // width is NS slabs (pool.H == NS * kSlab, launcher).
 template <int FMT, int NS>
-__global__ __launch_bounds__(kXThreads, 3) void up_x_kernel(PoolView pool, Items items,
-                                                            const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(kXThreads, 3) void up_x_kernel(MOE_GROUP_LEAD_PARAMS, PoolView pool_in,
+                                                            Items items_in, const uint16_t *__restrict__ x,
                                                             uint16_t *__restrict__ h) {
     extern __shared__ __align__(16) uint16_t xs[];   // [kTile][H + kXPad], then scales
+    MOE_GROUP_TAKE_LEAD();
     constexpr int H = NS * kSlab, nslab = NS;
     constexpr int AHEAD = NS < kXAhead ? NS : kXAhead;
     using QS = QScales<FMT, H>;
@@ -572,10 +593,11 @@ __global__ __launch_bounds__(kXThreads, 3) void up_x_kernel(PoolView pool, Items
 // per workgroup), the batch's activations h from LDS; the FFN width is NS
 // slabs (pool.F == NS * kSlab, launcher).
 template <int FMT, int RT, int NS>
-__global__ __launch_bounds__(kXThreads, 3) void down_x_kernel(PoolView pool, Items items,
-                                                              const uint16_t *__restrict__ h,
+__global__ __launch_bounds__(kXThreads, 3) void down_x_kernel(MOE_GROUP_LEAD_PARAMS, PoolView pool_in,
+                                                              Items items_in, const uint16_t *__restrict__ h,
                                                               float *__restrict__ d) {
     extern __shared__ __align__(16) uint16_t hs[];   // [kTile][F + kXPad], then scales
+    MOE_GROUP_TAKE_LEAD();
     constexpr int F = NS * kSlab, nslab = NS;
     constexpr int NB0 = kXDownAhead / RT > 0 ? kXDownAhead / RT : 1;
     constexpr int NB = NS < NB0 ? NS : NB0;
@@ -800,7 +822,8 @@ hipError_t launch_up_shape(const PoolView &pool, const Items &items, int max_ite
     const int rows = kMWaves * kTile * UT;
     const int cols = pool.F / rows;
     const dim3 grid(cols, group_rows(max_items, cols, resident(up_mfma_kernel<FMT, UT, NB>, res)));
-    hipLaunchKernelGGL((up_mfma_kernel<FMT, UT, NB>), grid, dim3(kMThreads), 0, s, pool, items, x, h);
+    hipLaunchKernelGGL((up_mfma_kernel<FMT, UT, NB>), grid, dim3(kMThreads), 0, s,
+                       MOE_GROUP_LEAD_ARGS(pool, items), pool, items, x, h);
     return hipGetLastError();
 }
 
@@ -812,7 +835,8 @@ hipError_t launch_down_shape(const PoolView &pool, const Items &items, int max_i
     const int rows = kMWaves * kTile * RT;
     const int cols = (pool.H + rows - 1) / rows;
     const dim3 grid(cols, group_rows(max_items, cols, resident(down_mfma_kernel<FMT, RT, NB>, res)));
-    hipLaunchKernelGGL((down_mfma_kernel<FMT, RT, NB>), grid, dim3(kMThreads), 0, s, pool, items, h, d);
+    hipLaunchKernelGGL((down_mfma_kernel<FMT, RT, NB>), grid, dim3(kMThreads), 0, s,
+                       MOE_GROUP_LEAD_ARGS(pool, items), pool, items, h, d);
     return hipGetLastError();
 }
 }  // namespace
@@ -861,7 +885,8 @@ hipError_t launch_up_x(const PoolView &pool, const Items &items, int max_items, 
     constexpr size_t lds = up_x_lds<FMT, NS * kSlab>();
     const int cols = pool.F / (kXWaves * kTile);
     const dim3 grid(cols, group_rows(max_items, cols, resident_x(up_x_kernel<FMT, NS>, res, lds)));
-    hipLaunchKernelGGL((up_x_kernel<FMT, NS>), grid, dim3(kXThreads), lds, s, pool, items, x, h);
+    hipLaunchKernelGGL((up_x_kernel<FMT, NS>), grid, dim3(kXThreads), lds, s, MOE_GROUP_LEAD_ARGS(pool, items),
+                       pool, items, x, h);
     return hipGetLastError();
 }
 
@@ -875,7 +900,8 @@ hipError_t launch_down_x(const PoolView &pool, const Items &items, int max_items
     const int rows = kXWaves * kTile * RT;
     const int cols = (pool.H + rows - 1) / rows;
     const dim3 grid(cols, group_rows(max_items, cols, resident_x(down_x_kernel<FMT, RT, NS>, res, lds)));
-    hipLaunchKernelGGL((down_x_kernel<FMT, RT, NS>), grid, dim3(kXThreads), lds, s, pool, items, h, d);
+    hipLaunchKernelGGL((down_x_kernel<FMT, RT, NS>), grid, dim3(kXThreads), lds, s,
+                       MOE_GROUP_LEAD_ARGS(pool, items), pool, items, h, d);
     return hipGetLastError();
 }
 
