@@ -46,6 +46,8 @@ def test_query_widths_match_the_pages():
 def test_bank_row_bytes():
     assert m.moe_bank_row_bytes(m.MOE_FMT_BF16, 2048, 512) == [4 * 512 * 2048, 2 * 2048 * 512]
     assert m.moe_bank_row_bytes(m.MOE_FMT_E2M1, 1024, 256) == [262144, 32768, 4, 131072, 16384, 4]
+    # MXFP4: gate/up codes, one E8M0 per 32 of them, then down's two
+    assert m.moe_bank_row_bytes(m.MOE_FMT_MXFP4, 1024, 256) == [262144, 16384, 131072, 8192]
     with pytest.raises(m.MoeError):
         m.moe_bank_row_bytes(7, 64, 64)
 
